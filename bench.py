@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of the MiniMax-M3 pre-attention prologue on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+
+A step is one whole prologue call (pre_attn_decode or pre_attn_prefill through
+the C ABI) over one batch of synthetic input. Inputs rotate over a pool of
+distinct weight / activation sets of at least 512 MB (twice the 256 MB
+Infinity Cache), so every step streams its weight from HBM. The K timed steps
+are captured into one HIP graph (as a serving engine replays decode steps) and
+replayed between device synchronizations; a second, eager pass over the same
+pool records HIP events around every launch of the dominant kernel to get its
+average duration for the roofline. Prints one JSON line.
+
+Workloads (``--config``): c1 tiny decode, c2 decode batch (default: the
+decode-throughput headline shape), c3 speculative decode, c4 / c5 prefill.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--pool-mb", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    return ap.parse_args()
+
+
+def algorithmic(wl):
+    """(bytes per call, bytes of the dominant kernel per launch, flops per call)."""
+    S, K, nkv = wl.tokens, wl.hidden, wl.nkv
+    N = (19 * nkv + 1) * 128
+    call_bytes = (N * K + 4 * N + 4 * S * K + 2 * S * K + 2 * K + 4 * 256
+                  + S * 16 * nkv * 256 + S * nkv * 256 + S * nkv * (256 + 8) + 128 * S
+                  + 128 * S + 16 * S)
+    if wl.mode == "prefill":
+        call_bytes += N * K // 32 - 4 * N  # E8M0 block scales instead of row scales
+    kernel_bytes = N * K + S * K  # FP8 weight + FP8 activation codes
+    flops = 2 * S * N * K
+    return call_bytes, kernel_bytes, flops
+
+
+def source_sha(mode: str) -> str:
+    name = "pa_decode.hip" if mode == "decode" else "pa_prefill.hip"
+    with open(os.path.join(ROOT, "kv_residual_add_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str, mode: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(mode):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from tests import parity
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max((i["num_threads"] for i in blas), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = 1
+    S = wl.tokens
+    rows = np.arange(S) if wl.mode == "decode" else np.arange(min(S, 64))
+    sub = inp if len(rows) == S else parity.subset(inp, rows)
+    fn = oracle.decode if wl.mode == "decode" else oracle.prefill
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn(sub)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    t = float(np.median(times))
+    N = (19 * wl.nkv + 1) * 128
+    if wl.mode == "decode":
+        value, unit = len(rows) / t, "tokens/s"
+    else:
+        value, unit = 2 * len(rows) * N * wl.hidden / t / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {S} tokens per oracle call, median of {len(times)} calls "
+                      f"({sum(times):.1f} s), float64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the prologue shards by heads with no exchange, so per-GPU throughput is the "
+              "figure that matters", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from kv_residual_add_amd import _binding as B
+    from kv_residual_add_amd.runner import Problem
+
+    torch.cuda.set_device(0)
+    wl = synth.named_config(args.config)
+    inp = synth.make_workload(wl, seed=0)
+    prob = Problem(inp)
+    dev = prob.device
+    S, K = wl.tokens, wl.hidden
+    N = prob.N
+    call_bytes, kernel_bytes, flops = algorithmic(wl)
+
+    # rotating pool of distinct weight + activation sets
+    set_bytes = prob.w_packed.numel() + prob.w_scales.numel() * prob.w_scales.element_size() \
+        + 4 * S * K
+    n_sets = max(2, math.ceil(args.pool_mb * 2**20 / set_bytes))
+    w_dev = torch.from_numpy(inp["w"]).to(dev)
+    sets = []
+    for i in range(n_sets):
+        sh = (i * 128) % K
+        wp = torch.empty_like(prob.w_packed)
+        if prob.mode == B.PA_MODE_DECODE:
+            B.pa_pack_weight_decode(torch.roll(w_dev, sh, dims=1).contiguous(), wp)
+            ws = torch.roll(prob.w_scales, i)
+        else:
+            we = torch.from_numpy(inp["w_e8m0"]).to(dev)
+            ws = torch.empty_like(prob.w_scales)
+            B.pa_pack_weight_prefill(torch.roll(w_dev, sh, dims=1).contiguous(),
+                                     torch.roll(we, sh // 32, dims=1).contiguous(), wp, ws)
+        ar = torch.roll(prob.t["ar"], sh, dims=1).contiguous()
+        res = torch.roll(prob.t["res"], sh, dims=1).contiguous()
+        sets.append((wp, ws, ar, res))
+    del w_dev
+    torch.cuda.synchronize()
+
+    def step(i):
+        wp, ws, ar, res = sets[i % n_sets]
+        prob.run(w_packed=wp, w_scales=ws, ar=ar, res=res)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.steps):
+                    step(args.warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()  # first replay uploads the graph; not timed
+        torch.cuda.synchronize()
+    t_ev0 = torch.cuda.Event(enable_timing=True)
+    t_ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_ev0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    t_ev1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_s = t_ev0.elapsed_time(t_ev1) / 1e3
+    elapsed = max(wall_s, gpu_s)
+
+    # eager pass with HIP events around every launch of the dominant kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        B.pa_set_kernel_events(*evs[i])
+        step(args.warmup + i)
+    e1.record()
+    B.pa_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    eager_s = e0.elapsed_time(e1) / 1e3
+
+    key = args.config
+    traffic = measured_traffic(key, wl.mode)
+    if wl.mode == "decode":
+        metric, unit = "decode tokens/s", "tokens/s"
+        value = S * args.steps / elapsed
+        achieved = kernel_bytes / (kern_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "decode_gemv", "kernel_ms": round(kern_ms, 5),
+                "algorithmic_bytes_per_launch": kernel_bytes}
+        extra = {"step_hbm_gbs": round(call_bytes * args.steps / elapsed / 1e9, 1),
+                 "step_hbm_frac": round(call_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes_per_step": call_bytes}
+    else:
+        metric, unit = "prefill FP8 TFLOP/s", "TFLOP/s"
+        value = flops * args.steps / elapsed / 1e12
+        achieved = flops / (kern_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "prefill_gemm", "kernel_ms": round(kern_ms, 5),
+                "algorithmic_flops_per_launch": flops}
+        extra = {"step_tflops_frac": round(value / FP8_PEAK_TFLOPS, 4),
+                 "tokens_per_s": round(S * args.steps / elapsed, 1)}
+
+    line = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if wl.mode == "decode" else "mxfp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": S, "hidden": K, "nkv": wl.nkv, "n_rows": N,
+                   "pool_sets": n_sets, "timing": "hip graph replay" if graph else "eager"},
+        "roofline": roof,
+        "eager_ms_per_step": round(eager_s / args.steps * 1e3, 5),
+        **extra,
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * pre_attn.h — C ABI of the MiniMax-M3 fused pre-attention prologue for one
+ * layer on one GPU (AMD Instinct MI355X, gfx950).
+ *
+ * What one call computes, per token (row) of the batch. Sources are the vLLM
+ * API pages "vllm.models.minimax_m3.amd.mono.kernels.pre_attn" (K1 mono_pre:
+ * module docstring, emit_pre_attn with norm_quant, the GEMV tasks and the head
+ * tasks, head_norm_rope, page16_of) and
+ * "vllm.models.minimax_m3.nvidia.ops.qkv_index_fused_epilogue" (module and class
+ * docstrings, _rms_norm, _rope64, the per-role epilogue branches and the
+ * argument rules of minimax_m3_qkv_index_fused_epilogue):
+ *
+ *   acc   = f32(ar) + f32(res)                      h_out = bf16(acc)
+ *   xn    = acc / sqrt(mean(acc^2) + eps) * (1 + g_in)          (Gemma RMSNorm)
+ *   decode : per-token FP8   s_x = max|xn| / 448 (1 if 0), x8 = E4M3(xn / s_x)
+ *            y[n] = (x8 . w8[n]) * s_x * w_scale[n]
+ *   prefill: MXFP8           per 32-wide k block, scale 2^(floor(log2 amax) - 8)
+ *            y[n] = sum_k xq_k 2^(ex-127) * wq_k 2^(ew-127)
+ *   y is split into 128-wide heads  q x 16nkv | k x nkv | v x nkv | iq x nkv | ik
+ *   (N = (19 nkv + 1) * 128 rows); it is never written to memory.
+ *   q, k, iq, ik heads: Gemma RMSNorm over the head with g_q / g_k / g_iq / g_ik,
+ *            then NeoX RoPE on dims 0..63 (dim i pairs with i + 32),
+ *            cos = cos_sin[pos][0..31], sin = cos_sin[pos][32..63].
+ *   q_out, iq_out = bf16 of the result.
+ *   K  (normed + roped) and V (raw y) per KV head j: scale s = max|.| / 448
+ *            (1 if 0), codes E4M3(. / s), into the page-16 caches at the
+ *            token's slot; index_k (normed + roped) as E4M3 with unit scale.
+ *   E4M3 is OCP E4M3FN, round to nearest even, saturating at +-448.
+ *
+ * Memory layouts (all device memory, row-major, owned by the caller):
+ *   ar, res, h_out   bf16 [tokens][hidden]
+ *   g_in             bf16 [hidden];   g_q, g_k, g_iq, g_ik  bf16 [128]
+ *   cos_sin          bf16 [max_pos][64]   (cos | sin)
+ *   positions        int64 [tokens], each in [0, max_pos)
+ *   slot_mapping     int64 [tokens]; slot < 0: the token writes no cache byte;
+ *                    otherwise page = slot / 16, row t = slot % 16 and
+ *                    slot < num_pages * 16; slots of one call are distinct
+ *   k_cache, v_cache uint8 [num_pages][nkv][2048]
+ *       K byte of dim d: (d / 16) * 256 + t * 16 + d % 16   ("shuffle" layout)
+ *       V byte of dim d: d * 16 + t                          (dim-major)
+ *   k_scale, v_scale float [num_pages][nkv][16], entry t
+ *   index_cache      uint8 [num_pages * 16][128], row = slot
+ *   q_out            bf16 [tokens][16 nkv][128]
+ *   iq_out           bf16 [tokens][nkv][128]
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are device pointers. ar, res, h_out, g_in, the packed
+ *     weights, q_out, iq_out, the caches and the workspace must be 16-byte
+ *     aligned; positions and slot_mapping 8-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work on it: they never synchronize the host and never allocate memory.
+ *   - The library never frees or keeps caller memory. Outputs h_out, q_out
+ *     and iq_out are written in full; cache bytes and scales only at the
+ *     slots of tokens with slot >= 0; nothing else is written.
+ *   - Return 0 (PA_OK) on success, a negative pa_status otherwise. Argument
+ *     errors are detected before anything is enqueued. Device preconditions
+ *     (positions in range, slots in range and distinct) are the caller's; an
+ *     out-of-range position or slot is clamped or skipped, never dereferenced
+ *     out of bounds.
+ *   - Calls on different streams with distinct workspaces are independent.
+ *     Two calls that share a workspace must be ordered (same stream).
+ */
+#ifndef PRE_ATTN_H
+#define PRE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_HEAD_DIM 128
+#define PA_ROTARY_DIM 64
+#define PA_PAGE 16
+#define PA_PAGE_BYTES 2048
+#define PA_MAX_HIDDEN 16384
+#define PA_DECODE_MAX_TOKENS 64
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,      /* a required pointer is NULL */
+  PA_ERR_ALIGN = -2,     /* a pointer is not aligned as stated above */
+  PA_ERR_NKV = -3,       /* nkv is not 1, 2 or 4 */
+  PA_ERR_HIDDEN = -4,    /* hidden is not a multiple of 128 in [128, 16384] */
+  PA_ERR_TOKENS = -5,    /* tokens < 1, or > 64 for decode, or > 2^24 */
+  PA_ERR_WORKSPACE = -6, /* workspace smaller than pa_workspace_bytes() */
+  PA_ERR_DIMS = -7,      /* num_pages < 1, max_pos < 1 or eps not finite >= 0 */
+  PA_ERR_HIP = -8,       /* a HIP runtime call or launch failed */
+  PA_ERR_DEVICE = -9,    /* the current device is not a gfx950 GPU */
+  PA_ERR_MODE = -10      /* unknown mode argument */
+} pa_status;
+
+/* Problem size of one call. */
+typedef struct pa_dims {
+  int32_t tokens;    /* rows of ar / res (decode: 1..64, prefill: 1..2^24) */
+  int32_t hidden;    /* K, a multiple of 128, at most 16384 */
+  int32_t nkv;       /* KV heads on this GPU: 1, 2 or 4 */
+  int32_t num_pages; /* pages of k_cache / v_cache (16 slots each) */
+  int32_t max_pos;   /* rows of cos_sin */
+  float eps;         /* RMSNorm epsilon, used by the input norm and every head norm */
+} pa_dims;
+
+#define PA_MODE_DECODE 0
+#define PA_MODE_PREFILL 1
+
+/* Bytes of device workspace a call with these dims needs (0 on bad dims or
+ * mode). The workspace is caller-owned scratch; it may be reused by any later
+ * call whose requirement it meets, once pa_workspace_init has run on it. */
+size_t pa_workspace_bytes(const pa_dims* dims, int mode);
+
+/* Prepares a freshly allocated workspace of `bytes` bytes for use (clears the
+ * library's counters with a fill kernel on `stream`). Needed once per
+ * allocation; calls leave it ready for the next call. */
+int pa_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Bytes of the packed weight (and packed block scales) for N rows x hidden. */
+size_t pa_packed_weight_bytes(int mode, int32_t n_rows, int32_t hidden);
+size_t pa_packed_scale_bytes(int mode, int32_t n_rows, int32_t hidden);
+
+/* Decode weight: the fused projection's per-output-channel FP8 weight (the
+ * pre_attn page's "preshuffled ptpc-FP8 weight", prepared once at load time).
+ *   w         E4M3 codes [n_rows][hidden], row-major, head order as above
+ *   w_packed  output, pa_packed_weight_bytes(PA_MODE_DECODE, ...) bytes
+ * n_rows must be (19 nkv + 1) * 128 for nkv in {1, 2, 4}. */
+int pa_pack_weight_decode(const uint8_t* w, uint8_t* w_packed, int32_t n_rows,
+                          int32_t hidden, void* stream);
+
+/* Prefill weight: MXFP8 codes plus one E8M0 scale per 32-wide k block (the
+ * epilogue page's K-major MXFP8 weight and its scales), repacked for the
+ * library's MFMA tiles.
+ *   w         E4M3 codes [n_rows][hidden]
+ *   w_e8m0    E8M0 codes [n_rows][hidden / 32]
+ *   w_packed  output, pa_packed_weight_bytes(PA_MODE_PREFILL, ...) bytes
+ *   s_packed  output, pa_packed_scale_bytes(PA_MODE_PREFILL, ...) bytes */
+int pa_pack_weight_prefill(const uint8_t* w, const uint8_t* w_e8m0, uint8_t* w_packed,
+                           uint8_t* s_packed, int32_t n_rows, int32_t hidden,
+                           void* stream);
+
+/* Decode prologue (per-token FP8 activations, per-row FP8 weight scales).
+ *   w_packed  from pa_pack_weight_decode;  w_scale  float [N] per output row.
+ * tokens <= PA_DECODE_MAX_TOKENS. */
+int pre_attn_decode(const pa_dims* dims, const uint16_t* ar, const uint16_t* res,
+                    uint16_t* h_out, const uint16_t* g_in, const uint8_t* w_packed,
+                    const float* w_scale, const uint16_t* g_q, const uint16_t* g_k,
+                    const uint16_t* g_iq, const uint16_t* g_ik, const uint16_t* cos_sin,
+                    const int64_t* positions, const int64_t* slot_mapping,
+                    uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                    uint8_t* index_cache, uint16_t* q_out, uint16_t* iq_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Prefill prologue (MXFP8 activations and weight).
+ *   w_packed, s_packed  from pa_pack_weight_prefill. */
+int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* res,
+                     uint16_t* h_out, const uint16_t* g_in, const uint8_t* w_packed,
+                     const uint8_t* s_packed, const uint16_t* g_q, const uint16_t* g_k,
+                     const uint16_t* g_iq, const uint16_t* g_ik, const uint16_t* cos_sin,
+                     const int64_t* positions, const int64_t* slot_mapping,
+                     uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                     uint8_t* index_cache, uint16_t* q_out, uint16_t* iq_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Instrumentation: from now on, calls on this host thread record `start` and
+ * `stop` (hipEvent_t, created by the caller) on their stream immediately
+ * before and after their dominant kernel (decode: the projection GEMV;
+ * prefill: the MFMA GEMM with the fused epilogue), so that
+ * hipEventElapsedTime gives that kernel's duration. Both NULL turns it off.
+ * The events stay owned by the caller. */
+int pa_set_kernel_events(void* start, void* stop);
+
+/* Static text for a pa_status value. */
+const char* pa_strerror(int status);
+
+/* Detail of the last PA_ERR_HIP on the calling thread ("" if none). */
+const char* pa_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRE_ATTN_H */

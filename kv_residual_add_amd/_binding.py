@@ -1,0 +1,245 @@
+"""ctypes binding of libpre_attn.so (declared in include/pre_attn.h).
+
+The functions keep the C names and argument order. They only marshal: torch
+tensors become device pointers after dtype / size / device checks (the C ABI
+cannot see buffer sizes, so the checks here keep every kernel access inside
+the caller's tensors), and the stream defaults to torch's current stream.
+Every step of the prologue runs in the HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpre_attn.so")
+
+PA_MODE_DECODE = 0
+PA_MODE_PREFILL = 1
+HEAD_DIM = 128
+PAGE = 16
+PAGE_BYTES = 2048
+DECODE_MAX_TOKENS = 64
+
+EXPORTS = (
+    "pa_workspace_bytes",
+    "pa_workspace_init",
+    "pa_packed_weight_bytes",
+    "pa_packed_scale_bytes",
+    "pa_pack_weight_decode",
+    "pa_pack_weight_prefill",
+    "pre_attn_decode",
+    "pre_attn_prefill",
+    "pa_set_kernel_events",
+    "pa_strerror",
+    "pa_last_error_detail",
+)
+
+
+class pa_dims(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("nkv", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pos", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.pa_strerror(status).decode()
+        detail = lib.pa_last_error_detail().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python kv_residual_add_amd/build.py`"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        sz = ctypes.c_size_t
+        i32 = ctypes.c_int32
+        dims_p = ctypes.POINTER(pa_dims)
+        lib.pa_workspace_bytes.argtypes = [dims_p, ctypes.c_int]
+        lib.pa_workspace_bytes.restype = sz
+        lib.pa_workspace_init.argtypes = [P, sz, P]
+        lib.pa_workspace_init.restype = ctypes.c_int
+        lib.pa_packed_weight_bytes.argtypes = [ctypes.c_int, i32, i32]
+        lib.pa_packed_weight_bytes.restype = sz
+        lib.pa_packed_scale_bytes.argtypes = [ctypes.c_int, i32, i32]
+        lib.pa_packed_scale_bytes.restype = sz
+        lib.pa_pack_weight_decode.argtypes = [P, P, i32, i32, P]
+        lib.pa_pack_weight_decode.restype = ctypes.c_int
+        lib.pa_pack_weight_prefill.argtypes = [P, P, P, P, i32, i32, P]
+        lib.pa_pack_weight_prefill.restype = ctypes.c_int
+        lib.pre_attn_decode.argtypes = [dims_p] + [P] * 21 + [sz, P]
+        lib.pre_attn_decode.restype = ctypes.c_int
+        lib.pre_attn_prefill.argtypes = [dims_p] + [P] * 21 + [sz, P]
+        lib.pre_attn_prefill.restype = ctypes.c_int
+        lib.pa_set_kernel_events.argtypes = [P, P]
+        lib.pa_set_kernel_events.restype = ctypes.c_int
+        lib.pa_strerror.argtypes = [ctypes.c_int]
+        lib.pa_strerror.restype = ctypes.c_char_p
+        lib.pa_last_error_detail.argtypes = []
+        lib.pa_last_error_detail.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def make_dims(tokens, hidden, nkv, num_pages, max_pos, eps) -> pa_dims:
+    return pa_dims(int(tokens), int(hidden), int(nkv), int(num_pages), int(max_pos), float(eps))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor, name: str, dtype, numel: int, device) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PaError(status, where)
+
+
+def pa_set_kernel_events(start, stop) -> None:
+    """Record torch.cuda.Event pair (or None, None) around the dominant kernel of
+    later calls on this thread (see include/pre_attn.h)."""
+    ps = None if start is None else start.cuda_event
+    pe = None if stop is None else stop.cuda_event
+    _check(load().pa_set_kernel_events(ps, pe), "pa_set_kernel_events")
+
+
+def pa_workspace_bytes(dims: pa_dims, mode: int) -> int:
+    return load().pa_workspace_bytes(ctypes.byref(dims), mode)
+
+
+def pa_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    _check(load().pa_workspace_init(workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "pa_workspace_init")
+
+
+def pa_packed_weight_bytes(mode: int, n_rows: int, hidden: int) -> int:
+    return load().pa_packed_weight_bytes(mode, n_rows, hidden)
+
+
+def pa_packed_scale_bytes(mode: int, n_rows: int, hidden: int) -> int:
+    return load().pa_packed_scale_bytes(mode, n_rows, hidden)
+
+
+def pa_pack_weight_decode(w: torch.Tensor, w_packed: torch.Tensor, stream=None) -> None:
+    n, k = w.shape
+    dev = w.device
+    nb = pa_packed_weight_bytes(PA_MODE_DECODE, n, k)
+    if nb == 0:
+        raise ValueError(f"unsupported weight shape {tuple(w.shape)}")
+    _check(load().pa_pack_weight_decode(
+        _ptr(w, "w", torch.uint8, n * k, dev), _ptr(w_packed, "w_packed", torch.uint8, nb, dev),
+        n, k, _stream(stream)), "pa_pack_weight_decode")
+
+
+def pa_pack_weight_prefill(w: torch.Tensor, w_e8m0: torch.Tensor, w_packed: torch.Tensor,
+                           s_packed: torch.Tensor, stream=None) -> None:
+    n, k = w.shape
+    dev = w.device
+    nb = pa_packed_weight_bytes(PA_MODE_PREFILL, n, k)
+    ns = pa_packed_scale_bytes(PA_MODE_PREFILL, n, k)
+    if nb == 0:
+        raise ValueError(f"unsupported weight shape {tuple(w.shape)}")
+    _check(load().pa_pack_weight_prefill(
+        _ptr(w, "w", torch.uint8, n * k, dev),
+        _ptr(w_e8m0, "w_e8m0", torch.uint8, n * k // 32, dev),
+        _ptr(w_packed, "w_packed", torch.uint8, nb, dev),
+        _ptr(s_packed, "s_packed", torch.uint8, ns, dev),
+        n, k, _stream(stream)), "pa_pack_weight_prefill")
+
+
+def _run(fn_name: str, mode: int, dims: pa_dims, ar, res, h_out, g_in, w_packed, w_scales,
+         g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+         v_scale, index_cache, q_out, iq_out, workspace, stream):
+    S, K, nkv = dims.tokens, dims.hidden, dims.nkv
+    P, L = dims.num_pages, dims.max_pos
+    N = (19 * nkv + 1) * HEAD_DIM
+    dev = ar.device
+    bf, u8, f32, i64 = torch.bfloat16, torch.uint8, torch.float32, torch.int64
+    ws_need = pa_workspace_bytes(dims, mode)
+    if ws_need == 0:
+        # let the library name the invalid dimension
+        _check(getattr(load(), fn_name)(ctypes.byref(dims), *([None] * 21), 0, None), fn_name)
+    if workspace.numel() < ws_need:
+        raise ValueError(f"workspace: need {ws_need} bytes, got {workspace.numel()}")
+    if mode == PA_MODE_DECODE:
+        wp = _ptr(w_packed, "w_packed", u8, pa_packed_weight_bytes(mode, N, K), dev)
+        sc = _ptr(w_scales, "w_scale", f32, N, dev)
+    else:
+        wp = _ptr(w_packed, "w_packed", u8, pa_packed_weight_bytes(mode, N, K), dev)
+        sc = _ptr(w_scales, "s_packed", u8, pa_packed_scale_bytes(mode, N, K), dev)
+    args = [
+        _ptr(ar, "ar", bf, S * K, dev), _ptr(res, "res", bf, S * K, dev),
+        _ptr(h_out, "h_out", bf, S * K, dev), _ptr(g_in, "g_in", bf, K, dev), wp, sc,
+        _ptr(g_q, "g_q", bf, HEAD_DIM, dev), _ptr(g_k, "g_k", bf, HEAD_DIM, dev),
+        _ptr(g_iq, "g_iq", bf, HEAD_DIM, dev), _ptr(g_ik, "g_ik", bf, HEAD_DIM, dev),
+        _ptr(cos_sin, "cos_sin", bf, L * 64, dev),
+        _ptr(positions, "positions", i64, S, dev), _ptr(slot_mapping, "slot_mapping", i64, S, dev),
+        _ptr(k_cache, "k_cache", u8, P * nkv * PAGE_BYTES, dev),
+        _ptr(v_cache, "v_cache", u8, P * nkv * PAGE_BYTES, dev),
+        _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
+        _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
+        _ptr(index_cache, "index_cache", u8, P * PAGE * HEAD_DIM, dev),
+        _ptr(q_out, "q_out", bf, S * 16 * nkv * HEAD_DIM, dev),
+        _ptr(iq_out, "iq_out", bf, S * nkv * HEAD_DIM, dev),
+        workspace.data_ptr(),
+    ]
+    if workspace.dtype != u8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = getattr(load(), fn_name)(ctypes.byref(dims), *args, workspace.numel(), _stream(stream))
+    _check(st, fn_name)
+
+
+def pre_attn_decode(dims, ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik,
+                    cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                    index_cache, q_out, iq_out, workspace, stream=None) -> None:
+    """Decode prologue; argument meaning as in include/pre_attn.h."""
+    _run("pre_attn_decode", PA_MODE_DECODE, dims, ar, res, h_out, g_in, w_packed, w_scale,
+         g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+         v_scale, index_cache, q_out, iq_out, workspace, stream)
+
+
+def pre_attn_prefill(dims, ar, res, h_out, g_in, w_packed, s_packed, g_q, g_k, g_iq, g_ik,
+                     cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                     index_cache, q_out, iq_out, workspace, stream=None) -> None:
+    """Prefill prologue; argument meaning as in include/pre_attn.h."""
+    _run("pre_attn_prefill", PA_MODE_PREFILL, dims, ar, res, h_out, g_in, w_packed, s_packed,
+         g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+         v_scale, index_cache, q_out, iq_out, workspace, stream)

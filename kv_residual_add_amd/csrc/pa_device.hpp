@@ -1,0 +1,84 @@
+// Device helpers for the prologue kernels (gfx950, wave64).
+//
+// Number formats: bf16 is the top half of an IEEE binary32 rounded to nearest
+// even; E4M3 is OCP E4M3FN (bias 7, max 448, no infinities, S.1111.111 = NaN),
+// produced here by round-to-nearest-even with saturation at +-448, the FP8
+// rounding the K1 mono_pre page (vllm.models.minimax_m3.amd.mono.kernels.pre_attn)
+// applies to activations and to the K / V / index_k caches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;
+constexpr int kRotary = 64;
+constexpr int kPage = 16;
+constexpr int kPageBytes = kPage * kHeadDim;
+constexpr double kFp8Max = 448.0;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return ((b >> 16) | 0x40u) & 0xffffu;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// float64 -> E4M3 code, saturating round-to-nearest-even. Within a binade
+// [2^e, 2^(e+1)) (e >= -6) the codes are spaced 2^(e-3); below 2^-6 the step
+// is 2^-9. Scaling by a power of two is exact, so rint() on the scaled
+// magnitude is the exact RNE and the code is the grid index from zero.
+__device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
+  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t sign = static_cast<uint32_t>(bits >> 56) & 0x80u;
+  double a = __builtin_fabs(v);
+  a = a < kFp8Max ? a : kFp8Max;
+  uint32_t code;
+  if (a < 0x1p-6) {
+    code = static_cast<uint32_t>(__builtin_rint(a * 512.0));
+  } else {
+    const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(a)) >> 52) & 0x7ff) - 1023;
+    const double scale = __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
+    code = static_cast<uint32_t>((e + 6) * 8) + static_cast<uint32_t>(__builtin_rint(a * scale));
+  }
+  return sign | code;
+}
+
+// Wave64 reductions (xor butterflies; every lane ends with the result).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double o = __shfl_xor(v, m, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Page-16 addressing of a slot at the default (contiguous) page stride.
+__device__ __forceinline__ int64_t slot_page(int64_t slot) { return slot >> 4; }
+__device__ __forceinline__ int slot_row(int64_t slot) { return static_cast<int>(slot & 15); }
+
+}  // namespace pa

@@ -1,0 +1,89 @@
+"""Device-side set-up for one prologue call: uploads host arrays (raw bits in
+numpy, the layouts of include/pre_attn.h), packs the weight once, allocates and
+initializes the workspace, and calls pre_attn_decode / pre_attn_prefill.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+_BF16_KEYS = ("ar", "res", "g_in", "g_q", "g_k", "g_iq", "g_ik", "cos_sin")
+
+
+def _to_dev(a: np.ndarray, device, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+class Problem:
+    """All device buffers of one prologue call."""
+
+    def __init__(self, arrays: dict, device="cuda:0"):
+        self.device = torch.device(device)
+        self.mode = B.PA_MODE_DECODE if arrays["mode"] == "decode" else B.PA_MODE_PREFILL
+        S, K = arrays["ar"].shape
+        self.nkv = int(arrays["nkv"])
+        self.N = (19 * self.nkv + 1) * B.HEAD_DIM
+        self.dims = B.make_dims(S, K, self.nkv, arrays["k_cache"].shape[0],
+                                arrays["cos_sin"].shape[0], float(arrays["eps"]))
+        dev = self.device
+        t = {}
+        for k in _BF16_KEYS:
+            t[k] = _to_dev(arrays[k].view(np.int16), dev, torch.bfloat16)
+        for k in ("positions", "slot_mapping"):
+            t[k] = _to_dev(arrays[k].astype(np.int64), dev)
+        for k in ("k_cache", "v_cache", "index_cache"):
+            t[k] = _to_dev(arrays[k], dev)
+        for k in ("k_scale", "v_scale"):
+            t[k] = _to_dev(arrays[k], dev)
+        t["h_out"] = torch.empty((S, K), dtype=torch.bfloat16, device=dev)
+        t["q_out"] = torch.empty((S, 16 * self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        t["iq_out"] = torch.empty((S, self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.t = t
+        self.set_weight(arrays)
+        nbytes = B.pa_workspace_bytes(self.dims, self.mode)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        B.pa_workspace_init(self.workspace)
+
+    def set_weight(self, arrays: dict) -> None:
+        dev = self.device
+        K = self.dims.hidden
+        w = _to_dev(arrays["w"], dev)
+        nb = B.pa_packed_weight_bytes(self.mode, self.N, K)
+        self.w_packed = torch.empty(nb, dtype=torch.uint8, device=dev)
+        if self.mode == B.PA_MODE_DECODE:
+            B.pa_pack_weight_decode(w, self.w_packed)
+            self.w_scales = _to_dev(arrays["w_scale"].astype(np.float32), dev)
+        else:
+            we = _to_dev(arrays["w_e8m0"], dev)
+            ns = B.pa_packed_scale_bytes(self.mode, self.N, K)
+            self.w_scales = torch.empty(ns, dtype=torch.uint8, device=dev)
+            B.pa_pack_weight_prefill(w, we, self.w_packed, self.w_scales)
+
+    def args(self, w_packed=None, w_scales=None, **over):
+        t = dict(self.t, **over)
+        return (self.dims, t["ar"], t["res"], t["h_out"], t["g_in"],
+                self.w_packed if w_packed is None else w_packed,
+                self.w_scales if w_scales is None else w_scales,
+                t["g_q"], t["g_k"], t["g_iq"], t["g_ik"], t["cos_sin"], t["positions"],
+                t["slot_mapping"], t["k_cache"], t["v_cache"], t["k_scale"], t["v_scale"],
+                t["index_cache"], t["q_out"], t["iq_out"], self.workspace)
+
+    def run(self, stream=None, **over) -> None:
+        fn = B.pre_attn_decode if self.mode == B.PA_MODE_DECODE else B.pre_attn_prefill
+        fn(*self.args(**over), stream=stream)
+
+    def outputs(self) -> dict:
+        """Outputs and caches as numpy raw bits (synchronizes)."""
+        torch.cuda.synchronize(self.device)
+        out = {}
+        for k in ("h_out", "q_out", "iq_out"):
+            out[k] = self.t[k].view(torch.int16).cpu().numpy().view(np.uint16)
+        for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
+            out[k] = self.t[k].cpu().numpy()
+        return out

@@ -1,0 +1,134 @@
+"""Comparison of the HIP path's outputs with the oracle's, to the tolerances the
+prologue's contract states:
+
+  h_out                         bit-exact
+  q_out, iq_out (bf16)          |got - ref| <= 2e-2 |ref| + 1e-3 rms(ref head)
+  which cache bytes / scales    bit-exact set (caches start as sentinels)
+  FP8 cache codes               code distance <= 1, in at most 0.1% of codes
+  K / V scales                  relative difference <= 1e-6
+
+Code distance: |ord(a) - ord(b)| with ord(c) = +-(c & 0x7F) by the sign bit,
+so +0 and -0 are equal.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import codecs
+
+Q_RTOL = 2e-2
+Q_ATOL_RMS = 1e-3
+CODE_FRAC = 1e-3
+SCALE_RTOL = 1e-6
+
+
+def subset(inp: dict, rows) -> dict:
+    """The same call restricted to token rows `rows` (fresh sentinel caches)."""
+    rows = np.asarray(rows)
+    out = dict(inp)
+    for k in ("ar", "res", "positions", "slot_mapping"):
+        out[k] = inp[k][rows]
+    return out
+
+
+def code_ord(c):
+    c = np.asarray(c, np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def _bf16(a):
+    return codecs.bf16_bits_to_f64(a)
+
+
+def compare(inp: dict, ref: dict, got: dict, rows=None) -> dict:
+    """Asserts parity of `got` (GPU, all tokens) against `ref` (oracle on the
+    tokens `rows`, all tokens if None). Returns statistics."""
+    S = inp["ar"].shape[0]
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    stats = {}
+    assert np.array_equal(got["h_out"][rows], ref["h_out"]), "h_out differs"
+    for key in ("q_out", "iq_out"):
+        g = _bf16(got[key][rows])
+        r = _bf16(ref[key])
+        rms = np.sqrt((r * r).mean(axis=-1, keepdims=True))
+        bound = Q_RTOL * np.abs(r) + Q_ATOL_RMS * rms
+        err = np.abs(g - r)
+        bad = err > bound
+        stats[key + "_max_rel"] = float((err / np.maximum(np.abs(r), 1e-30)).max())
+        assert not bad.any(), f"{key}: {int(bad.sum())} elements out of tolerance"
+
+    slots = np.asarray(inp["slot_mapping"])[rows]
+    nkv = int(inp["nkv"])
+    live = slots >= 0
+    # written-byte sets at the sampled tokens' slots: bit-exact
+    codes_g, codes_r = [], []
+    for s, slot in zip(rows, slots):
+        if slot < 0:
+            continue
+        page, t = slot // 16, slot % 16
+        for name in ("k_cache", "v_cache"):
+            codes_g.append(got[name][page, :, :].reshape(nkv, 2048))
+            codes_r.append(ref[name][page, :, :].reshape(nkv, 2048))
+        codes_g.append(got["index_cache"][slot][None])
+        codes_r.append(ref["index_cache"][slot][None])
+    if codes_g:
+        # whole pages: other tokens of the full run may share a page, so only
+        # positions the oracle wrote are compared, and they must be written
+        g = np.concatenate([c.reshape(-1) for c in codes_g])
+        r = np.concatenate([c.reshape(-1) for c in codes_r])
+        wr = r != 0x7F
+        assert np.all(g[wr] != 0x7F), "a byte the oracle writes was not written"
+        d = np.abs(code_ord(g[wr]) - code_ord(r[wr]))
+        stats["code_max_dist"] = int(d.max()) if d.size else 0
+        stats["code_frac_diff"] = float((d > 0).mean()) if d.size else 0.0
+        assert d.max(initial=0) <= 1, f"FP8 code distance {d.max()} > 1"
+        assert (d > 0).mean() <= CODE_FRAC, f"{(d > 0).mean():.2e} of codes differ"
+    ks_g, ks_r = [], []
+    for s, slot in zip(rows, slots):
+        if slot < 0:
+            continue
+        page, t = slot // 16, slot % 16
+        for name in ("k_scale", "v_scale"):
+            ks_g.append(got[name][page, :, t])
+            ks_r.append(ref[name][page, :, t])
+    if ks_g:
+        g = np.concatenate(ks_g).astype(np.float64)
+        r = np.concatenate(ks_r).astype(np.float64)
+        rel = np.abs(g - r) / np.abs(r)
+        stats["scale_max_rel"] = float(rel.max())
+        assert rel.max() <= SCALE_RTOL, f"K/V scale rel diff {rel.max():.3e} > 1e-6"
+    stats["live_slots"] = int(live.sum())
+    return stats
+
+
+def expected_written_masks(inp: dict) -> dict:
+    """Which cache bytes / scale entries a call must write, from the slots alone."""
+    nkv = int(inp["nkv"])
+    P = inp["k_cache"].shape[0]
+    k = np.zeros((P, nkv, 2048), bool)
+    v = np.zeros((P, nkv, 2048), bool)
+    ks = np.zeros((P, nkv, 16), bool)
+    ic = np.zeros(inp["index_cache"].shape, bool)
+    d = np.arange(128)
+    for slot in np.asarray(inp["slot_mapping"]):
+        if slot < 0:
+            continue
+        page, t = slot // 16, slot % 16
+        k[page, :, (d // 16) * 256 + t * 16 + d % 16] = True
+        v[page, :, d * 16 + t] = True
+        ks[page, :, t] = True
+        ic[slot, :] = True
+    return {"k_cache": k, "v_cache": v, "k_scale": ks, "v_scale": ks, "index_cache": ic}
+
+
+def check_written_sets(inp: dict, got: dict) -> None:
+    """Bytes that changed from the sentinels are exactly the slots' bytes."""
+    masks = expected_written_masks(inp)
+    for name in ("k_cache", "v_cache", "index_cache"):
+        changed = got[name] != inp[name]
+        assert np.array_equal(changed, masks[name]), f"{name}: written-byte set differs"
+    for name in ("k_scale", "v_scale"):
+        changed = got[name].view(np.uint32) != inp[name].view(np.uint32)
+        assert np.array_equal(changed, masks[name]), f"{name}: written-entry set differs"
+        assert np.all(np.isfinite(got[name][masks[name]])), f"{name}: non-finite scale"

@@ -1,0 +1,118 @@
+"""Host-side checks of libpre_attn.so that need no GPU: it loads, exports every
+function include/pre_attn.h declares, sizes its workspace and packed weights,
+and rejects invalid arguments before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_residual_add_amd as K
+from kv_residual_add_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pre_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_api():
+    assert _declared_functions() == sorted(B.EXPORTS)
+
+
+@pytest.mark.parametrize("name", _declared_functions())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(B.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def _dims(**kw):
+    base = dict(tokens=8, hidden=6144, nkv=1, num_pages=2048, max_pos=32768, eps=1e-6)
+    base.update(kw)
+    return K.make_dims(**base)
+
+
+def test_workspace_sizes():
+    dec = K.pa_workspace_bytes(_dims(), K.PA_MODE_DECODE)
+    # x8 (8 x 6144) + scales + k-slice partials (8 slices x 8 x 2560 f32) + counters
+    assert dec >= 8 * 6144 + 8 * 2560 * 4
+    pre = K.pa_workspace_bytes(_dims(tokens=8192, nkv=4, num_pages=512, max_pos=2048),
+                               K.PA_MODE_PREFILL)
+    assert pre >= 8192 * 6144 + 8192 * 6144 // 32
+    assert K.pa_workspace_bytes(_dims(tokens=65), K.PA_MODE_DECODE) == 0
+    assert K.pa_workspace_bytes(_dims(tokens=65), K.PA_MODE_PREFILL) > 0
+    assert K.pa_workspace_bytes(_dims(nkv=3), K.PA_MODE_DECODE) == 0
+    assert K.pa_workspace_bytes(_dims(hidden=6100), K.PA_MODE_DECODE) == 0
+    assert K.pa_workspace_bytes(_dims(), 7) == 0
+
+
+def test_packed_sizes():
+    assert K.pa_packed_weight_bytes(0, 2560, 6144) == 2560 * 6144
+    assert K.pa_packed_weight_bytes(1, 9856, 6144) == 9856 * 6144
+    assert K.pa_packed_scale_bytes(1, 9856, 6144) == 9856 * 6144 // 32
+    assert K.pa_packed_weight_bytes(0, 2561, 6144) == 0
+    assert K.pa_packed_weight_bytes(0, 19 * 3 * 128 + 128, 6144) == 0  # nkv = 3
+
+
+def _call(fn, dims, ptrs=None, ws_bytes=1 << 30):
+    lib = B.load()
+    if ptrs is None:
+        ptrs = [4096 * (i + 1) for i in range(21)]  # never dereferenced: rejected first
+    return getattr(lib, fn)(ctypes.byref(dims) if dims is not None else None, *ptrs,
+                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["pre_attn_decode", "pre_attn_prefill"])
+def test_invalid_arguments_rejected(fn):
+    lib = B.load()
+    assert _call(fn, None) == -1  # NULL dims
+    assert _call(fn, _dims(nkv=3)) == -3
+    assert _call(fn, _dims(hidden=100)) == -4
+    assert _call(fn, _dims(hidden=20000 // 128 * 128)) == -4
+    assert _call(fn, _dims(tokens=0)) == -5
+    assert _call(fn, _dims(num_pages=0)) == -7
+    assert _call(fn, _dims(eps=float("nan"))) == -7
+    ptrs = [4096 * (i + 1) for i in range(21)]
+    ptrs[3] = None
+    assert _call(fn, _dims(), ptrs) == -1
+    ptrs = [4096 * (i + 1) for i in range(21)]
+    ptrs[0] += 8  # ar not 16-byte aligned
+    assert _call(fn, _dims(), ptrs) == -2
+    ptrs = [4096 * (i + 1) for i in range(21)]
+    ptrs[11] += 4  # positions not 8-byte aligned
+    assert _call(fn, _dims(), ptrs) == -2
+    assert _call(fn, _dims(), ws_bytes=16) == -6
+    assert lib.pa_strerror(-6).decode().startswith("workspace")
+
+
+def test_decode_token_limit():
+    assert _call("pre_attn_decode", _dims(tokens=65)) == -5
+    # prefill accepts 65 tokens; the tiny workspace stops it before any launch
+    assert _call("pre_attn_prefill", _dims(tokens=65), ws_bytes=16) == -6
+
+
+def test_pack_rejects_bad_shapes():
+    lib = B.load()
+    assert lib.pa_pack_weight_decode(None, 4096, 2560, 6144, None) == -1
+    assert lib.pa_pack_weight_decode(4096, 8192, 2560, 6100, None) == -4
+    assert lib.pa_pack_weight_decode(4096, 8192, 2600, 6144, None) == -3
+    assert lib.pa_pack_weight_prefill(4096, 8192, 12288, 16384, 2560, 6144 + 8, None) == -4
+
+
+def test_strerror_covers_all_codes():
+    lib = B.load()
+    for code in range(0, -11, -1):
+        assert lib.pa_strerror(code).decode() != "unknown status"
+    assert lib.pa_strerror(-99).decode() == "unknown status"
+
+
+def test_binding_requires_built_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libpre_attn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load()
