@@ -8,11 +8,12 @@
 //                       vllm.models.minimax_m3.amd.mono.kernels.pre_attn,
 //                       emit_pre_attn: norm_quant).
 //   2. decode_gemv      the fused projection as an HBM-bound GEMV: each CTA
-//                       owns 64 output rows x a k slice; every wave streams its
-//                       16 rows' packed weight with dwordx4 loads issued before
-//                       anything waits on them, the FP8 activation slice sits
-//                       in LDS, and 16x16x128 FP8 MFMAs take up to 16 tokens a
-//                       column group. k-slice partial sums go to the workspace.
+//                       owns one 128-row head x a k slice; every wave streams
+//                       its 32 rows' packed weight with dwordx4 loads issued
+//                       before anything waits on them, the FP8 activation slice
+//                       sits in LDS, and 32x32x16 bf16 MFMAs take up to 32
+//                       tokens a tile on exactly widened FP8 codes. k-slice
+//                       partial sums go to the workspace.
 //   3. decode_epilogue  one wave per (token, head): sums the k-slice partials,
 //                       applies the activation and row scales, then the head's
 //                       role (pre_attn page, head tasks; head_norm_rope; the
@@ -21,8 +22,10 @@
 //
 // Numerics: the input norm, its FP8 decision and the head epilogue run in
 // float64 with contraction off, so a code is decided from the same value the
-// float64 statement of the method gives; the projection accumulates products
-// exactly inside each MFMA and in float32 across at most 8 MFMAs per k slice.
+// float64 statement of the method gives; the projection's products are exact
+// and accumulate in float32 (FP8-input MFMAs sum at lower internal precision,
+// which moves the per-token K / V scales by ~1e-5, so the codes are widened to
+// bf16 first).
 #include <hip/hip_runtime.h>
 
 #include "pa_device.hpp"
@@ -32,8 +35,6 @@ namespace pa {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kGemvWaves = 4;
-constexpr int kRowsPerCta = 16 * kGemvWaves;
 constexpr int kLdsPad = 16;
 constexpr int kMaxLds = 64 * 1024;
 
@@ -136,32 +137,32 @@ __global__ __launch_bounds__(kNormThreads) void decode_norm(
 }
 
 // ---------------------------------------------------------------------------
-// 2. GEMV partials. Packed weight: for 16-row group rg and 128-wide k chunk c,
-//    a 2 KB block at (rg * K/128 + c) * 2048; lane l's A operand (row l % 16,
-//    k = 128c + 32(l/16) + [0,32)) is bytes [16l, 16l+16) then
-//    [1024 + 16l, 1024 + 16l + 16), so each dwordx4 wave load is 1 KB contiguous.
-//    The activation B operand takes the same k order from LDS, so the dot
-//    product needs no shuffles. Tokens past S reuse token S-1 (never stored).
-template <int CPC>
+// 2. GEMV partials. Packed weight: head h, 128-wide k chunk c, 32-row tile m ->
+//    a 4 KB block at ((h * K/128 + c) * 4 + m) * 4096. Its dwordx4 piece q of
+//    lane l sits at q * 1024 + 16 l (each wave load is 1 KB contiguous) and holds
+//    row 32m + l % 32 for MFMA steps j = 2q and 2q + 1, each 8 codes at
+//    k = 128c + 16j + 8 (l / 32) + [0, 8). The activation B operand takes the
+//    same k from LDS, so the dot product needs no shuffles. Tokens past S reuse
+//    token S-1 and are never stored. NT = 32-token tiles (1 or 2).
+template <int CPC, int NT>
 __global__ __launch_bounds__(256) void decode_gemv(
     const uint8_t* __restrict__ x8, const uint8_t* __restrict__ wp, float* __restrict__ part,
     int S, int K, int N) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = blockIdx.x * kGemvWaves + wave;
-  const int ks = blockIdx.y;
+  const int h = blockIdx.x, ks = blockIdx.y;
   const int nchk = K >> 7;
   const int c0 = ks * CPC;
   constexpr int ldw = CPC * 128 + kLdsPad;
 
   // the weight stream first: nothing waits on it until the MFMAs
-  i32x4 wv[CPC][2];
-  const uint8_t* wb = wp + (static_cast<size_t>(rg) * nchk + c0) * 2048 + lane * 16;
+  i32x4 wv[CPC][4];
+  const uint8_t* wb = wp + ((static_cast<size_t>(h) * nchk + c0) * 4 + wave) * 4096 + lane * 16;
 #pragma unroll
-  for (int c = 0; c < CPC; ++c) {
-    wv[c][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 2048));
-    wv[c][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 2048 + 1024));
-  }
+  for (int c = 0; c < CPC; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
   // the FP8 activation slice of every token into LDS
   const int per_row = CPC * 8;  // 16-byte pieces per token row
   for (int i = tid; i < S * per_row; i += 256) {
@@ -171,26 +172,41 @@ __global__ __launch_bounds__(256) void decode_gemv(
   }
   __syncthreads();
 
-  const int ngroups = (S + 15) >> 4;
-  const int kq = (lane >> 4) * 32;
-  for (int g = 0; g < ngroups; ++g) {
-    const int tok = min(g * 16 + (lane & 15), S - 1);
-    const uint8_t* brow = lds + tok * ldw + kq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int hh = lane >> 5;
+  const uint8_t* brow[NT];
 #pragma unroll
-    for (int c = 0; c < CPC; ++c) {
-      const i32x4 b0 = *reinterpret_cast<const i32x4*>(brow + c * 128);
-      const i32x4 b1 = *reinterpret_cast<const i32x4*>(brow + c * 128 + 16);
-      const i32x8 A = {wv[c][0][0], wv[c][0][1], wv[c][0][2], wv[c][0][3],
-                       wv[c][1][0], wv[c][1][1], wv[c][1][2], wv[c][1][3]};
-      const i32x8 B = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      // E4M3 x E4M3 (format 0 / 0), unit E8M0 scales (127)
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 127, 0, 127);
+  for (int tt = 0; tt < NT; ++tt) brow[tt] = lds + min(tt * 32 + (lane & 31), S - 1) * ldw + 8 * hh;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tt][r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPC; ++c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const i32x4& w = wv[c][j >> 1];
+      const bf16x8 A = fp8x8_to_bf16(w[2 * (j & 1)], w[2 * (j & 1) + 1], 1.0f);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const uint2 bv = *reinterpret_cast<const uint2*>(brow[tt] + c * 128 + 16 * j);
+        const bf16x8 B = fp8x8_to_bf16(bv.x, bv.y, 1.0f);
+        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[tt], 0, 0, 0);
+      }
     }
-    const int t = g * 16 + (lane & 15);
+  }
+  // D[i][j]: token j = lane % 32, row i = 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    pin_registers(acc[tt]);
+    const int t = tt * 32 + (lane & 31);
     if (t < S) {
-      const int n0 = rg * 16 + (lane >> 4) * 4;
-      *reinterpret_cast<f32x4*>(part + (static_cast<size_t>(ks) * S + t) * N + n0) = acc;
+      float* dst = part + (static_cast<size_t>(ks) * S + t) * N + h * kHeadDim + wave * 32 + 4 * hh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[tt][4 * q], acc[tt][4 * q + 1], acc[tt][4 * q + 2], acc[tt][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(dst + 8 * q) = v;
+      }
     }
   }
 }
@@ -286,14 +302,18 @@ __global__ void pack_decode(const uint8_t* __restrict__ w, uint8_t* __restrict__
   const size_t pieces = static_cast<size_t>(N) * K / 16;
   if (idx >= pieces) return;
   const int nchk = K >> 7;
-  const size_t b = idx >> 7;
-  const int p = static_cast<int>(idx & 127);
-  const int rg = static_cast<int>(b / nchk), c = static_cast<int>(b % nchk);
-  const int half = p >> 6, l = p & 63;
-  const int row = rg * 16 + (l & 15);
-  const int k = c * 128 + (l >> 4) * 32 + half * 16;
-  const i32x4 v = *reinterpret_cast<const i32x4*>(w + static_cast<size_t>(row) * K + k);
-  *reinterpret_cast<i32x4*>(wp + b * 2048 + half * 1024 + l * 16) = v;
+  const size_t blk = idx >> 8;  // 4 KB blocks of 256 pieces
+  const int p = static_cast<int>(idx & 255);
+  const int q = p >> 6, l = p & 63;
+  const int m = static_cast<int>(blk & 3);
+  const size_t hc = blk >> 2;
+  const int h = static_cast<int>(hc / nchk), c = static_cast<int>(hc % nchk);
+  const int row = h * kHeadDim + m * 32 + (l & 31);
+  const uint8_t* src = w + static_cast<size_t>(row) * K + c * 128 + 8 * (l >> 5);
+  // steps j = 2q (bytes 0..7) and 2q + 1 (bytes 8..15)
+  const uint2 lo = *reinterpret_cast<const uint2*>(src + 16 * (2 * q));
+  const uint2 hi = *reinterpret_cast<const uint2*>(src + 16 * (2 * q + 1));
+  *reinterpret_cast<uint4*>(wp + blk * 4096 + q * 1024 + l * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 __global__ void fill_zero(uint32_t* p, size_t n) {
@@ -306,9 +326,14 @@ template <int CPC>
 hipError_t launch_gemv_cpc(const Args& a, const DecodePlan& p) {
   const int N = a.N();
   const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
-  dim3 grid(N / kRowsPerCta, p.ksplit);
-  hipLaunchKernelGGL(decode_gemv<CPC>, grid, dim3(256), lds, a.stream, a.ws + p.off_x8, a.w_packed,
-                     reinterpret_cast<float*>(a.ws + p.off_part), a.S, a.K, N);
+  dim3 grid(a.heads(), p.ksplit);
+  float* part = reinterpret_cast<float*>(a.ws + p.off_part);
+  if (a.S <= 32)
+    hipLaunchKernelGGL((decode_gemv<CPC, 1>), grid, dim3(256), lds, a.stream, a.ws + p.off_x8,
+                       a.w_packed, part, a.S, a.K, N);
+  else
+    hipLaunchKernelGGL((decode_gemv<CPC, 2>), grid, dim3(256), lds, a.stream, a.ws + p.off_x8,
+                       a.w_packed, part, a.S, a.K, N);
   return hipGetLastError();
 }
 
@@ -326,8 +351,8 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   DecodePlan p{};
   const int N = (19 * nkv + 1) * 128;
   const int nchk = K / 128;
-  const int row_ctas = N / kRowsPerCta;
-  static const int kCands[] = {8, 6, 4, 3, 2, 1};
+  const int row_ctas = N / kHeadDim;
+  static const int kCands[] = {4, 3, 2, 1};
   int pick = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
@@ -371,8 +396,6 @@ hipError_t launch_decode(const Args& a, const DecodePlan& p) {
     case 2: e = launch_gemv_cpc<2>(a, p); break;
     case 3: e = launch_gemv_cpc<3>(a, p); break;
     case 4: e = launch_gemv_cpc<4>(a, p); break;
-    case 6: e = launch_gemv_cpc<6>(a, p); break;
-    case 8: e = launch_gemv_cpc<8>(a, p); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

@@ -5,10 +5,15 @@
 //                       out, Gemma RMSNorm, then OCP-MX quantization (E8M0
 //                       scale per 32-wide k block, E4M3 elements) into the
 //                       GEMM's packed activation layout in the workspace.
-//   2. prefill_gemm     C^T = W . X^T on block-scaled FP8 MFMA
-//                       (v_mfma_scale_f32_32x32x64_f8f6f4). One CTA owns one
-//                       128-wide head x 128 tokens; each wave 32 tokens x the
-//                       whole head, so after the k loop a lane holds one
+//   2. prefill_gemm     C^T = W . X^T on MFMA. One CTA owns one 128-wide head
+//                       x 128 tokens; each wave 32 tokens x the whole head.
+//                       q and index_q heads run block-scaled FP8 MFMAs
+//                       (v_mfma_scale_f32_32x32x64_f8f6f4); the k, v and
+//                       index_k heads, whose per-token scales and codes must
+//                       follow the exact projection closely, run bf16 MFMAs on
+//                       the MXFP8 values widened exactly to bf16 (FP8-input
+//                       MFMAs sum their products at reduced internal
+//                       precision). Either way, after the k loop a lane holds one
 //                       token's 64 dims of the head and its lane ^ 32 partner
 //                       the other 64: the per-head Gemma norm is an in-register
 //                       sum plus one swap, and the RoPE pair (i, i + 32) sits
@@ -33,15 +38,19 @@ constexpr int kTokTile = 128;   // tokens per GEMM CTA (4 waves x 32)
 constexpr int kKStep = 64;      // k per MFMA
 constexpr int kTileBytes = 2048;  // one 32 x 64 FP8 operand tile
 
+// Operand order of the 32x32x64 FP8 MFMA (measured on gfx950): lane l holds
+// row / column l % 32; with h = l / 32 its bytes 0..15 are k = 16h + [0, 16)
+// (MX block 0) and bytes 16..31 are k = 32 + 16h + [0, 16) (block 1); the E8M0
+// scale operand of lane l is that row's scale for block l / 32.
 // Packed activation: token tile tt (32 tokens), k step ks -> 2 KB block at
-// (tt * nks + ks) * 2048; lane l = token (l % 32) + 32 * (k-half), its 32 bytes
-// k = 64 ks + 32 (l / 32) + [0, 32) split as [16 l, 16 l + 16) and
-// [1024 + 16 l, ...). Scales: byte (tt * nks + ks) * 64 + l.
+// (tt * nks + ks) * 2048; lane l's bytes 0..15 at 16 l, bytes 16..31 at
+// 1024 + 16 l (so each dwordx4 wave load is 1 KB contiguous).
+// Scales: byte (tt * nks + ks) * 64 + l.
 __device__ __forceinline__ size_t xq_offset(int m, int k, int nks) {
   const int tt = m >> 5, tl = m & 31;
-  const int ks = k >> 6, kg = (k >> 5) & 1, kb = k & 31;
-  const int l = tl + 32 * kg;
-  return (static_cast<size_t>(tt) * nks + ks) * kTileBytes + (kb >> 4) * 1024 + l * 16 + (kb & 15);
+  const int ks = k >> 6, kk = k & 63;
+  const int region = kk >> 5, h = (kk >> 4) & 1;
+  return (static_cast<size_t>(tt) * nks + ks) * kTileBytes + region * 1024 + (tl + 32 * h) * 16 + (kk & 15);
 }
 
 __device__ __forceinline__ size_t xs_offset(int m, int blk, int nks) {
@@ -142,31 +151,36 @@ __global__ __launch_bounds__(kPreThreads) void prefill_prepass(
   }
 }
 
-// Packed weight: head h, k step ks, 32-row tile m -> 2 KB block at
-// ((h * nks + ks) * 4 + m) * 2048 with the same lane layout as the
-// activation (row 32m + l % 32, k = 64 ks + 32 (l / 32) + [0, 32)).
-// Scales: dword (h * nks + ks) * 64 + l holds tiles m = 0..3 in bytes 0..3.
-__global__ __launch_bounds__(256) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
-                                                   const uint8_t* __restrict__ xs) {
-  __shared__ __align__(16) uint8_t sA[4 * kTileBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x;
-  const int tt = blockIdx.y * (kTokTile / 32) + wave;  // this wave's 32-token tile
-  const int K = a.K;
-  const int nks = K / kKStep;
+// Packed weight, FP8 part (every head): head h, k step ks, 32-row tile m ->
+// 2 KB block at ((h * nks + ks) * 4 + m) * 2048 in the activation's lane order
+// (row 32m + l % 32). Scales: dword (h * nks + ks) * 64 + l holds tiles
+// m = 0..3 in bytes 0..3, each the row's E8M0 for block 2 ks + l / 32.
+// bf16 part (k, v and index_k heads, index p = 0 .. 2 nkv), after the N x K FP8
+// bytes: 1 KB block (((p * nks + ks) * 4 + m) * 4 + j) * 1024 for bf16 MFMA step
+// j of the k step; lane l's 8 values (row 32m + l % 32) sit at 16 l and are
+// k = 64 ks + 32 (j / 2) + 16 (l / 32) + 8 (j % 2) + [0, 8), times the block
+// scale: exactly the FP8 bytes 8 (j % 2) .. + 8 of region j / 2 of the lane.
+
+__device__ __forceinline__ bool precise_head(int h, int nkv) {
+  return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv;
+}
+
+__device__ __forceinline__ int precise_index(int h, int nkv) {
+  return h == 19 * nkv ? 2 * nkv : h - 16 * nkv;
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return __uint_as_float(c ? c << 23 : 0x00400000u);
+}
+
+// q / index_q heads: block-scaled FP8 MFMA.
+__device__ __forceinline__ void mainloop_fp8(const Args& a, int h, const uint8_t* xbase,
+                                             const uint8_t* xsb, uint8_t* sA, f32x16 (&acc)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nks = a.K / kKStep;
   const uint8_t* wbase = a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes;
   const uint32_t* sbase = reinterpret_cast<const uint32_t*>(a.s_packed) + static_cast<size_t>(h) * nks * 64;
-  const uint8_t* xbase = xq + static_cast<size_t>(tt) * nks * kTileBytes;
-  const uint8_t* xsb = xs + static_cast<size_t>(tt) * nks * 64;
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-
   for (int ks = 0; ks < nks; ++ks) {
-    // W tile (128 rows x 64 k, 8 KB) -> LDS, 32 bytes per thread
     const i32x4* wsrc = reinterpret_cast<const i32x4*>(wbase + static_cast<size_t>(ks) * 4 * kTileBytes);
     const i32x4 w0 = wsrc[tid];
     const i32x4 w1 = wsrc[tid + 256];
@@ -193,6 +207,66 @@ __global__ __launch_bounds__(256) void prefill_gemm(Args a, const uint8_t* __res
       }
     }
   }
+}
+
+// k / v / index_k heads: bf16 MFMA on exactly widened MXFP8 values.
+__device__ __forceinline__ void mainloop_bf16(const Args& a, int h, const uint8_t* xbase,
+                                              const uint8_t* xsb, uint8_t* sA, f32x16 (&acc)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nks = a.K / kKStep;
+  const int p = precise_index(h, a.nkv);
+  const uint8_t* wbase = a.w_packed + static_cast<size_t>(a.N()) * a.K +
+                         static_cast<size_t>(p) * nks * 16384;
+  for (int ks = 0; ks < nks; ++ks) {
+    const i32x4* wsrc = reinterpret_cast<const i32x4*>(wbase + static_cast<size_t>(ks) * 16384);
+    const i32x4 w0 = wsrc[tid], w1 = wsrc[tid + 256], w2 = wsrc[tid + 512], w3 = wsrc[tid + 768];
+    const i32x4* xsrc = reinterpret_cast<const i32x4*>(xbase + static_cast<size_t>(ks) * kTileBytes);
+    const i32x4 b0 = xsrc[lane];
+    const i32x4 b1 = xsrc[lane + 64];
+    const float x0 = e8m0_to_f32(xsb[static_cast<size_t>(ks) * 64 + (lane & 31)]);
+    const float x1 = e8m0_to_f32(xsb[static_cast<size_t>(ks) * 64 + (lane & 31) + 32]);
+    __syncthreads();
+    reinterpret_cast<i32x4*>(sA)[tid] = w0;
+    reinterpret_cast<i32x4*>(sA)[tid + 256] = w1;
+    reinterpret_cast<i32x4*>(sA)[tid + 512] = w2;
+    reinterpret_cast<i32x4*>(sA)[tid + 768] = w3;
+    __syncthreads();
+    bf16x8 B[4];
+    B[0] = fp8x8_to_bf16(b0[0], b0[1], x0);
+    B[1] = fp8x8_to_bf16(b0[2], b0[3], x0);
+    B[2] = fp8x8_to_bf16(b1[0], b1[1], x1);
+    B[3] = fp8x8_to_bf16(b1[2], b1[3], x1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(sA + ((m * 4 + j) * 1024) + lane * 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[j], acc[m], 0, 0, 0);
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
+                                                   const uint8_t* __restrict__ xs) {
+  __shared__ __align__(16) uint8_t sA[16384];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x;
+  const int tt = blockIdx.y * (kTokTile / 32) + wave;  // this wave's 32-token tile
+  const int nks = a.K / kKStep;
+  const uint8_t* xbase = xq + static_cast<size_t>(tt) * nks * kTileBytes;
+  const uint8_t* xsb = xs + static_cast<size_t>(tt) * nks * 64;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+  if (precise_head(h, a.nkv))
+    mainloop_bf16(a, h, xbase, xsb, sA, acc);
+  else
+    mainloop_fp8(a, h, xbase, xsb, sA, acc);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) pin_registers(acc[m]);
 
   // ---------------- epilogue: lane holds token tok, dims 32m + 8(r/4) + 4(l/32) + r%4
   {
@@ -327,13 +401,49 @@ __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __res
   const int m = static_cast<int>(blk & 3);
   const size_t hk = blk >> 2;
   const int h = static_cast<int>(hk / nks), ks = static_cast<int>(hk % nks);
-  const int half = p >> 6, l = p & 63;
+  const int region = p >> 6, l = p & 63;
   const int row = h * 128 + m * 32 + (l & 31);
-  const int k = ks * kKStep + (l >> 5) * 32 + half * 16;
-  *reinterpret_cast<i32x4*>(wp + blk * kTileBytes + half * 1024 + l * 16) =
+  const int k = ks * kKStep + region * 32 + (l >> 5) * 16;
+  *reinterpret_cast<i32x4*>(wp + blk * kTileBytes + region * 1024 + l * 16) =
       *reinterpret_cast<const i32x4*>(w + static_cast<size_t>(row) * K + k);
-  if (half == 0)  // one scale byte per (tile, lane)
+  if (region == 0)  // one scale byte per (tile, lane)
     sp[hk * 256 + l * 4 + m] = we[static_cast<size_t>(row) * (K / 32) + ks * 2 + (l >> 5)];
+}
+
+// bf16 copy of the k, v and index_k heads (one thread per 8 values).
+__global__ void pack_prefill_bf16(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
+                                  uint8_t* __restrict__ wb, int nkv, int K) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nks = K / kKStep;
+  const size_t pieces = static_cast<size_t>(2 * nkv + 1) * nks * 4 * 4 * 64;
+  if (idx >= pieces) return;
+  const int l = static_cast<int>(idx & 63);
+  const int j = static_cast<int>((idx >> 6) & 3);
+  const int m = static_cast<int>((idx >> 8) & 3);
+  const size_t pk = idx >> 10;
+  const int p = static_cast<int>(pk / nks), ks = static_cast<int>(pk % nks);
+  const int head = p < 2 * nkv ? 16 * nkv + p : 19 * nkv;
+  const int row = head * 128 + m * 32 + (l & 31);
+  const int k = ks * kKStep + 32 * (j >> 1) + 16 * (l >> 5) + 8 * (j & 1);
+  const uint8_t* src = w + static_cast<size_t>(row) * K + k;
+  const int e = we[static_cast<size_t>(row) * (K / 32) + (k >> 5)];
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t two = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t c = src[2 * i + q];
+      const uint32_t sgn = c & 0x80u, ex = (c >> 3) & 0xfu, mt = c & 7u;
+      // E4M3 value as float32, then times 2^(e - 127); exact in bf16
+      float v = ex ? __uint_as_float(((ex + 120u) << 23) | (mt << 20)) : static_cast<float>(mt) * 0x1p-9f;
+      v = __builtin_ldexpf(v, e - 127);
+      uint32_t bits = (__float_as_uint(v) >> 16) | (sgn << 8);
+      two |= bits << (16 * q);
+    }
+    out[i] = two;
+  }
+  *reinterpret_cast<uint4*>(wb + idx * 16) = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 template <int NV>
@@ -360,7 +470,10 @@ PrefillPlan prefill_plan(int M, int K, int nkv) {
   return p;
 }
 
-size_t prefill_packed_weight_bytes(int N, int K) { return static_cast<size_t>(N) * K; }
+size_t prefill_packed_weight_bytes(int N, int K) {
+  const int nkv = (N / 128 - 1) / 19;
+  return static_cast<size_t>(N) * K + static_cast<size_t>(2 * nkv + 1) * 128 * K * 2;
+}
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
@@ -391,6 +504,12 @@ hipError_t launch_pack_prefill(const uint8_t* w, const uint8_t* we, uint8_t* wp,
   const size_t pieces = static_cast<size_t>(N) * K / 16;
   const unsigned blocks = static_cast<unsigned>((pieces + 255) / 256);
   hipLaunchKernelGGL(pack_prefill, dim3(blocks), dim3(256), 0, s, w, we, wp, sp, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkv = (N / 128 - 1) / 19;
+  const size_t pieces16 = static_cast<size_t>(2 * nkv + 1) * (K / kKStep) * 1024;
+  hipLaunchKernelGGL(pack_prefill_bf16, dim3(static_cast<unsigned>((pieces16 + 255) / 256)), dim3(256),
+                     0, s, w, we, wp + static_cast<size_t>(N) * K, nkv, K);
   return hipGetLastError();
 }
 
