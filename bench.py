@@ -200,6 +200,9 @@ def main():
     # eager pass with HIP events around every launch of the dominant kernel
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a, b in evs:  # torch creates an event at its first record
+        a.record()
+        b.record()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -168,6 +168,13 @@ int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* re
  * The events stay owned by the caller. */
 int pa_set_kernel_events(void* start, void* stop);
 
+/* Instrumentation: from now on, calls on this host thread have thread 0 of
+ * every CTA of the dominant kernel store the 100 MHz s_memrealtime counter at
+ * its phase boundaries into `buffer` (device memory, 8 uint64 slots per CTA,
+ * CTA-major; slot 0 = start, 1 = end for the decode GEMV; the prefill GEMM adds
+ * its own phases). Stamps beyond `bytes` are dropped. NULL turns it off. */
+int pa_set_timeline(void* buffer, size_t bytes);
+
 /* Static text for a pa_status value. */
 const char* pa_strerror(int status);
 

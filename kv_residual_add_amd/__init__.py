@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     pa_pack_weight_decode,
     pa_pack_weight_prefill,
     pa_set_kernel_events,
+    pa_set_timeline,
     pa_packed_scale_bytes,
     pa_packed_weight_bytes,
     pa_workspace_bytes,

@@ -33,6 +33,7 @@ EXPORTS = (
     "pre_attn_decode",
     "pre_attn_prefill",
     "pa_set_kernel_events",
+    "pa_set_timeline",
     "pa_strerror",
     "pa_last_error_detail",
 )
@@ -90,6 +91,8 @@ def load() -> ctypes.CDLL:
         lib.pre_attn_decode.restype = ctypes.c_int
         lib.pre_attn_prefill.argtypes = [dims_p] + [P] * 21 + [sz, P]
         lib.pre_attn_prefill.restype = ctypes.c_int
+        lib.pa_set_timeline.argtypes = [P, sz]
+        lib.pa_set_timeline.restype = ctypes.c_int
         lib.pa_set_kernel_events.argtypes = [P, P]
         lib.pa_set_kernel_events.restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]
@@ -136,7 +139,20 @@ def pa_set_kernel_events(start, stop) -> None:
     later calls on this thread (see include/pre_attn.h)."""
     ps = None if start is None else start.cuda_event
     pe = None if stop is None else stop.cuda_event
+    if (start is not None and not ps) or (stop is not None and not pe):
+        raise ValueError("record each torch.cuda.Event once before passing it (torch creates "
+                         "the underlying event lazily)")
     _check(load().pa_set_kernel_events(ps, pe), "pa_set_kernel_events")
+
+
+def pa_set_timeline(buffer) -> None:
+    """Per-CTA phase stamps of later decode calls into a uint64 CUDA tensor (None: off)."""
+    if buffer is None:
+        _check(load().pa_set_timeline(None, 0), "pa_set_timeline")
+        return
+    if buffer.dtype != torch.int64 or not buffer.is_cuda or not buffer.is_contiguous():
+        raise ValueError("timeline buffer must be a contiguous int64 CUDA tensor")
+    _check(load().pa_set_timeline(buffer.data_ptr(), buffer.numel() * 8), "pa_set_timeline")
 
 
 def pa_workspace_bytes(dims: pa_dims, mode: int) -> int:

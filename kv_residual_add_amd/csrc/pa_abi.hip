@@ -15,6 +15,8 @@ namespace {
 
 thread_local char g_detail[256] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+thread_local uint64_t* g_timeline = nullptr;
+thread_local uint32_t g_timeline_slots = 0;
 
 int hip_fail(hipError_t e, const char* where) {
   std::snprintf(g_detail, sizeof(g_detail), "%s: %s", where, hipGetErrorString(e));
@@ -129,6 +131,8 @@ pa::Args make_args(const pa_dims* d, const Ptrs& p, void* stream) {
   a.stream = static_cast<hipStream_t>(stream);
   a.ev_start = g_ev_start;
   a.ev_stop = g_ev_stop;
+  a.timeline = g_timeline;
+  a.timeline_slots = g_timeline_slots;
   return a;
 }
 
@@ -264,6 +268,14 @@ const char* pa_strerror(int status) {
 }
 
 const char* pa_last_error_detail(void) { return g_detail; }
+
+int pa_set_timeline(void* buffer, size_t bytes) {
+  if (buffer && !aligned(buffer, 8)) return PA_ERR_ALIGN;
+  g_timeline = static_cast<uint64_t*>(buffer);
+  const size_t slots = buffer ? bytes / 8 : 0;
+  g_timeline_slots = static_cast<uint32_t>(slots > 0xffffffffu ? 0xffffffffu : slots);
+  return PA_OK;
+}
 
 int pa_set_kernel_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr)) return PA_ERR_NULL;

@@ -1,24 +1,27 @@
 // Decode prologue on gfx950: per-token FP8 activations against a per-row
 // scaled FP8 weight, for up to 64 tokens.
 //
-// Three kernels on the caller's stream:
-//   1. decode_norm      one CTA per token: residual add (f32) + bf16 residual
-//                       out, Gemma RMSNorm, per-token FP8 quantization into a
-//                       workspace row (the K1 mono_pre page,
-//                       vllm.models.minimax_m3.amd.mono.kernels.pre_attn,
-//                       emit_pre_attn: norm_quant).
-//   2. decode_gemv      the fused projection as an HBM-bound GEMV: each CTA
-//                       owns one 128-row head x a k slice; every wave streams
-//                       its 32 rows' packed weight with dwordx4 loads issued
-//                       before anything waits on them, the FP8 activation slice
-//                       sits in LDS, and 32x32x16 bf16 MFMAs take up to 32
-//                       tokens a tile on exactly widened FP8 codes. k-slice
-//                       partial sums go to the workspace.
-//   3. decode_epilogue  one wave per (token, head): sums the k-slice partials,
-//                       applies the activation and row scales, then the head's
-//                       role (pre_attn page, head tasks; head_norm_rope; the
-//                       epilogue page vllm.models.minimax_m3.nvidia.ops.
-//                       qkv_index_fused_epilogue, per-role branches).
+// Three kernels on the caller's stream (the K1 mono_pre page,
+// vllm.models.minimax_m3.amd.mono.kernels.pre_attn, emit_pre_attn: norm tasks,
+// GEMV tasks, head tasks):
+//   decode_norm      per token, one CTA of up to 1024 threads: residual add (f32)
+//                    + bf16 residual out, Gemma RMSNorm, per-token FP8
+//                    quantization into a workspace row (norm_quant).
+//   decode_gemv      the fused projection as an HBM-bound GEMV: a CTA owns one
+//                    128-row head x a k slice; every wave streams its 32 rows'
+//                    packed weight with dwordx4 loads issued before anything
+//                    waits on them, the FP8 activation slice sits in LDS, and
+//                    32x32x16 bf16 MFMAs take up to 32 tokens a tile on exactly
+//                    widened FP8 codes. k-slice partial sums go to the workspace.
+//   decode_epilogue  per (token, head), one wave: sums the k-slice partials in
+//                    a fixed order, applies the activation and row scales, then
+//                    the head's role (head tasks; head_norm_rope; the epilogue
+//                    page vllm.models.minimax_m3.nvidia.ops.qkv_index_fused_epilogue,
+//                    per-role branches).
+// The kernel boundaries carry the results from one stage to the next: measured
+// on MI355X, a device-scope hand-off between CTAs inside one launch (L2
+// write-back on publish, invalidate on acquire, on every CTA) cost more than the
+// two boundaries under graph replay.
 //
 // Numerics: the input norm, its FP8 decision and the head epilogue run in
 // float64 with contraction off, so a code is decided from the same value the
@@ -34,141 +37,178 @@
 namespace pa {
 namespace {
 
-constexpr int kNormThreads = 256;
 constexpr int kLdsPad = 16;
 constexpr int kMaxLds = 64 * 1024;
 
+// Block reductions over up to 16 waves: each wave's result goes to LDS, then
+// every thread combines the waves' values in the same fixed order (pairwise).
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = static_cast<int>(blockDim.x >> 6);
   if (lane == 0) red[wave] = v;
+  for (int w = nw; w < 16; ++w)
+    if (threadIdx.x == 0) red[w] = 0.0;
   __syncthreads();
-  double t = red[0];
-  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) t += red[w];
+  double t[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) t[w] = red[w] + red[w + 8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) t[w] += t[w + 4];
+  const double r = (t[0] + t[2]) + (t[1] + t[3]);
   __syncthreads();
-  return t;
+  return r;
 }
 
 __device__ __forceinline__ double block_max_f64(double v, double* red) {
   v = wave_max_f64(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = static_cast<int>(blockDim.x >> 6);
   if (lane == 0) red[wave] = v;
+  for (int w = nw; w < 16; ++w)
+    if (threadIdx.x == 0) red[w] = 0.0;
   __syncthreads();
-  double t = red[0];
-  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) t = t > red[w] ? t : red[w];
+  double t[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) t[w] = __builtin_fmax(red[w], red[w + 8]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) t[w] = __builtin_fmax(t[w], t[w + 4]);
+  const double r = __builtin_fmax(__builtin_fmax(t[0], t[2]), __builtin_fmax(t[1], t[3]));
   __syncthreads();
-  return t;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
-// 1. residual add + Gemma RMSNorm + per-token FP8, one token per CTA.
-//    NV = 8-element vectors per thread (hidden <= NV * 8 * 256).
+// norm: residual add + Gemma RMSNorm + per-token FP8 for token `row`; thread
+// t owns the 8-element vectors t, t + blockDim.x, ... (NV of them). The element
+// loops stay rolled: each wave runs this code once, so its size, not its
+// instruction count, sets the time.
 template <int NV>
-__global__ __launch_bounds__(kNormThreads) void decode_norm(
-    const uint16_t* __restrict__ ar, const uint16_t* __restrict__ res,
-    uint16_t* __restrict__ h_out, const uint16_t* __restrict__ g_in,
-    uint8_t* __restrict__ x8, float* __restrict__ sx, int K, float eps) {
+__device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __restrict__ x8,
+                                           float* __restrict__ sx, double* red, int tl) {
 #pragma clang fp contract(off)
-  __shared__ double red[kNormThreads / 64];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int K = a.K;
   const int nvec = K >> 3;
   const size_t base = static_cast<size_t>(row) * K;
-  double xn[NV][8];
-  double ss = 0.0;
+  uint4 av[NV], bv[NV], gv[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kNormThreads;
+  for (int i = 0; i < NV; ++i) {  // every load in flight before any use
+    const int v = tid + i * nthreads;
+    av[i] = bv[i] = gv[i] = make_uint4(0u, 0u, 0u, 0u);
     if (v < nvec) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ar + base + 8 * v);
-      const uint4 b = *reinterpret_cast<const uint4*>(res + base + 8 * v);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-      uint32_t hw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
-        const float hi = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
-        hw[q] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-        xn[i][2 * q] = lo;
-        xn[i][2 * q + 1] = hi;
-        ss += static_cast<double>(lo) * lo;
-        ss += static_cast<double>(hi) * hi;
-      }
-      *reinterpret_cast<uint4*>(h_out + base + 8 * v) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xn[i][e] = 0.0;
+      av[i] = *reinterpret_cast<const uint4*>(a.ar + base + 8 * v);
+      bv[i] = *reinterpret_cast<const uint4*>(a.res + base + 8 * v);
+      gv[i] = *reinterpret_cast<const uint4*>(a.g_in + 8 * v);
     }
   }
-  ss = block_sum_f64(ss, red);
-  const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(eps));
+  stamp(a.timeline, a.timeline_slots, tl, 0);
+  float acc[NV][8];
+  double ssp[4] = {0.0, 0.0, 0.0, 0.0};  // four chains, combined pairwise
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t aw[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+    const uint32_t bw[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
+    uint32_t hw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[i][2 * q] = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
+      acc[i][2 * q + 1] = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
+      hw[q] = f32_to_bf16(acc[i][2 * q]) | (f32_to_bf16(acc[i][2 * q + 1]) << 16);
+      ssp[q] += static_cast<double>(acc[i][2 * q]) * acc[i][2 * q];
+      ssp[q] += static_cast<double>(acc[i][2 * q + 1]) * acc[i][2 * q + 1];
+    }
+    const int v = tid + i * nthreads;
+    if (v < nvec)
+      *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  }
+  stamp(a.timeline, a.timeline_slots, tl, 1);
+  const double ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
+  stamp(a.timeline, a.timeline_slots, tl, 2);
+  const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(a.eps));
+  double xn[NV][8];
   double amax = 0.0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kNormThreads;
-    if (v < nvec) {
-      const uint4 g = *reinterpret_cast<const uint4*>(g_in + 8 * v);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+    double m[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t gb = (e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffffu);
-        const double gp = 1.0 + static_cast<double>(bf16_to_f32(gb));
-        xn[i][e] = (xn[i][e] * rstd) * gp;
-        const double m = __builtin_fabs(xn[i][e]);
-        amax = amax > m ? amax : m;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t gb = (gw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      xn[i][e] = (static_cast<double>(acc[i][e]) * rstd) * (1.0 + static_cast<double>(bf16_to_f32(gb)));
+      m[e] = __builtin_fabs(xn[i][e]);
     }
+    const double mm = __builtin_fmax(__builtin_fmax(__builtin_fmax(m[0], m[1]), __builtin_fmax(m[2], m[3])),
+                                     __builtin_fmax(__builtin_fmax(m[4], m[5]), __builtin_fmax(m[6], m[7])));
+    amax = __builtin_fmax(amax, mm);
   }
+  stamp(a.timeline, a.timeline_slots, tl, 3);
   amax = block_max_f64(amax, red);
+  stamp(a.timeline, a.timeline_slots, tl, 4);
   const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
   const double sd = static_cast<double>(s);
+  const double rcp = 1.0 / sd;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kNormThreads;
-    if (v < nvec) {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w0 |= e4m3_from_f64(xn[i][e] / sd) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w1 |= e4m3_from_f64(xn[i][4 + e] / sd) << (8 * e);
-      *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w0, w1);
-    }
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll 1
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_div(xn[i][e], sd, rcp) << (8 * (e & 3));
+    const int v = tid + i * nthreads;
+    if (v < nvec) *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w[0], w[1]);
   }
   if (tid == 0) sx[row] = s;
+  stamp(a.timeline, a.timeline_slots, tl, 5);
 }
 
 // ---------------------------------------------------------------------------
-// 2. GEMV partials. Packed weight: head h, 128-wide k chunk c, 32-row tile m ->
-//    a 4 KB block at ((h * K/128 + c) * 4 + m) * 4096. Its dwordx4 piece q of
-//    lane l sits at q * 1024 + 16 l (each wave load is 1 KB contiguous) and holds
-//    row 32m + l % 32 for MFMA steps j = 2q and 2q + 1, each 8 codes at
-//    k = 128c + 16j + 8 (l / 32) + [0, 8). The activation B operand takes the
-//    same k from LDS, so the dot product needs no shuffles. Tokens past S reuse
-//    token S-1 and are never stored. NT = 32-token tiles (1 or 2).
+// GEMV. Packed weight: head h, 128-wide k chunk c, 32-row tile m -> a 4 KB
+// block at ((h * K/128 + c) * 4 + m) * 4096. Its dwordx4 piece q of lane l sits
+// at q * 1024 + 16 l (each wave load is 1 KB contiguous) and holds row
+// 32m + l % 32 for MFMA steps j = 2q and 2q + 1, each 8 codes at
+// k = 128c + 16j + 8 (l / 32) + [0, 8). The activation B operand takes the same
+// k from LDS, so the dot product needs no shuffles. Tokens past S reuse token
+// S-1 and are never stored. NT = 32-token tiles (1 or 2).
 template <int CPC, int NT>
-__global__ __launch_bounds__(256) void decode_gemv(
-    const uint8_t* __restrict__ x8, const uint8_t* __restrict__ wp, float* __restrict__ part,
-    int S, int K, int N) {
+__global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, ks = blockIdx.y;
+  const int S = a.S, K = a.K, N = a.N();
   const int nchk = K >> 7;
-  const int c0 = ks * CPC;
   constexpr int ldw = CPC * 128 + kLdsPad;
+  const uint8_t* x8 = a.ws + off_x8;
+  float* part = reinterpret_cast<float*>(a.ws + off_part);
+  const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
+  stamp(a.timeline, a.timeline_slots, tlb, 0);
 
-  // the weight stream first: nothing waits on it until the MFMAs
+  // the activation slice first (small, L2), then the weight stream: the LDS
+  // stores below wait only for the former
+  const int per_row = CPC * 8;  // 16-byte pieces per token row
+  constexpr int kMaxPieces = 64 * CPC * 8 / 256;
+  i32x4 xv[kMaxPieces];
+#pragma unroll
+  for (int r = 0; r < kMaxPieces; ++r) {
+    const int i = tid + r * 256;
+    if (i < S * per_row) {
+      const int s = i / per_row, j = i - s * per_row;
+      xv[r] = *reinterpret_cast<const i32x4*>(x8 + static_cast<size_t>(s) * K + ks * CPC * 128 + j * 16);
+    }
+  }
   i32x4 wv[CPC][4];
-  const uint8_t* wb = wp + ((static_cast<size_t>(h) * nchk + c0) * 4 + wave) * 4096 + lane * 16;
+  const uint8_t* wb = a.w_packed + ((static_cast<size_t>(h) * nchk + ks * CPC) * 4 + wave) * 4096 + lane * 16;
 #pragma unroll
   for (int c = 0; c < CPC; ++c)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
-  // the FP8 activation slice of every token into LDS
-  const int per_row = CPC * 8;  // 16-byte pieces per token row
-  for (int i = tid; i < S * per_row; i += 256) {
-    const int s = i / per_row, j = i - s * per_row;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(x8 + static_cast<size_t>(s) * K + c0 * 128 + j * 16);
-    *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = v;
+#pragma unroll
+  for (int r = 0; r < kMaxPieces; ++r) {
+    const int i = tid + r * 256;
+    if (i < S * per_row) {
+      const int s = i / per_row, j = i - s * per_row;
+      *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = xv[r];
+    }
   }
   __syncthreads();
 
@@ -209,36 +249,55 @@ __global__ __launch_bounds__(256) void decode_gemv(
       }
     }
   }
+  stamp(a.timeline, a.timeline_slots, tlb, 1);
 }
 
 // ---------------------------------------------------------------------------
-// 3. head epilogue, one wave per (token, head). Lane l holds dims l and l+64;
-//    the RoPE partner of dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
-__global__ __launch_bounds__(64) void decode_epilogue(Args a, const float* __restrict__ part,
-                                                     const float* __restrict__ sx, int ksplit) {
+// epilogue of head h for token tok, one wave. Lane l holds dims l and l + 64;
+// the RoPE partner of dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
+__global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, size_t off_sx,
+                                                     int ksplit) {
 #pragma clang fp contract(off)
   const int H = a.heads();
+  const int h = blockIdx.x % H, tok = blockIdx.x / H;
+  const float* __restrict__ part = reinterpret_cast<const float*>(a.ws + off_part);
+  const float* __restrict__ sx = reinterpret_cast<const float*>(a.ws + off_sx);
   const int N = a.N();
-  const int h = blockIdx.x % H;
-  const int tok = blockIdx.x / H;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int nkv = a.nkv;
   const int S = a.S;
   const int d0 = lane, d1 = lane + 64;
   const int n0 = h * kHeadDim + d0, n1 = h * kHeadDim + d1;
+  const int tlb = S + H * ksplit + blockIdx.x;  // timeline slot
+  stamp(a.timeline, a.timeline_slots, tlb, 0);
 
+  // the slice partials, eight slices' loads in flight at a time, summed in
+  // slice order
   double y0 = 0.0, y1 = 0.0;
-  for (int ks = 0; ks < ksplit; ++ks) {
-    const float* p = part + (static_cast<size_t>(ks) * S + tok) * N;
-    y0 += static_cast<double>(p[n0]);
-    y1 += static_cast<double>(p[n1]);
+  const size_t stride = static_cast<size_t>(S) * N;
+  const float* p = part + static_cast<size_t>(tok) * N;
+  for (int k8 = 0; k8 < ksplit; k8 += 8) {
+    float v0[8], v1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // clamped indices: every load is unconditional
+      const size_t ks = static_cast<size_t>(min(k8 + u, ksplit - 1));
+      v0[u] = p[ks * stride + n0];
+      v1[u] = p[ks * stride + n1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = k8 + u < ksplit;
+      y0 += in ? static_cast<double>(v0[u]) : 0.0;
+      y1 += in ? static_cast<double>(v1[u]) : 0.0;
+    }
   }
+  stamp(a.timeline, a.timeline_slots, tlb, 1);
   const double sxv = static_cast<double>(sx[tok]);
   y0 = (y0 * sxv) * static_cast<double>(a.w_scale[n0]);
   y1 = (y1 * sxv) * static_cast<double>(a.w_scale[n1]);
 
   const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
-  int64_t slot = a.slot_mapping[tok];
+  const int64_t slot = a.slot_mapping[tok];
   const bool store_cache = slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
@@ -248,9 +307,10 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, const float* __res
     const double amax = wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
+      const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes;
-      vc[d0 * kPage + t] = static_cast<uint8_t>(e4m3_from_f64(y0 / static_cast<double>(s)));
-      vc[d1 * kPage + t] = static_cast<uint8_t>(e4m3_from_f64(y1 / static_cast<double>(s)));
+      vc[d0 * kPage + t] = static_cast<uint8_t>(e4m3_div(y0, sd, rcp));
+      vc[d1 * kPage + t] = static_cast<uint8_t>(e4m3_div(y1, sd, rcp));
       if (lane == 0) a.v_scale[(page * nkv + j) * kPage + t] = s;
     }
     return;
@@ -279,9 +339,10 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, const float* __res
     const double amax = wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
+      const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* kc = a.k_cache + (page * nkv + j) * kPageBytes + t * 16;
-      kc[(d0 >> 4) * 256 + (d0 & 15)] = static_cast<uint8_t>(e4m3_from_f64(o0 / static_cast<double>(s)));
-      kc[(d1 >> 4) * 256 + (d1 & 15)] = static_cast<uint8_t>(e4m3_from_f64(o1 / static_cast<double>(s)));
+      kc[(d0 >> 4) * 256 + (d0 & 15)] = static_cast<uint8_t>(e4m3_div(o0, sd, rcp));
+      kc[(d1 >> 4) * 256 + (d1 & 15)] = static_cast<uint8_t>(e4m3_div(o1, sd, rcp));
       if (lane == 0) a.k_scale[(page * nkv + j) * kPage + t] = s;
     }
   } else if (h < ik0) {
@@ -296,7 +357,16 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, const float* __res
   }
 }
 
-// Weight repack for decode_gemv (one thread per 16-byte piece).
+// ---------------------------------------------------------------------------
+// norm kernel: blockDim.x threads (a multiple of 64, at most 1024)
+template <int NV>
+__global__ __launch_bounds__(1024) void decode_norm(Args a, size_t off_x8, size_t off_sx) {
+  __shared__ double red[16];
+  norm_token<NV>(a, blockIdx.x, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_sx), red,
+                 blockIdx.x);
+}
+
+// Weight repack for the GEMV (one thread per 16-byte piece).
 __global__ void pack_decode(const uint8_t* __restrict__ w, uint8_t* __restrict__ wp, int N, int K) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t pieces = static_cast<size_t>(N) * K / 16;
@@ -322,27 +392,17 @@ __global__ void fill_zero(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-template <int CPC>
-hipError_t launch_gemv_cpc(const Args& a, const DecodePlan& p) {
-  const int N = a.N();
+template <int CPC, int NT>
+hipError_t launch_gemv(const Args& a, const DecodePlan& p) {
   const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
-  dim3 grid(a.heads(), p.ksplit);
-  float* part = reinterpret_cast<float*>(a.ws + p.off_part);
-  if (a.S <= 32)
-    hipLaunchKernelGGL((decode_gemv<CPC, 1>), grid, dim3(256), lds, a.stream, a.ws + p.off_x8,
-                       a.w_packed, part, a.S, a.K, N);
-  else
-    hipLaunchKernelGGL((decode_gemv<CPC, 2>), grid, dim3(256), lds, a.stream, a.ws + p.off_x8,
-                       a.w_packed, part, a.S, a.K, N);
+  hipLaunchKernelGGL((decode_gemv<CPC, NT>), dim3(a.heads(), p.ksplit), dim3(256), lds, a.stream, a,
+                     p.off_x8, p.off_part);
   return hipGetLastError();
 }
 
-template <int NV>
-hipError_t launch_norm_nv(const Args& a, const DecodePlan& p) {
-  hipLaunchKernelGGL(decode_norm<NV>, dim3(a.S), dim3(kNormThreads), 0, a.stream, a.ar, a.res,
-                     a.h_out, a.g_in, a.ws + p.off_x8, reinterpret_cast<float*>(a.ws + p.off_sx),
-                     a.K, a.eps);
-  return hipGetLastError();
+template <int CPC>
+hipError_t launch_gemv_nt(const Args& a, const DecodePlan& p) {
+  return a.S <= 32 ? launch_gemv<CPC, 1>(a, p) : launch_gemv<CPC, 2>(a, p);
 }
 
 }  // namespace
@@ -351,14 +411,14 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   DecodePlan p{};
   const int N = (19 * nkv + 1) * 128;
   const int nchk = K / 128;
-  const int row_ctas = N / kHeadDim;
+  const int heads = N / kHeadDim;
   static const int kCands[] = {4, 3, 2, 1};
   int pick = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
     if (static_cast<size_t>(S) * (c * 128 + kLdsPad) > kMaxLds) continue;
     pick = c;  // smallest fitting candidate so far
-    if (row_ctas * (nchk / c) >= 256) break;
+    if (heads * (nchk / c) >= 256) break;
   }
   p.chunks_per_cta = pick;
   p.ksplit = pick ? nchk / pick : 0;
@@ -370,39 +430,35 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   p.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.ksplit) * S * N, 256);
   p.off_cnt = off;
-  off += 1024;
   p.total = off;
   return p;
 }
 
 hipError_t launch_decode(const Args& a, const DecodePlan& p) {
-  hipError_t e;
-  const int nv = (a.K / 8 + kNormThreads - 1) / kNormThreads;
-  switch (nv) {
-    case 1: e = launch_norm_nv<1>(a, p); break;
-    case 2: e = launch_norm_nv<2>(a, p); break;
-    case 3: e = launch_norm_nv<3>(a, p); break;
-    case 4: e = launch_norm_nv<4>(a, p); break;
-    case 5: e = launch_norm_nv<5>(a, p); break;
-    case 6: e = launch_norm_nv<6>(a, p); break;
-    case 7: e = launch_norm_nv<7>(a, p); break;
-    case 8: e = launch_norm_nv<8>(a, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  // norm: one thread per 8-element vector up to 1024 threads, then loop
+  const int vecs = a.K / 8;
+  const int threads = vecs >= 1024 ? 1024 : (vecs + 63) / 64 * 64;
+  const int nv = (vecs + threads - 1) / threads;
+  if (nv == 1)
+    hipLaunchKernelGGL((decode_norm<1>), dim3(a.S), dim3(threads), 0, a.stream, a, p.off_x8, p.off_sx);
+  else if (nv == 2)
+    hipLaunchKernelGGL((decode_norm<2>), dim3(a.S), dim3(threads), 0, a.stream, a, p.off_x8, p.off_sx);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
   switch (p.chunks_per_cta) {
-    case 1: e = launch_gemv_cpc<1>(a, p); break;
-    case 2: e = launch_gemv_cpc<2>(a, p); break;
-    case 3: e = launch_gemv_cpc<3>(a, p); break;
-    case 4: e = launch_gemv_cpc<4>(a, p); break;
+    case 1: e = launch_gemv_nt<1>(a, p); break;
+    case 2: e = launch_gemv_nt<2>(a, p); break;
+    case 3: e = launch_gemv_nt<3>(a, p); break;
+    case 4: e = launch_gemv_nt<4>(a, p); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a,
-                     reinterpret_cast<const float*>(a.ws + p.off_part),
-                     reinterpret_cast<const float*>(a.ws + p.off_sx), p.ksplit);
+  hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part,
+                     p.off_sx, p.ksplit);
   return hipGetLastError();
 }
 

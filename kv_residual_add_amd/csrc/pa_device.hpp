@@ -76,26 +76,84 @@ __device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
   return sign | code;
 }
 
-// Wave64 reductions (xor butterflies; every lane ends with the result).
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// The rare path of e4m3_div, kept out of line so the division sequence is not
+// copied into every caller.
+__device__ __attribute__((noinline)) uint32_t e4m3_div_exact(double x, double s);
+
+// E4M3 code of RN64(x / s) (s > 0) without a float64 division in the common
+// case: q = x * rcp with rcp = RN64(1 / s) is within 2 ulp of the correctly
+// rounded quotient, so both round to the same code unless q lies within a few
+// ulp of a rounding midpoint of the code grid; there (tested with a margin of
+// 2^-40 grid steps, far above the 2^-48 bound) the true quotient is used.
+__device__ __forceinline__ uint32_t e4m3_div(double x, double s, double rcp) {
+  const double q = x * rcp;
+  double a = __builtin_fabs(q);
+  a = a < kFp8Max ? a : kFp8Max;
+  double t;  // position on the code grid (exact)
+  if (a < 0x1p-6) {
+    t = a * 512.0;
+  } else {
+    const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(a)) >> 52) & 0x7ff) - 1023;
+    t = a * __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
+  }
+  const double f = t - __builtin_floor(t);
+  if (__builtin_fabs(f - 0.5) < 0x1p-40) return e4m3_div_exact(x, s);
+  return e4m3_from_f64(q);
 }
 
+__device__ __attribute__((noinline)) inline uint32_t e4m3_div_exact(double x, double s) {
+  return e4m3_from_f64(x / s);
+}
+
+// Wave64 reductions of float64 with DPP row operations (no LDS traffic):
+// xor-1 and xor-2 inside quads, the half-row and row mirrors, then the row
+// broadcasts of lanes 15 and 31 carry the partial results up to lane 63, which
+// is read back for every lane. A DPP move works on 32 bits, so each step moves
+// both halves; rows outside `row_mask` receive the identity.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_f64(double v, double identity) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(identity), __double2loint(v), kCtrl, kRowMask, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(identity), __double2hiint(v), kCtrl, kRowMask, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double lane63_f64(double v) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1, 0xf>(v, 0.0);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E, 0xf>(v, 0.0);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141, 0xf>(v, 0.0);  // row_half_mirror
+  v += dpp_f64<0x140, 0xf>(v, 0.0);  // row_mirror
+  v += dpp_f64<0x142, 0xa>(v, 0.0);  // row_bcast:15 into rows 1, 3
+  v += dpp_f64<0x143, 0xc>(v, 0.0);  // row_bcast:31 into rows 2, 3
+  return lane63_f64(v);
+}
+
+// max of non-negative values (identity 0)
 __device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const double o = __shfl_xor(v, m, 64);
-    v = v > o ? v : o;
-  }
-  return v;
+  v = __builtin_fmax(v, dpp_f64<0xB1, 0xf>(v, 0.0));
+  v = __builtin_fmax(v, dpp_f64<0x4E, 0xf>(v, 0.0));
+  v = __builtin_fmax(v, dpp_f64<0x141, 0xf>(v, 0.0));
+  v = __builtin_fmax(v, dpp_f64<0x140, 0xf>(v, 0.0));
+  v = __builtin_fmax(v, dpp_f64<0x142, 0xa>(v, 0.0));
+  v = __builtin_fmax(v, dpp_f64<0x143, 0xc>(v, 0.0));
+  return lane63_f64(v);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   return v;
+}
+
+// Timeline stamp k of CTA b (8 per CTA): the 100 MHz s_memrealtime counter.
+__device__ __forceinline__ void stamp(uint64_t* tl, uint32_t slots, int b, int k) {
+  if (tl != nullptr && threadIdx.x == 0 && static_cast<uint32_t>(b * 8 + k) < slots)
+    tl[b * 8 + k] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Page-16 addressing of a slot at the default (contiguous) page stride.

@@ -28,6 +28,8 @@ struct Args {
   uint8_t* ws;
   hipStream_t stream;
   hipEvent_t ev_start, ev_stop;  // optional, around the dominant kernel
+  uint64_t* timeline;            // optional per-CTA phase stamps (s_memrealtime)
+  uint32_t timeline_slots;       // stamps available in `timeline`
   __host__ __device__ int N() const { return (19 * nkv + 1) * 128; }
   __host__ __device__ int heads() const { return 19 * nkv + 1; }
 };

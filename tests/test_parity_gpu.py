@@ -154,3 +154,4 @@ def test_positions_out_of_range_are_clamped():
     ref = oracle.decode(clamped)
     _, got = _gpu(inp)
     parity.compare(inp, ref, got)
+
