@@ -41,7 +41,24 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 10 times (the known-size "
+                         "reference for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 10}))
 
 
 def algorithmic(wl):
@@ -116,6 +133,9 @@ def cpu_baseline(wl, inp, budget_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the prologue shards by heads with no exchange, so per-GPU throughput is the "
