@@ -76,33 +76,36 @@ __device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
   return sign | code;
 }
 
-// The rare path of e4m3_div, kept out of line so the division sequence is not
-// copied into every caller.
-__device__ __attribute__((noinline)) uint32_t e4m3_div_exact(double x, double s);
-
-// E4M3 code of RN64(x / s) (s > 0) without a float64 division in the common
-// case: q = x * rcp with rcp = RN64(1 / s) is within 2 ulp of the correctly
-// rounded quotient, so both round to the same code unless q lies within a few
-// ulp of a rounding midpoint of the code grid; there (tested with a margin of
-// 2^-40 grid steps, far above the 2^-48 bound) the true quotient is used.
+// E4M3 code of RN64(x / s) (s > 0) without a float64 division. q = x * rcp,
+// rcp = RN64(1 / s), is within 2 ulp of the correctly rounded quotient, so both
+// round to the same code unless q lies within a few ulp of a midpoint m of the
+// code grid. There (tested with a margin of 2^-40 grid steps, far above the
+// 2^-50 bound) the side of m is decided exactly: fma(-m, s, |x|) rounds the
+// exact |x| - m s once, which keeps its sign, so it is positive, negative or
+// zero exactly when |x| / s is above, below or at m. The grid values on either
+// side and m itself are exact doubles; e4m3_from_f64 then rounds the chosen one
+// (a tie at m to the even code).
 __device__ __forceinline__ uint32_t e4m3_div(double x, double s, double rcp) {
-  const double q = x * rcp;
+  double q = x * rcp;
   double a = __builtin_fabs(q);
   a = a < kFp8Max ? a : kFp8Max;
-  double t;  // position on the code grid (exact)
+  double up;  // grid steps per unit value (a power of two)
   if (a < 0x1p-6) {
-    t = a * 512.0;
+    up = 512.0;
   } else {
     const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(a)) >> 52) & 0x7ff) - 1023;
-    t = a * __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
+    up = __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
   }
-  const double f = t - __builtin_floor(t);
-  if (__builtin_fabs(f - 0.5) < 0x1p-40) return e4m3_div_exact(x, s);
+  const double t = a * up;  // position on the code grid (exact)
+  const double fl = __builtin_floor(t);
+  if (__builtin_fabs((t - fl) - 0.5) < 0x1p-40) {
+    const double step = 1.0 / up;  // exact
+    const double m = (fl + 0.5) * step;
+    const double r = __builtin_fma(-m, s, __builtin_fabs(x));
+    const double pick = r > 0.0 ? (fl + 1.0) * step : (r < 0.0 ? fl * step : m);
+    q = __builtin_copysign(pick, x);
+  }
   return e4m3_from_f64(q);
-}
-
-__device__ __attribute__((noinline)) inline uint32_t e4m3_div_exact(double x, double s) {
-  return e4m3_from_f64(x / s);
 }
 
 // Wave64 reductions of float64 with DPP row operations (no LDS traffic):

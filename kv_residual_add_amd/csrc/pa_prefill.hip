@@ -34,7 +34,7 @@ namespace pa {
 namespace {
 
 constexpr int kPreThreads = 256;
-constexpr int kTokTile = 128;   // tokens per GEMM CTA (4 waves x 32)
+constexpr int kTokAlign = 256;  // token rows of the packed activation (largest CTA tile)
 constexpr int kKStep = 64;      // k per MFMA
 constexpr int kTileBytes = 2048;  // one 32 x 64 FP8 operand tile
 
@@ -173,221 +173,345 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
   return __uint_as_float(c ? c << 23 : 0x00400000u);
 }
 
-// q / index_q heads: block-scaled FP8 MFMA.
-__device__ __forceinline__ void mainloop_fp8(const Args& a, int h, const uint8_t* xbase,
-                                             const uint8_t* xsb, uint8_t* sA, f32x16 (&acc)[4]) {
+// ---------------------------------------------------------------------------
+// Main loop. A wave owns the whole 128-row head x NTW 32-token tiles; the CTA's
+// four waves share the head's weight tile, staged through a two-slot LDS ring,
+// while each wave keeps its own activation tiles in registers. Global loads run
+// two k steps ahead of the MFMAs (three register sets), so the ~0.4-1 us of L2
+// / Infinity Cache latency overlaps two steps of MFMA work.
+//
+// Per 64-wide k step, FP8 heads: A 8 KB (4 row tiles x 2 KB) + one scale dword
+// per lane; B per token tile 2 KB + one scale byte per lane. Precise heads: A is
+// the 16 KB bf16 copy (4 row tiles x 4 MFMA steps x 1 KB) and B is widened to
+// bf16 with its two block scales.
+template <bool PRECISE, int NTW>
+struct Stage {
+  static constexpr int kAPieces = PRECISE ? 4 : 2;  // dwordx4 per thread of A
+  i32x4 a[kAPieces];
+  uint32_t sa;       // FP8: A scale dword (row tiles in bytes 0..3)
+  i32x4 b[NTW][2];   // B bytes 0..15 and 16..31 of the lane
+  uint32_t sb[NTW];  // FP8: the lane's B scale; precise: blocks 0 | 1 << 8
+};
+
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void stage_load(Stage<PRECISE, NTW>& st, const Args& a, int h, int tt0,
+                                           const uint8_t* __restrict__ xq,
+                                           const uint8_t* __restrict__ xs, int ks) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int nks = a.K / kKStep;
-  const uint8_t* wbase = a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes;
-  const uint32_t* sbase = reinterpret_cast<const uint32_t*>(a.s_packed) + static_cast<size_t>(h) * nks * 64;
-  for (int ks = 0; ks < nks; ++ks) {
-    const i32x4* wsrc = reinterpret_cast<const i32x4*>(wbase + static_cast<size_t>(ks) * 4 * kTileBytes);
-    const i32x4 w0 = wsrc[tid];
-    const i32x4 w1 = wsrc[tid + 256];
-    const uint32_t sa = sbase[static_cast<size_t>(ks) * 64 + lane];
-    const i32x4* xsrc = reinterpret_cast<const i32x4*>(xbase + static_cast<size_t>(ks) * kTileBytes);
-    const i32x4 b0 = xsrc[lane];
-    const i32x4 b1 = xsrc[lane + 64];
-    const uint32_t sb = xsb[static_cast<size_t>(ks) * 64 + lane];
-    __syncthreads();
-    reinterpret_cast<i32x4*>(sA)[tid] = w0;
-    reinterpret_cast<i32x4*>(sA)[tid + 256] = w1;
-    __syncthreads();
-    const i32x8 B = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  if (PRECISE) {
+    const int p = precise_index(h, a.nkv);
+    const i32x4* src = reinterpret_cast<const i32x4*>(
+        a.w_packed + static_cast<size_t>(a.N()) * a.K + (static_cast<size_t>(p) * nks + ks) * 16384);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const i32x4 a0 = reinterpret_cast<const i32x4*>(sA + m * kTileBytes)[lane];
-      const i32x4 a1 = reinterpret_cast<const i32x4*>(sA + m * kTileBytes + 1024)[lane];
-      const i32x8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      switch (m) {  // the scale byte of tile m (op_sel is an immediate)
-        case 0: acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[0], 0, 0, 0, sa, 0, sb); break;
-        case 1: acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[1], 0, 0, 1, sa, 0, sb); break;
-        case 2: acc[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[2], 0, 0, 2, sa, 0, sb); break;
-        default: acc[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[3], 0, 0, 3, sa, 0, sb); break;
-      }
-    }
+    for (int i = 0; i < 4; ++i) st.a[i] = src[tid + 256 * i];
+    st.sa = 0;
+  } else {
+    const i32x4* src = reinterpret_cast<const i32x4*>(
+        a.w_packed + (static_cast<size_t>(h) * nks + ks) * 4 * kTileBytes);
+    st.a[0] = src[tid];
+    st.a[1] = src[tid + 256];
+    st.sa = reinterpret_cast<const uint32_t*>(a.s_packed)[(static_cast<size_t>(h) * nks + ks) * 64 + lane];
+  }
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) {
+    const size_t blk = static_cast<size_t>(tt0 + n) * nks + ks;
+    const i32x4* src = reinterpret_cast<const i32x4*>(xq + blk * kTileBytes);
+    st.b[n][0] = src[lane];
+    st.b[n][1] = src[lane + 64];
+    const uint8_t* sx = xs + blk * 64;
+    st.sb[n] = PRECISE ? (static_cast<uint32_t>(sx[lane & 31]) | (static_cast<uint32_t>(sx[(lane & 31) + 32]) << 8))
+                       : static_cast<uint32_t>(sx[lane]);
   }
 }
 
-// k / v / index_k heads: bf16 MFMA on exactly widened MXFP8 values.
-__device__ __forceinline__ void mainloop_bf16(const Args& a, int h, const uint8_t* xbase,
-                                              const uint8_t* xsb, uint8_t* sA, f32x16 (&acc)[4]) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int nks = a.K / kKStep;
-  const int p = precise_index(h, a.nkv);
-  const uint8_t* wbase = a.w_packed + static_cast<size_t>(a.N()) * a.K +
-                         static_cast<size_t>(p) * nks * 16384;
-  for (int ks = 0; ks < nks; ++ks) {
-    const i32x4* wsrc = reinterpret_cast<const i32x4*>(wbase + static_cast<size_t>(ks) * 16384);
-    const i32x4 w0 = wsrc[tid], w1 = wsrc[tid + 256], w2 = wsrc[tid + 512], w3 = wsrc[tid + 768];
-    const i32x4* xsrc = reinterpret_cast<const i32x4*>(xbase + static_cast<size_t>(ks) * kTileBytes);
-    const i32x4 b0 = xsrc[lane];
-    const i32x4 b1 = xsrc[lane + 64];
-    const float x0 = e8m0_to_f32(xsb[static_cast<size_t>(ks) * 64 + (lane & 31)]);
-    const float x1 = e8m0_to_f32(xsb[static_cast<size_t>(ks) * 64 + (lane & 31) + 32]);
-    __syncthreads();
-    reinterpret_cast<i32x4*>(sA)[tid] = w0;
-    reinterpret_cast<i32x4*>(sA)[tid + 256] = w1;
-    reinterpret_cast<i32x4*>(sA)[tid + 512] = w2;
-    reinterpret_cast<i32x4*>(sA)[tid + 768] = w3;
-    __syncthreads();
-    bf16x8 B[4];
-    B[0] = fp8x8_to_bf16(b0[0], b0[1], x0);
-    B[1] = fp8x8_to_bf16(b0[2], b0[3], x0);
-    B[2] = fp8x8_to_bf16(b1[0], b1[1], x1);
-    B[3] = fp8x8_to_bf16(b1[2], b1[3], x1);
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void stage_store_a(const Stage<PRECISE, NTW>& st, uint8_t* slot) {
+  const int tid = threadIdx.x;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(sA + ((m * 4 + j) * 1024) + lane * 16);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[j], acc[m], 0, 0, 0);
-      }
-  }
+  for (int i = 0; i < Stage<PRECISE, NTW>::kAPieces; ++i)
+    reinterpret_cast<i32x4*>(slot)[tid + 256 * i] = st.a[i];
 }
 
-__global__ __launch_bounds__(256) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
-                                                   const uint8_t* __restrict__ xs) {
-  __shared__ __align__(16) uint8_t sA[16384];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x;
-  const int tt = blockIdx.y * (kTokTile / 32) + wave;  // this wave's 32-token tile
-  const int nks = a.K / kKStep;
-  const uint8_t* xbase = xq + static_cast<size_t>(tt) * nks * kTileBytes;
-  const uint8_t* xsb = xs + static_cast<size_t>(tt) * nks * 64;
-
-  f32x16 acc[4];
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const uint8_t* slot,
+                                           f32x16 (&acc)[NTW][4]) {
+  const int lane = threadIdx.x & 63;
+  if (PRECISE) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-  if (precise_head(h, a.nkv))
-    mainloop_bf16(a, h, xbase, xsb, sA, acc);
-  else
-    mainloop_fp8(a, h, xbase, xsb, sA, acc);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) pin_registers(acc[m]);
-
-  // ---------------- epilogue: lane holds token tok, dims 32m + 8(r/4) + 4(l/32) + r%4
-  {
-#pragma clang fp contract(off)
-    const int tok = tt * 32 + (lane & 31);
-    const bool live = tok < a.S;
-    const int tk = live ? tok : a.S - 1;  // padded rows use clamped metadata
-    const int nkv = a.nkv;
-    const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
-    const int hi = (lane >> 5) * 4;
-    auto dim = [&](int m, int r) { return 32 * m + 8 * (r >> 2) + hi + (r & 3); };
-
-    int64_t slot = a.slot_mapping[tk];
-    const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
-    const int64_t page = slot_page(slot);
-    const int t = slot_row(slot);
-
-    if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale
-      const int j = h - v0;
-      double amax = 0.0;
+    for (int n = 0; n < NTW; ++n) {
+      const float x0 = e8m0_to_f32(st.sb[n] & 0xffu), x1 = e8m0_to_f32(st.sb[n] >> 8);
+      bf16x8 B[4];
+      B[0] = fp8x8_to_bf16(st.b[n][0][0], st.b[n][0][1], x0);
+      B[1] = fp8x8_to_bf16(st.b[n][0][2], st.b[n][0][3], x0);
+      B[2] = fp8x8_to_bf16(st.b[n][1][0], st.b[n][1][1], x1);
+      B[3] = fp8x8_to_bf16(st.b[n][1][2], st.b[n][1][3], x1);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) amax = fmax(amax, __builtin_fabs(static_cast<double>(acc[m][r])));
-      const double o = __shfl_xor(amax, 32, 64);
-      amax = amax > o ? amax : o;
-      const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
-      if (store_cache) {
-        uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes + t;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            vc[dim(m, r) * kPage] = static_cast<uint8_t>(
-                e4m3_from_f64(static_cast<double>(acc[m][r]) / static_cast<double>(s)));
-        if (lane < 32) a.v_scale[(page * nkv + j) * kPage + t] = s;
-      }
-      return;
-    }
-
-    const uint16_t* g = h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik));
-    double ss = 0.0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ss += static_cast<double>(acc[m][r]) * static_cast<double>(acc[m][r]);
-    ss += __shfl_xor(ss, 32, 64);
-    const double rr = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
-    int64_t pos = a.positions[tk];
-    pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
-    const uint16_t* cs = a.cos_sin + pos * kRotary;
-
-    double o[4][16];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        o[m][r] = (static_cast<double>(acc[m][r]) * rr) * (1.0 + static_cast<double>(bf16_to_f32(g[dim(m, r)])));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = dim(0, r);
-      const double c = static_cast<double>(bf16_to_f32(cs[i]));
-      const double sn = static_cast<double>(bf16_to_f32(cs[32 + i]));
-      const double x1 = o[0][r], x2 = o[1][r];
-      o[0][r] = x1 * c - x2 * sn;
-      o[1][r] = x2 * c + x1 * sn;
-    }
-
-    if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: bf16 out
-      uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
-                             : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim;
-      if (live) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t p0 = f32_to_bf16(static_cast<float>(o[m][4 * q])) |
-                          (f32_to_bf16(static_cast<float>(o[m][4 * q + 1])) << 16);
-            uint32_t p1 = f32_to_bf16(static_cast<float>(o[m][4 * q + 2])) |
-                          (f32_to_bf16(static_cast<float>(o[m][4 * q + 3])) << 16);
-            *reinterpret_cast<uint2*>(dst + dim(m, 4 * q)) = make_uint2(p0, p1);
-          }
-      }
-    } else if (h < v0) {  // K: per-token scale, shuffled page-16 layout
-      const int j = h - k0;
-      double amax = 0.0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) amax = fmax(amax, __builtin_fabs(o[m][r]));
-      const double ot = __shfl_xor(amax, 32, 64);
-      amax = amax > ot ? amax : ot;
-      const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
-      if (store_cache) {
-        uint8_t* kc = a.k_cache + (page * nkv + j) * kPageBytes + t * 16;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              w |= e4m3_from_f64(o[m][4 * q + e] / static_cast<double>(s)) << (8 * e);
-            const int d = dim(m, 4 * q);
-            *reinterpret_cast<uint32_t*>(kc + (d >> 4) * 256 + (d & 15)) = w;
-          }
-        if (lane < 32) a.k_scale[(page * nkv + j) * kPage + t] = s;
-      }
-    } else if (store_cache) {  // index_k: unit-scale E4M3 into the slot's row
-      uint8_t* ic = a.index_cache + slot * kHeadDim;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w |= e4m3_from_f64(o[m][4 * q + e]) << (8 * e);
-          *reinterpret_cast<uint32_t*>(ic + dim(m, 4 * q)) = w;
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(slot + (m * 4 + j) * 1024 + lane * 16);
+          acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[j], acc[n][m], 0, 0, 0);
         }
     }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const i32x4 a0 = reinterpret_cast<const i32x4*>(slot + m * kTileBytes)[lane];
+      const i32x4 a1 = reinterpret_cast<const i32x4*>(slot + m * kTileBytes + 1024)[lane];
+      const i32x8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) {
+        const i32x8 B = {st.b[n][0][0], st.b[n][0][1], st.b[n][0][2], st.b[n][0][3],
+                         st.b[n][1][0], st.b[n][1][1], st.b[n][1][2], st.b[n][1][3]};
+        switch (m) {  // the scale byte of row tile m (op_sel is an immediate)
+          case 0: acc[n][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][0], 0, 0, 0, st.sa, 0, st.sb[n]); break;
+          case 1: acc[n][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][1], 0, 0, 1, st.sa, 0, st.sb[n]); break;
+          case 2: acc[n][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][2], 0, 0, 2, st.sa, 0, st.sb[n]); break;
+          default: acc[n][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][3], 0, 0, 3, st.sa, 0, st.sb[n]); break;
+        }
+      }
+    }
   }
+}
+
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const uint8_t* __restrict__ xq,
+                                         const uint8_t* __restrict__ xs, uint8_t* lds,
+                                         f32x16 (&acc)[NTW][4]) {
+  constexpr int kSlot = PRECISE ? 16384 : 8192;
+  const int nks = a.K / kKStep;
+  Stage<PRECISE, NTW> st[3];
+  stage_load(st[0], a, h, tt0, xq, xs, 0);
+  if (nks > 1) stage_load(st[1], a, h, tt0, xq, xs, 1);
+  stage_store_a(st[0], lds);
+  __syncthreads();
+  // steps in groups of six so that register set (s % 3) and LDS slot (s % 2)
+  // are compile-time indices
+  for (int s0 = 0; s0 < nks; s0 += 6) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int s = s0 + i;
+      if (s < nks) {
+        if (s + 2 < nks) stage_load(st[(i + 2) % 3], a, h, tt0, xq, xs, s + 2);
+        stage_mfma(st[i % 3], lds + (i % 2) * kSlot, acc);
+        if (s + 1 < nks) stage_store_a(st[(i + 1) % 3], lds + ((i + 1) % 2) * kSlot);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue of one 32-token tile, read back from LDS where each wave has left its
+// 32 x 128 f32 tile (token rows of kEpiStride floats). Lane l takes token
+// tt * 32 + l % 32 and dims [64 (l / 32), 64 (l / 32) + 64): the lower half
+// holds both members (d, d + 32) of every rotated pair, the upper half none,
+// and runs the same code with cos = 1 and sin = 0, an exact identity in f64.
+// Loops are kept rolled: the 64 values never live in registers at once.
+constexpr int kEpiStride = kHeadDim + 4;  // floats per token row
+constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;
+
+__device__ __forceinline__ void unpack4(uint2 v, double (&o)[4]) {
+  o[0] = static_cast<double>(bf16_to_f32(v.x & 0xffffu));
+  o[1] = static_cast<double>(bf16_to_f32(v.x >> 16));
+  o[2] = static_cast<double>(bf16_to_f32(v.y & 0xffffu));
+  o[3] = static_cast<double>(bf16_to_f32(v.y >> 16));
+}
+
+__device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h, int tt) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int tok = tt * 32 + (lane & 31);
+  const bool live = tok < a.S;
+  const int tk = live ? tok : a.S - 1;  // padded rows use clamped metadata
+  const int nkv = a.nkv;
+  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
+  const int dbase = 64 * half;
+  x += dbase;  // x[i] is dim dbase + i of the token
+
+  const int64_t slot = a.slot_mapping[tk];
+  const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
+  const int64_t page = slot_page(slot);
+  const int t = slot_row(slot);
+
+  if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale
+    const int j = h - v0;
+    float am = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < 64; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(x + i);
+      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                                               __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+    }
+    double amax = static_cast<double>(am);  // a maximum of magnitudes is exact in f32
+    amax = __builtin_fmax(amax, __shfl_xor(amax, 32, 64));
+    const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
+    if (store_cache) {
+      const double sd = static_cast<double>(s), rcp = 1.0 / sd;
+      uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes + t + dbase * kPage;
+#pragma unroll 4
+      for (int i = 0; i < 64; ++i) vc[i * kPage] = static_cast<uint8_t>(e4m3_div(static_cast<double>(x[i]), sd, rcp));
+      if (lane < 32) a.v_scale[(page * nkv + j) * kPage + t] = s;
+    }
+    return;
+  }
+
+  double ssm[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+  for (int i = 0; i < 64; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    ssm[0] += static_cast<double>(v.x) * static_cast<double>(v.x);
+    ssm[1] += static_cast<double>(v.y) * static_cast<double>(v.y);
+    ssm[2] += static_cast<double>(v.z) * static_cast<double>(v.z);
+    ssm[3] += static_cast<double>(v.w) * static_cast<double>(v.w);
+  }
+  double ss = (ssm[0] + ssm[1]) + (ssm[2] + ssm[3]);
+  ss += __shfl_xor(ss, 32, 64);
+  const double rr = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
+  int64_t pos = a.positions[tk];
+  pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
+  const uint16_t* cs = a.cos_sin + pos * kRotary;
+  const uint16_t* gam = (h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik))) + dbase;
+
+  // One copy of the group code serves every head type: pass kOut stores bf16
+  // (q, index_q), kAmax finds the K row's scale, kCodes writes E4M3 codes
+  // (K with its scale into the shuffled page layout, index_k with unit scale).
+  enum { kOut, kAmax, kCodes };
+  int mode;
+  uint16_t* dst = nullptr;
+  uint8_t* cbase = nullptr;
+  int cstride = 0;  // bytes between 16-dim groups of the code row
+  double sd = 1.0, rcp = 1.0;
+  bool unit = false;
+  if (h < k0 || (h >= iq0 && h < ik0)) {
+    if (!live) return;
+    mode = kOut;
+    dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
+                  : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
+  } else if (h < v0) {
+    mode = kAmax;
+    cbase = a.k_cache + (page * nkv + (h - k0)) * kPageBytes + t * 16 + (dbase >> 4) * 256;
+    cstride = 256;
+  } else {
+    if (!store_cache) return;
+    mode = kCodes;
+    unit = true;
+    cbase = a.index_cache + slot * kHeadDim + dbase;
+    cstride = 16;
+  }
+  auto consume = [&](int i, const double (&v)[4], double& amax) {  // dims dbase + i .. + 3
+    if (mode == kOut) {
+      const uint32_t p0 = f32_to_bf16(static_cast<float>(v[0])) | (f32_to_bf16(static_cast<float>(v[1])) << 16);
+      const uint32_t p1 = f32_to_bf16(static_cast<float>(v[2])) | (f32_to_bf16(static_cast<float>(v[3])) << 16);
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(p0, p1);
+    } else if (mode == kAmax) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = __builtin_fmax(amax, __builtin_fabs(v[e]));
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= (unit ? e4m3_from_f64(v[e]) : e4m3_div(v[e], sd, rcp)) << (8 * e);
+      *reinterpret_cast<uint32_t*>(cbase + (i >> 4) * cstride + (i & 15)) = w;
+    }
+  };
+  double amax = 0.0;
+#pragma nounroll
+  for (;;) {
+#pragma nounroll
+    for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
+      const float4 a1 = *reinterpret_cast<const float4*>(x + i);
+      const float4 a2 = *reinterpret_cast<const float4*>(x + i + 32);
+      double g1[4], g2[4], cv[4], sv[4];
+      unpack4(*reinterpret_cast<const uint2*>(gam + i), g1);
+      unpack4(*reinterpret_cast<const uint2*>(gam + i + 32), g2);
+      if (half == 0) {
+        unpack4(*reinterpret_cast<const uint2*>(cs + i), cv);
+        unpack4(*reinterpret_cast<const uint2*>(cs + 32 + i), sv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cv[e] = 1.0, sv[e] = 0.0;
+      }
+      const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
+      double v1[4], v2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double x1 = (static_cast<double>(f1[e]) * rr) * (1.0 + g1[e]);
+        const double x2 = (static_cast<double>(f2[e]) * rr) * (1.0 + g2[e]);
+        v1[e] = x1 * cv[e] - x2 * sv[e];
+        v2[e] = x2 * cv[e] + x1 * sv[e];
+      }
+      consume(i, v1, amax);
+      consume(i + 32, v2, amax);
+    }
+    if (mode != kAmax) break;
+    amax = __builtin_fmax(amax, __shfl_xor(amax, 32, 64));
+    const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
+    if (!store_cache) break;
+    if (lane < 32) a.k_scale[(page * nkv + (h - k0)) * kPage + t] = s;
+    sd = static_cast<double>(s);
+    rcp = 1.0 / sd;
+    mode = kCodes;
+  }
+}
+
+// One CTA = one head x (4 * NTW) 32-token tiles. Tiles are assigned so that the
+// CTAs of each XCD (blocks b with the same b % 8, dispatched round-robin over
+// the eight XCDs) cover a contiguous range of heads across every token tile:
+// the heads' weight panels and the token tiles' activation panels are then
+// re-read from that XCD's L2 by the CTAs running together. The mapping is a
+// bijection onto the tiles whatever the hardware's placement.
+template <int NTW>
+__global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
+                                                      const uint8_t* __restrict__ xs, int mtiles) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int wave = threadIdx.x >> 6;
+  const int H = a.heads();
+  const int b = blockIdx.x;
+  const int xcd = b & 7, idx = b >> 3;
+  const int hx0 = xcd * H / 8, hx1 = (xcd + 1) * H / 8;
+  const int hxn = hx1 - hx0;
+  if (hxn == 0 || idx >= hxn * mtiles) return;  // blocks beyond this XCD's share
+  const int h = hx0 + idx % hxn;
+  const int mt = idx / hxn;
+  const int tt0 = (mt * 4 + wave) * NTW;  // this wave's first 32-token tile
+  stamp(a.timeline, a.timeline_slots, b, 0);
+
+  f32x16 acc[NTW][4];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[n][m][r] = 0.f;
+  if (precise_head(h, a.nkv))
+    mainloop<true, NTW>(a, h, tt0, xq, xs, lds, acc);
+  else
+    mainloop<false, NTW>(a, h, tt0, xq, xs, lds, acc);
+#pragma unroll
+  for (int n = 0; n < NTW; ++n)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pin_registers(acc[n][m]);
+  stamp(a.timeline, a.timeline_slots, b, 1);
+  // The main loop's last barrier follows its last LDS reads, so the ring can
+  // take the waves' output tiles. Lane l holds token l % 32 and dims
+  // 32m + 8(r/4) + 4(l/32) + r%4 in acc[n][m][r].
+  const int lane = threadIdx.x & 63;
+  float* tile = reinterpret_cast<float*>(lds + wave * kEpiWaveBytes);
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) {
+    if (n > 0) __syncthreads();  // the previous tile has been read
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(tile + (lane & 31) * kEpiStride + 32 * m + 8 * q + 4 * (lane >> 5)) =
+            f32x4{acc[n][m][4 * q], acc[n][m][4 * q + 1], acc[n][m][4 * q + 2], acc[n][m][4 * q + 3]};
+    __syncthreads();
+    tile_epilogue(a, tile + (lane & 31) * kEpiStride, h, tt0 + n);
+  }
+  stamp(a.timeline, a.timeline_slots, b, 2);
 }
 
 __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
@@ -458,7 +582,7 @@ hipError_t launch_prepass(const Args& a, const PrefillPlan& p, int mpad) {
 PrefillPlan prefill_plan(int M, int K, int nkv) {
   (void)nkv;
   PrefillPlan p{};
-  const size_t mpad = (static_cast<size_t>(M) + kTokTile - 1) / kTokTile * kTokTile;
+  const size_t mpad = (static_cast<size_t>(M) + kTokAlign - 1) / kTokAlign * kTokAlign;
   size_t off = 0;
   p.off_xq = off;
   off = align_up(off + mpad * K, 256);
@@ -477,7 +601,7 @@ size_t prefill_packed_weight_bytes(int N, int K) {
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
-  const int mpad = (a.S + kTokTile - 1) / kTokTile * kTokTile;
+  const int mpad = (a.S + kTokAlign - 1) / kTokAlign * kTokAlign;
   const int nv = (a.K / 8 + kPreThreads - 1) / kPreThreads;
   hipError_t e;
   switch (nv) {
@@ -492,9 +616,17 @@ hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  const int mtiles = (a.S + 127) / 128;
+  const int per_xcd = (a.heads() + 7) / 8 * mtiles;  // the largest XCD share
+  const size_t lds = 4 * kEpiWaveBytes;  // output tiles; the two A slots (2 x 16 KB) fit inside
+  // above the default 64 KB of dynamic LDS: raise the kernel's limit once
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_gemm<1>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(lds));
+  if (lds_ok != hipSuccess) return lds_ok;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_gemm, dim3(a.heads(), mpad / kTokTile), dim3(256), 0, a.stream, a,
-                     a.ws + p.off_xq, a.ws + p.off_xs);
+  hipLaunchKernelGGL(prefill_gemm<1>, dim3(8 * per_xcd), dim3(256), lds, a.stream, a,
+                     a.ws + p.off_xq, a.ws + p.off_xs, mtiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(a.ev_stop, a.stream);
 }
