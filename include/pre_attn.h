@@ -44,9 +44,10 @@
  *   iq_out           bf16 [tokens][nkv][128]
  *
  * Conventions for every entry point:
- *   - All data pointers are device pointers. ar, res, h_out, g_in, the packed
- *     weights, q_out, iq_out, the caches and the workspace must be 16-byte
- *     aligned; positions and slot_mapping 8-byte aligned.
+ *   - All data pointers are device pointers. ar, res, h_out, the five norm
+ *     weights, cos_sin, the packed weights, q_out, iq_out, the caches and the
+ *     workspace must be 16-byte aligned; positions and slot_mapping 8-byte
+ *     aligned; the float scale arrays 4-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *     work on it: they never synchronize the host and never allocate memory.
  *   - The library never frees or keeps caller memory. Outputs h_out, q_out

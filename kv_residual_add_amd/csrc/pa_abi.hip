@@ -84,8 +84,8 @@ int check_ptrs(const Ptrs& p) {
                        p.v_cache, p.k_scale, p.v_scale, p.index_cache, p.q_out, p.iq_out, p.ws};
   for (const void* q : all)
     if (!q) return PA_ERR_NULL;
-  const void* a16[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.q_out, p.iq_out,
-                       p.k_cache, p.v_cache, p.index_cache, p.ws};
+  const void* a16[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.q_out, p.iq_out, p.g_q, p.g_k,
+                       p.g_iq, p.g_ik, p.cos_sin, p.k_cache, p.v_cache, p.index_cache, p.ws};
   for (const void* q : a16)
     if (!aligned(q, 16)) return PA_ERR_ALIGN;
   const void* a8[] = {p.positions, p.slot_mapping};
@@ -94,9 +94,6 @@ int check_ptrs(const Ptrs& p) {
   const void* a4[] = {p.w_scales, p.k_scale, p.v_scale};
   for (const void* q : a4)
     if (!aligned(q, 4)) return PA_ERR_ALIGN;
-  const void* a2[] = {p.g_q, p.g_k, p.g_iq, p.g_ik, p.cos_sin};
-  for (const void* q : a2)
-    if (!aligned(q, 2)) return PA_ERR_ALIGN;
   return PA_OK;
 }
 

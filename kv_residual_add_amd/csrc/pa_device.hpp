@@ -159,6 +159,16 @@ __device__ __forceinline__ void stamp(uint64_t* tl, uint32_t slots, int b, int k
     tl[b * 8 + k] = __builtin_amdgcn_s_memrealtime();
 }
 
+// Where the stamping wave runs: XCC_ID (hardware register 20) in the upper
+// word, HW_ID (register 4: wave, SIMD, CU, shader array and engine) below.
+__device__ __forceinline__ void stamp_place(uint64_t* tl, uint32_t slots, int b, int k) {
+  if (tl != nullptr && threadIdx.x == 0 && static_cast<uint32_t>(b * 8 + k) < slots) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    tl[b * 8 + k] = (static_cast<uint64_t>(xcc) << 32) | hw;
+  }
+}
+
 // Page-16 addressing of a slot at the default (contiguous) page stride.
 __device__ __forceinline__ int64_t slot_page(int64_t slot) { return slot >> 4; }
 __device__ __forceinline__ int slot_row(int64_t slot) { return static_cast<int>(slot & 15); }

@@ -177,13 +177,16 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 // Main loop. A wave owns the whole 128-row head x NTW 32-token tiles; the CTA's
 // four waves share the head's weight tile, staged through a two-slot LDS ring,
 // while each wave keeps its own activation tiles in registers. Global loads run
-// two k steps ahead of the MFMAs (three register sets), so the ~0.4-1 us of L2
-// / Infinity Cache latency overlaps two steps of MFMA work.
+// kPrefetch k steps ahead of the MFMAs, so L2 and Infinity Cache latency (up to
+// about a microsecond when a load misses) overlaps that many steps of MFMA work.
 //
 // Per 64-wide k step, FP8 heads: A 8 KB (4 row tiles x 2 KB) + one scale dword
 // per lane; B per token tile 2 KB + one scale byte per lane. Precise heads: A is
 // the 16 KB bf16 copy (4 row tiles x 4 MFMA steps x 1 KB) and B is widened to
 // bf16 with its two block scales.
+// k steps that a step's global loads are issued ahead of their use
+constexpr int kPrefetch = 3;
+
 template <bool PRECISE, int NTW>
 struct Stage {
   static constexpr int kAPieces = PRECISE ? 4 : 2;  // dwordx4 per thread of A
@@ -193,35 +196,59 @@ struct Stage {
   uint32_t sb[NTW];  // FP8: the lane's B scale; precise: blocks 0 | 1 << 8
 };
 
+// Global loads of one k step go through buffer resources, one per operand
+// panel (the head's weight rows, the wave's token tiles): the per-lane offset
+// stays in one vector register for the whole loop and the step's offset is a
+// scalar, so no per-step 64-bit addresses occupy vector registers. A resource
+// also bounds its panel: a read past its size returns zeros instead of memory.
+constexpr int kBufWord3 = 0x00020000;  // raw, untyped buffer (gfx9 descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+
+struct Panels {
+  __amdgpu_buffer_rsrc_t a, sa, b, sb;
+};
+
 template <bool PRECISE, int NTW>
-__device__ __forceinline__ void stage_load(Stage<PRECISE, NTW>& st, const Args& a, int h, int tt0,
-                                           const uint8_t* __restrict__ xq,
-                                           const uint8_t* __restrict__ xs, int ks) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int nks = a.K / kKStep;
+__device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
+  const size_t nks = a.K / kKStep;
+  Panels p;
   if (PRECISE) {
-    const int p = precise_index(h, a.nkv);
-    const i32x4* src = reinterpret_cast<const i32x4*>(
-        a.w_packed + static_cast<size_t>(a.N()) * a.K + (static_cast<size_t>(p) * nks + ks) * 16384);
+    const size_t pi = precise_index(h, a.nkv);
+    p.a = panel(a.w_packed + static_cast<size_t>(a.N()) * a.K + pi * nks * 16384, nks * 16384);
+    p.sa = p.a;  // unused
+  } else {
+    p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
+    p.sa = panel(a.s_packed + static_cast<size_t>(h) * nks * 256, nks * 256);
+  }
+  p.b = panel(xq + static_cast<size_t>(tt0) * nks * kTileBytes, NTW * nks * kTileBytes);
+  p.sb = panel(xs + static_cast<size_t>(tt0) * nks * 64, NTW * nks * 64);
+  return p;
+}
+
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void stage_load(Stage<PRECISE, NTW>& st, const Panels& p, int nks, int ks) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (PRECISE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.a[i] = src[tid + 256 * i];
+    for (int i = 0; i < 4; ++i)
+      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 16384 + i * 4096, 0);
     st.sa = 0;
   } else {
-    const i32x4* src = reinterpret_cast<const i32x4*>(
-        a.w_packed + (static_cast<size_t>(h) * nks + ks) * 4 * kTileBytes);
-    st.a[0] = src[tid];
-    st.a[1] = src[tid + 256];
-    st.sa = reinterpret_cast<const uint32_t*>(a.s_packed)[(static_cast<size_t>(h) * nks + ks) * 64 + lane];
+    st.a[0] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 4 * kTileBytes, 0);
+    st.a[1] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 4 * kTileBytes + 4096, 0);
+    st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
   }
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
-    const size_t blk = static_cast<size_t>(tt0 + n) * nks + ks;
-    const i32x4* src = reinterpret_cast<const i32x4*>(xq + blk * kTileBytes);
-    st.b[n][0] = src[lane];
-    st.b[n][1] = src[lane + 64];
-    const uint8_t* sx = xs + blk * 64;
-    st.sb[n] = PRECISE ? (static_cast<uint32_t>(sx[lane & 31]) | (static_cast<uint32_t>(sx[(lane & 31) + 32]) << 8))
-                       : static_cast<uint32_t>(sx[lane]);
+    const int blk = n * nks + ks;
+    st.b[n][0] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes, 0);
+    st.b[n][1] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes + 1024, 0);
+    st.sb[n] = PRECISE ? (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane & 31, blk * 64, 0)) |
+                          (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, (lane & 31) + 32, blk * 64, 0)) << 8))
+                       : static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
   }
 }
 
@@ -280,24 +307,46 @@ __device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const ui
                                          const uint8_t* __restrict__ xs, uint8_t* lds,
                                          f32x16 (&acc)[NTW][4]) {
   constexpr int kSlot = PRECISE ? 16384 : 8192;
+  constexpr int kSets = kPrefetch + 1;  // register sets in rotation
   const int nks = a.K / kKStep;
-  Stage<PRECISE, NTW> st[3];
-  stage_load(st[0], a, h, tt0, xq, xs, 0);
-  if (nks > 1) stage_load(st[1], a, h, tt0, xq, xs, 1);
+  const int last = nks - 1;
+  const Panels p = make_panels<PRECISE, NTW>(a, h, tt0, xq, xs);
+  Stage<PRECISE, NTW> st[kSets];
+  // Issued step by step (no reordering across steps), so that the loads in
+  // flight when the loop starts are ordered as they are in every later group.
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) {
+    stage_load(st[i], p, nks, i < last ? i : last);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   stage_store_a(st[0], lds);
   __syncthreads();
-  // steps in groups of six so that register set (s % 3) and LDS slot (s % 2)
-  // are compile-time indices
-  for (int s0 = 0; s0 < nks; s0 += 6) {
+  // Step s computes from register set s % kSets and LDS slot s % 2 while the
+  // loads of step s + kPrefetch fill another set. In whole groups of kSets
+  // steps every load is issued unconditionally (the k step clamped to the last
+  // one; the extra loads at the end are never used), so the number of loads in
+  // flight is the same at every step and each wait covers only the step that
+  // needs its data.
+  static_assert(kSets % 2 == 0, "a group must return to LDS slot 0");
+  int s0 = 0;
+  for (; s0 + kSets <= nks; s0 += kSets) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < kSets; ++i) {
       const int s = s0 + i;
-      if (s < nks) {
-        if (s + 2 < nks) stage_load(st[(i + 2) % 3], a, h, tt0, xq, xs, s + 2);
-        stage_mfma(st[i % 3], lds + (i % 2) * kSlot, acc);
-        if (s + 1 < nks) stage_store_a(st[(i + 1) % 3], lds + ((i + 1) % 2) * kSlot);
-        __syncthreads();
-      }
+      stage_load(st[(i + kPrefetch) % kSets], p, nks, s + kPrefetch < last ? s + kPrefetch : last);
+      stage_mfma(st[i], lds + (i % 2) * kSlot, acc);
+      stage_store_a(st[(i + 1) % kSets], lds + ((i + 1) % 2) * kSlot);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kSets - 1; ++i) {  // the remaining nks % kSets steps
+    const int s = s0 + i;
+    if (s < nks) {
+      stage_load(st[(i + kPrefetch) % kSets], p, nks, s + kPrefetch < last ? s + kPrefetch : last);
+      stage_mfma(st[i], lds + (i % 2) * kSlot, acc);
+      stage_store_a(st[(i + 1) % kSets], lds + ((i + 1) % 2) * kSlot);
+      __syncthreads();
     }
   }
 }
@@ -308,30 +357,67 @@ __device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const ui
 // tt * 32 + l % 32 and dims [64 (l / 32), 64 (l / 32) + 64): the lower half
 // holds both members (d, d + 32) of every rotated pair, the upper half none,
 // and runs the same code with cos = 1 and sin = 0, an exact identity in f64.
-// Loops are kept rolled: the 64 values never live in registers at once.
+// The f32 values are read from LDS as they are needed, so the 64 of them never
+// live in registers as f64.
 constexpr int kEpiStride = kHeadDim + 4;  // floats per token row
 constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;
 
-__device__ __forceinline__ void unpack4(uint2 v, double (&o)[4]) {
-  o[0] = static_cast<double>(bf16_to_f32(v.x & 0xffffu));
-  o[1] = static_cast<double>(bf16_to_f32(v.x >> 16));
-  o[2] = static_cast<double>(bf16_to_f32(v.y & 0xffffu));
-  o[3] = static_cast<double>(bf16_to_f32(v.y >> 16));
+// The epilogue's global inputs, all requested before the accumulators go to
+// LDS so that their latency overlaps that hand-off: the lane's 64 gamma values
+// and, for the lower half, the 32 cos and 32 sin values of its token.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct EpiIn {
+  u32x4 g[8];   // gamma of dims dbase + 8j .. + 7
+  u32x4 c[4];   // cos of rotary index 8j .. + 7
+  u32x4 sn[4];  // sin of rotary index 8j .. + 7
+};
+
+__device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int h, int64_t pos) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const int nkv = a.nkv;
+  const uint16_t* gam = h < 16 * nkv ? a.g_q : (h < 17 * nkv ? a.g_k : (h < 19 * nkv ? a.g_iq : a.g_ik));
+  EpiIn in;
+  const u32x4* gp = reinterpret_cast<const u32x4*>(gam + 64 * half);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) in.g[j] = gp[j];
+  if (half == 0) {
+    const u32x4* cp = reinterpret_cast<const u32x4*>(a.cos_sin + pos * kRotary);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in.c[j] = cp[j], in.sn[j] = cp[4 + j];
+  } else {  // no rotation: cos = 1.0 (bf16 0x3f80), sin = 0
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in.c[j] = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u},
+                                in.sn[j] = u32x4{0u, 0u, 0u, 0u};
+  }
+  return in;
 }
 
-__device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h, int tt) {
+// bf16 element e (0..7) of a 16-byte piece, widened exactly to f32 / f64
+__device__ __forceinline__ float bf16_at_f32(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+__device__ __forceinline__ double bf16_at(const u32x4& v, int e) { return static_cast<double>(bf16_at_f32(v, e)); }
+
+// two floats to bf16 (round to nearest even; the hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h, int tok, int64_t slot,
+                              const EpiIn& in) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  const int tok = tt * 32 + (lane & 31);
   const bool live = tok < a.S;
-  const int tk = live ? tok : a.S - 1;  // padded rows use clamped metadata
   const int nkv = a.nkv;
   const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
   const int dbase = 64 * half;
   x += dbase;  // x[i] is dim dbase + i of the token
 
-  const int64_t slot = a.slot_mapping[tk];
   const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
@@ -369,28 +455,44 @@ __device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h,
   }
   double ss = (ssm[0] + ssm[1]) + (ssm[2] + ssm[3]);
   ss += __shfl_xor(ss, 32, 64);
-  const double rr = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
-  int64_t pos = a.positions[tk];
-  pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
-  const uint16_t* cs = a.cos_sin + pos * kRotary;
-  const uint16_t* gam = (h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik))) + dbase;
+  double rr = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
 
-  // One copy of the group code serves every head type: pass kOut stores bf16
-  // (q, index_q), kAmax finds the K row's scale, kCodes writes E4M3 codes
-  // (K with its scale into the shuffled page layout, index_k with unit scale).
-  enum { kOut, kAmax, kCodes };
+  if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: f32 norm and rotation, bf16 out
+    if (!live) return;
+    uint16_t* dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
+                            : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
+    const float rf = static_cast<float>(rr);
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
+      const float4 a1 = *reinterpret_cast<const float4*>(x + i);
+      const float4 a2 = *reinterpret_cast<const float4*>(x + i + 32);
+      const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
+      float v1[4], v2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = i + e;  // 0..31
+        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(in.g[d >> 3], d & 7));
+        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(in.g[4 + (d >> 3)], d & 7));
+        const float c = bf16_at_f32(in.c[d >> 3], d & 7), sn = bf16_at_f32(in.sn[d >> 3], d & 7);
+        v1[e] = x1 * c - x2 * sn;
+        v2[e] = x2 * c + x1 * sn;
+      }
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
+      *reinterpret_cast<uint2*>(dst + i + 32) = make_uint2(pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]));
+    }
+    return;
+  }
+
+  // K and index_k share one copy of the f64 group code: pass kAmax finds the K
+  // row's scale, pass kCodes writes E4M3 codes (K with its scale into the
+  // shuffled page layout, index_k with unit scale into its row).
+  enum { kAmax, kCodes };
   int mode;
-  uint16_t* dst = nullptr;
   uint8_t* cbase = nullptr;
   int cstride = 0;  // bytes between 16-dim groups of the code row
   double sd = 1.0, rcp = 1.0;
   bool unit = false;
-  if (h < k0 || (h >= iq0 && h < ik0)) {
-    if (!live) return;
-    mode = kOut;
-    dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
-                  : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
-  } else if (h < v0) {
+  if (h < v0) {
     mode = kAmax;
     cbase = a.k_cache + (page * nkv + (h - k0)) * kPageBytes + t * 16 + (dbase >> 4) * 256;
     cstride = 256;
@@ -402,11 +504,7 @@ __device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h,
     cstride = 16;
   }
   auto consume = [&](int i, const double (&v)[4], double& amax) {  // dims dbase + i .. + 3
-    if (mode == kOut) {
-      const uint32_t p0 = f32_to_bf16(static_cast<float>(v[0])) | (f32_to_bf16(static_cast<float>(v[1])) << 16);
-      const uint32_t p1 = f32_to_bf16(static_cast<float>(v[2])) | (f32_to_bf16(static_cast<float>(v[3])) << 16);
-      *reinterpret_cast<uint2*>(dst + i) = make_uint2(p0, p1);
-    } else if (mode == kAmax) {
+    if (mode == kAmax) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) amax = __builtin_fmax(amax, __builtin_fabs(v[e]));
     } else {
@@ -416,31 +514,35 @@ __device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h,
       *reinterpret_cast<uint32_t*>(cbase + (i >> 4) * cstride + (i & 15)) = w;
     }
   };
+  u32x4 g[8], c[4], sn[4];  // private copies the passes can mark as changed
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = in.g[j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = in.c[j], sn[j] = in.sn[j];
   double amax = 0.0;
 #pragma nounroll
   for (;;) {
-#pragma nounroll
+    // each pass recomputes the values: hoisted out of the loop, all 64 of them
+    // would be live in f64 at once
+    asm volatile("" : "+v"(rr));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(g[j]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(c[j]), "+v"(sn[j]));
+#pragma unroll
     for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
       const float4 a1 = *reinterpret_cast<const float4*>(x + i);
       const float4 a2 = *reinterpret_cast<const float4*>(x + i + 32);
-      double g1[4], g2[4], cv[4], sv[4];
-      unpack4(*reinterpret_cast<const uint2*>(gam + i), g1);
-      unpack4(*reinterpret_cast<const uint2*>(gam + i + 32), g2);
-      if (half == 0) {
-        unpack4(*reinterpret_cast<const uint2*>(cs + i), cv);
-        unpack4(*reinterpret_cast<const uint2*>(cs + 32 + i), sv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cv[e] = 1.0, sv[e] = 0.0;
-      }
       const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
       double v1[4], v2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double x1 = (static_cast<double>(f1[e]) * rr) * (1.0 + g1[e]);
-        const double x2 = (static_cast<double>(f2[e]) * rr) * (1.0 + g2[e]);
-        v1[e] = x1 * cv[e] - x2 * sv[e];
-        v2[e] = x2 * cv[e] + x1 * sv[e];
+        const int d = i + e;  // 0..31
+        const double x1 = (static_cast<double>(f1[e]) * rr) * (1.0 + bf16_at(g[d >> 3], d & 7));
+        const double x2 = (static_cast<double>(f2[e]) * rr) * (1.0 + bf16_at(g[4 + (d >> 3)], d & 7));
+        const double cd = bf16_at(c[d >> 3], d & 7), sd2 = bf16_at(sn[d >> 3], d & 7);
+        v1[e] = x1 * cd - x2 * sd2;
+        v2[e] = x2 * cd + x1 * sd2;
       }
       consume(i, v1, amax);
       consume(i + 32, v2, amax);
@@ -456,27 +558,48 @@ __device__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h,
   }
 }
 
-// One CTA = one head x (4 * NTW) 32-token tiles. Tiles are assigned so that the
-// CTAs of each XCD (blocks b with the same b % 8, dispatched round-robin over
-// the eight XCDs) cover a contiguous range of heads across every token tile:
-// the heads' weight panels and the token tiles' activation panels are then
-// re-read from that XCD's L2 by the CTAs running together. The mapping is a
+// Heads per XCD for the GEMM grid. Blocks b with the same b % 8 run on one XCD
+// (workgroups are dispatched round-robin over the eight XCDs), and each XCD
+// takes a list of heads across every token tile, so the CTAs running together
+// re-read those heads' weight panels and the token tiles' activation panels
+// from that XCD's L2. A precise head (bf16 MFMA) costs two FP8 heads; the lists
+// balance that cost (longest first, each to the least loaded XCD) and put the
+// precise heads first, so the longest CTAs of an XCD start earliest.
+constexpr int kMaxHeads = 19 * 4 + 1;  // 128-row heads at nkv = 4, the largest nkv accepted
+
+struct HeadMap {
+  uint8_t head[kMaxHeads];  // the XCDs' lists, one after another
+  uint8_t start[9];         // XCD x owns head[start[x] .. start[x + 1])
+};
+
+// One CTA = one head x (4 * NTW) 32-token tiles. Within an XCD the heads vary
+// fastest, so CTAs dispatched together share token tiles. The mapping is a
 // bijection onto the tiles whatever the hardware's placement.
 template <int NTW>
 __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
-                                                      const uint8_t* __restrict__ xs, int mtiles) {
+                                                      const uint8_t* __restrict__ xs, int mtiles, HeadMap map) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int wave = threadIdx.x >> 6;
-  const int H = a.heads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: panel bases stay scalar
   const int b = blockIdx.x;
   const int xcd = b & 7, idx = b >> 3;
-  const int hx0 = xcd * H / 8, hx1 = (xcd + 1) * H / 8;
-  const int hxn = hx1 - hx0;
-  if (hxn == 0 || idx >= hxn * mtiles) return;  // blocks beyond this XCD's share
-  const int h = hx0 + idx % hxn;
+  const int hx0 = map.start[xcd];
+  const int hxn = map.start[xcd + 1] - hx0;
+  if (idx >= hxn * mtiles) return;  // blocks beyond this XCD's share
+  const int h = map.head[hx0 + idx % hxn];
   const int mt = idx / hxn;
   const int tt0 = (mt * 4 + wave) * NTW;  // this wave's first 32-token tile
   stamp(a.timeline, a.timeline_slots, b, 0);
+  const int lane = threadIdx.x & 63;
+  // the tokens' slots and clamped positions, fetched now for the epilogue
+  int64_t slot_n[NTW], pos_n[NTW];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) {
+    const int tok = (tt0 + n) * 32 + (lane & 31);
+    const int tk = tok < a.S ? tok : a.S - 1;  // padded rows use clamped metadata
+    slot_n[n] = a.slot_mapping[tk];
+    const int64_t pos = a.positions[tk];
+    pos_n[n] = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
+  }
 
   f32x16 acc[NTW][4];
 #pragma unroll
@@ -497,10 +620,10 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
   // The main loop's last barrier follows its last LDS reads, so the ring can
   // take the waves' output tiles. Lane l holds token l % 32 and dims
   // 32m + 8(r/4) + 4(l/32) + r%4 in acc[n][m][r].
-  const int lane = threadIdx.x & 63;
   float* tile = reinterpret_cast<float*>(lds + wave * kEpiWaveBytes);
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
+    const EpiIn in = epilogue_loads(a, h, pos_n[n]);
     if (n > 0) __syncthreads();  // the previous tile has been read
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -509,9 +632,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
         *reinterpret_cast<f32x4*>(tile + (lane & 31) * kEpiStride + 32 * m + 8 * q + 4 * (lane >> 5)) =
             f32x4{acc[n][m][4 * q], acc[n][m][4 * q + 1], acc[n][m][4 * q + 2], acc[n][m][4 * q + 3]};
     __syncthreads();
-    tile_epilogue(a, tile + (lane & 31) * kEpiStride, h, tt0 + n);
+    if (n == 0) stamp(a.timeline, a.timeline_slots, b, 3);
+    tile_epilogue(a, tile + (lane & 31) * kEpiStride, h, (tt0 + n) * 32 + (lane & 31), slot_n[n], in);
   }
   stamp(a.timeline, a.timeline_slots, b, 2);
+  stamp_place(a.timeline, a.timeline_slots, b, 7);
 }
 
 __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
@@ -600,6 +725,33 @@ size_t prefill_packed_weight_bytes(int N, int K) {
 }
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
+HeadMap make_head_map(int nkv) {
+  const int H = 19 * nkv + 1;
+  auto precise = [&](int h) { return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv; };
+  int load[8] = {0}, count[8] = {0};
+  int owner[kMaxHeads];
+  for (int pass = 0; pass < 2; ++pass)  // precise heads (cost 2) first, then FP8 heads (cost 1)
+    for (int h = 0; h < H; ++h) {
+      if (precise(h) != (pass == 0)) continue;
+      int best = 0;
+      for (int x = 1; x < 8; ++x)
+        if (load[x] < load[best] || (load[x] == load[best] && count[x] < count[best])) best = x;
+      owner[h] = best;
+      load[best] += precise(h) ? 2 : 1;
+      ++count[best];
+    }
+  HeadMap m{};
+  int k = 0;
+  for (int x = 0; x < 8; ++x) {
+    m.start[x] = static_cast<uint8_t>(k);
+    for (int pass = 0; pass < 2; ++pass)
+      for (int h = 0; h < H; ++h)
+        if (owner[h] == x && precise(h) == (pass == 0)) m.head[k++] = static_cast<uint8_t>(h);
+  }
+  m.start[8] = static_cast<uint8_t>(k);
+  return m;
+}
+
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
   const int mpad = (a.S + kTokAlign - 1) / kTokAlign * kTokAlign;
   const int nv = (a.K / 8 + kPreThreads - 1) / kPreThreads;
@@ -617,7 +769,10 @@ hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
   }
   if (e != hipSuccess) return e;
   const int mtiles = (a.S + 127) / 128;
-  const int per_xcd = (a.heads() + 7) / 8 * mtiles;  // the largest XCD share
+  const HeadMap map = make_head_map(a.nkv);
+  int most = 0;  // heads of the largest XCD list
+  for (int x = 0; x < 8; ++x) most = map.start[x + 1] - map.start[x] > most ? map.start[x + 1] - map.start[x] : most;
+  const int per_xcd = most * mtiles;
   const size_t lds = 4 * kEpiWaveBytes;  // output tiles; the two A slots (2 x 16 KB) fit inside
   // above the default 64 KB of dynamic LDS: raise the kernel's limit once
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_gemm<1>),
@@ -626,7 +781,7 @@ hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
   if (lds_ok != hipSuccess) return lds_ok;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_gemm<1>, dim3(8 * per_xcd), dim3(256), lds, a.stream, a,
-                     a.ws + p.off_xq, a.ws + p.off_xs, mtiles);
+                     a.ws + p.off_xq, a.ws + p.off_xs, mtiles, map);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(a.ev_stop, a.stream);
 }

@@ -87,6 +87,10 @@ def test_invalid_arguments_rejected(fn):
     ptrs = [4096 * (i + 1) for i in range(21)]
     ptrs[11] += 4  # positions not 8-byte aligned
     assert _call(fn, _dims(), ptrs) == -2
+    for i, off in ((6, 8), (10, 2)):  # g_q, cos_sin: read in 16-byte pieces
+        ptrs = [4096 * (j + 1) for j in range(21)]
+        ptrs[i] += off
+        assert _call(fn, _dims(), ptrs) == -2
     assert _call(fn, _dims(), ws_bytes=16) == -6
     assert lib.pa_strerror(-6).decode().startswith("workspace")
 
