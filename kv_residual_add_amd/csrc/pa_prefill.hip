@@ -27,6 +27,8 @@
 // float64 with contraction off.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -174,33 +176,36 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// Main loop. A wave owns the whole 128-row head x NTW 32-token tiles; the CTA's
-// four waves share the head's weight tile, staged through a two-slot LDS ring,
-// while each wave keeps its own activation tiles in registers. Global loads run
-// kPrefetch k steps ahead of the MFMAs, so L2 and Infinity Cache latency (up to
-// about a microsecond when a load misses) overlaps that many steps of MFMA work.
+// Main loop. A wave owns the whole 128-row head x NTW 32-token tiles. The CTA's
+// four waves share the head's weight tile of each 64-wide k step, which the
+// buffer unit writes straight into a four-slot LDS ring (no registers on the
+// way), while each wave keeps its own activation tiles and the scales in one of
+// four register sets. A step's loads are issued kPrefetch steps ahead of its
+// MFMAs, so L2 and Infinity Cache latency (up to about a microsecond when a
+// load misses) overlaps that many steps of MFMA work.
 //
-// Per 64-wide k step, FP8 heads: A 8 KB (4 row tiles x 2 KB) + one scale dword
-// per lane; B per token tile 2 KB + one scale byte per lane. Precise heads: A is
-// the 16 KB bf16 copy (4 row tiles x 4 MFMA steps x 1 KB) and B is widened to
-// bf16 with its two block scales.
-// k steps that a step's global loads are issued ahead of their use
+// Per step, FP8 heads: weight 8 KB (4 row tiles x 2 KB) + one scale dword per
+// lane; activations per token tile 2 KB + one scale byte per lane. Precise
+// heads: the 16 KB bf16 weight copy (4 row tiles x 4 MFMA steps x 1 KB) and
+// the activations widened to bf16 with their two block scales.
+
+// k steps that a step's loads are issued ahead of its MFMAs; ring slots and
+// register sets: kPrefetch + 1
 constexpr int kPrefetch = 3;
+constexpr int kSlots = kPrefetch + 1;
+constexpr int kSlotBytes = 16384;  // one precise weight step; also one wave's 32 x 128 f32 output tile
 
 template <bool PRECISE, int NTW>
 struct Stage {
-  static constexpr int kAPieces = PRECISE ? 4 : 2;  // dwordx4 per thread of A
-  i32x4 a[kAPieces];
-  uint32_t sa;       // FP8: A scale dword (row tiles in bytes 0..3)
-  i32x4 b[NTW][2];   // B bytes 0..15 and 16..31 of the lane
-  uint32_t sb[NTW];  // FP8: the lane's B scale; precise: blocks 0 | 1 << 8
+  uint32_t sa;       // FP8: weight scale dword (row tiles in bytes 0..3)
+  i32x4 b[NTW][2];   // activation bytes 0..15 and 16..31 of the lane
+  uint32_t sb[NTW];  // FP8: the lane's activation scale; precise: blocks 0 | 1 << 8
 };
 
-// Global loads of one k step go through buffer resources, one per operand
-// panel (the head's weight rows, the wave's token tiles): the per-lane offset
-// stays in one vector register for the whole loop and the step's offset is a
-// scalar, so no per-step 64-bit addresses occupy vector registers. A resource
-// also bounds its panel: a read past its size returns zeros instead of memory.
+// Loads of one k step go through buffer resources, one per operand panel (the
+// head's weight rows, the wave's token tiles): the per-lane offset stays in one
+// vector register for the whole loop and the step's offset is a scalar. A
+// resource also bounds its panel: a read past its size returns zeros.
 constexpr int kBufWord3 = 0x00020000;  // raw, untyped buffer (gfx9 descriptor word 3)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
@@ -228,19 +233,23 @@ __device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, con
   return p;
 }
 
+// Vector-memory instructions one step issues per wave (the waits count them).
 template <bool PRECISE, int NTW>
-__device__ __forceinline__ void stage_load(Stage<PRECISE, NTW>& st, const Panels& p, int nks, int ks) {
+constexpr int step_vm_ops() {
+  return PRECISE ? 4 + 2 * NTW + 2 * NTW : 2 + 1 + 2 * NTW + NTW;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory instructions of
+// this wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; the
+// export and LDS/scalar counters left at their no-wait maxima)
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Issues step ks: the register loads first, then the weight tile's LDS writes.
+template <bool PRECISE, int NTW>
+__device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW>& st, const Panels& p, int nks, int ks,
+                                            uint8_t* slot, int wave) {
   const int tid = threadIdx.x, lane = tid & 63;
-  if (PRECISE) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 16384 + i * 4096, 0);
-    st.sa = 0;
-  } else {
-    st.a[0] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 4 * kTileBytes, 0);
-    st.a[1] = __builtin_amdgcn_raw_buffer_load_b128(p.a, tid * 16, ks * 4 * kTileBytes + 4096, 0);
-    st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
-  }
+  if (!PRECISE) st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
     const int blk = n * nks + ks;
@@ -250,14 +259,15 @@ __device__ __forceinline__ void stage_load(Stage<PRECISE, NTW>& st, const Panels
                           (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, (lane & 31) + 32, blk * 64, 0)) << 8))
                        : static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
   }
-}
-
-template <bool PRECISE, int NTW>
-__device__ __forceinline__ void stage_store_a(const Stage<PRECISE, NTW>& st, uint8_t* slot) {
-  const int tid = threadIdx.x;
+  // weight tile: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16,
+  // which land at the same offset of the slot (16 bytes per lane)
+  constexpr int kPieces = PRECISE ? 4 : 2;
+  const int step_bytes = PRECISE ? 16384 : 4 * kTileBytes;
 #pragma unroll
-  for (int i = 0; i < Stage<PRECISE, NTW>::kAPieces; ++i)
-    reinterpret_cast<i32x4*>(slot)[tid + 256 * i] = st.a[i];
+  for (int q = 0; q < kPieces; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        p.a, (__attribute__((address_space(3))) void*)(slot + q * 4096 + wave * 1024), 16, tid * 16,
+        ks * step_bytes + q * 4096, 0, 0);
 }
 
 template <bool PRECISE, int NTW>
@@ -265,21 +275,23 @@ __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const 
                                            f32x16 (&acc)[NTW][4]) {
   const int lane = threadIdx.x & 63;
   if (PRECISE) {
+    // one bf16 MFMA step j at a time: its widened activation slice (4 registers
+    // per token tile) serves the four row tiles
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-      const float x0 = e8m0_to_f32(st.sb[n] & 0xffu), x1 = e8m0_to_f32(st.sb[n] >> 8);
-      bf16x8 B[4];
-      B[0] = fp8x8_to_bf16(st.b[n][0][0], st.b[n][0][1], x0);
-      B[1] = fp8x8_to_bf16(st.b[n][0][2], st.b[n][0][3], x0);
-      B[2] = fp8x8_to_bf16(st.b[n][1][0], st.b[n][1][1], x1);
-      B[3] = fp8x8_to_bf16(st.b[n][1][2], st.b[n][1][3], x1);
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 B[NTW];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int n = 0; n < NTW; ++n) {
+        const float xsc = e8m0_to_f32(j < 2 ? (st.sb[n] & 0xffu) : (st.sb[n] >> 8));
+        const i32x4& src = st.b[n][j >> 1];
+        B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], xsc);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(slot + (m * 4 + j) * 1024 + lane * 16);
-          acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[j], acc[n][m], 0, 0, 0);
-        }
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(slot + (m * 4 + j) * 1024 + lane * 16);
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[n], acc[n][m], 0, 0, 0);
+      }
     }
   } else {
 #pragma unroll
@@ -302,85 +314,92 @@ __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const 
   }
 }
 
+// One step of the pipeline: wait until this wave's loads of step s have landed
+// (the two later steps' loads may still fly), barrier so every wave's part of
+// the weight tile is in LDS and every wave is done with step s - 1, then issue
+// step s + kPrefetch into the slot and register set step s - 1 used, and run
+// step s. The scheduling barriers keep each step's loads in issue order, which
+// the wait count relies on.
+template <bool PRECISE, int NTW, int I>
+__device__ __forceinline__ void pipeline_step(Stage<PRECISE, NTW> (&st)[kSlots], uint8_t* const (&ring)[kSlots],
+                                              const Panels& p, int nks, int s, int wave, f32x16 (&acc)[NTW][4]) {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kPrefetch - 1) * step_vm_ops<PRECISE, NTW>()));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const int last = nks - 1;
+  const int ahead = s + kPrefetch < last ? s + kPrefetch : last;  // clamped; extra steps are never used
+  stage_issue(st[(I + kPrefetch) % kSlots], p, nks, ahead, ring[(I + kPrefetch) % kSlots], wave);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_mfma(st[I], ring[I], acc);
+}
+
 template <bool PRECISE, int NTW>
 __device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const uint8_t* __restrict__ xq,
-                                         const uint8_t* __restrict__ xs, uint8_t* lds,
+                                         const uint8_t* __restrict__ xs, uint8_t* const (&ring)[kSlots], int wave,
                                          f32x16 (&acc)[NTW][4]) {
-  constexpr int kSlot = PRECISE ? 16384 : 8192;
-  constexpr int kSets = kPrefetch + 1;  // register sets in rotation
   const int nks = a.K / kKStep;
   const int last = nks - 1;
   const Panels p = make_panels<PRECISE, NTW>(a, h, tt0, xq, xs);
-  Stage<PRECISE, NTW> st[kSets];
-  // Issued step by step (no reordering across steps), so that the loads in
-  // flight when the loop starts are ordered as they are in every later group.
+  Stage<PRECISE, NTW> st[kSlots];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
-    stage_load(st[i], p, nks, i < last ? i : last);
+    stage_issue(st[i], p, nks, i < last ? i : last, ring[i], wave);
     __builtin_amdgcn_sched_barrier(0);
   }
-  stage_store_a(st[0], lds);
-  __syncthreads();
-  // Step s computes from register set s % kSets and LDS slot s % 2 while the
-  // loads of step s + kPrefetch fill another set. In whole groups of kSets
-  // steps every load is issued unconditionally (the k step clamped to the last
-  // one; the extra loads at the end are never used), so the number of loads in
-  // flight is the same at every step and each wait covers only the step that
-  // needs its data.
-  static_assert(kSets % 2 == 0, "a group must return to LDS slot 0");
+  // Whole groups of kSlots steps keep ring slot and register set indices
+  // static; the tail covers nks % kSlots steps.
   int s0 = 0;
-  for (; s0 + kSets <= nks; s0 += kSets) {
-#pragma unroll
-    for (int i = 0; i < kSets; ++i) {
-      const int s = s0 + i;
-      stage_load(st[(i + kPrefetch) % kSets], p, nks, s + kPrefetch < last ? s + kPrefetch : last);
-      stage_mfma(st[i], lds + (i % 2) * kSlot, acc);
-      stage_store_a(st[(i + 1) % kSets], lds + ((i + 1) % 2) * kSlot);
-      __syncthreads();
-    }
+  for (; s0 + kSlots <= nks; s0 += kSlots) {
+    pipeline_step<PRECISE, NTW, 0>(st, ring, p, nks, s0 + 0, wave, acc);
+    pipeline_step<PRECISE, NTW, 1>(st, ring, p, nks, s0 + 1, wave, acc);
+    pipeline_step<PRECISE, NTW, 2>(st, ring, p, nks, s0 + 2, wave, acc);
+    pipeline_step<PRECISE, NTW, 3>(st, ring, p, nks, s0 + 3, wave, acc);
   }
-#pragma unroll
-  for (int i = 0; i < kSets - 1; ++i) {  // the remaining nks % kSets steps
-    const int s = s0 + i;
-    if (s < nks) {
-      stage_load(st[(i + kPrefetch) % kSets], p, nks, s + kPrefetch < last ? s + kPrefetch : last);
-      stage_mfma(st[i], lds + (i % 2) * kSlot, acc);
-      stage_store_a(st[(i + 1) % kSets], lds + ((i + 1) % 2) * kSlot);
-      __syncthreads();
-    }
-  }
+  if (s0 + 0 < nks) pipeline_step<PRECISE, NTW, 0>(st, ring, p, nks, s0 + 0, wave, acc);
+  if (s0 + 1 < nks) pipeline_step<PRECISE, NTW, 1>(st, ring, p, nks, s0 + 1, wave, acc);
+  if (s0 + 2 < nks) pipeline_step<PRECISE, NTW, 2>(st, ring, p, nks, s0 + 2, wave, acc);
+  static_assert(kSlots == 4, "the group above is written out for four slots");
+  // every load (including the clamped extra steps) has landed and every wave
+  // is past its last LDS read before the ring is reused
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------------------
 // Epilogue of one 32-token tile, read back from LDS where each wave has left its
-// 32 x 128 f32 tile (token rows of kEpiStride floats). Lane l takes token
-// tt * 32 + l % 32 and dims [64 (l / 32), 64 (l / 32) + 64): the lower half
-// holds both members (d, d + 32) of every rotated pair, the upper half none,
-// and runs the same code with cos = 1 and sin = 0, an exact identity in f64.
-// The f32 values are read from LDS as they are needed, so the 64 of them never
-// live in registers as f64.
-constexpr int kEpiStride = kHeadDim + 4;  // floats per token row
-constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;
+// 32 x 128 f32 tile in one ring slot: token row r holds 32 16-byte chunks (4
+// dims each), chunk c stored at position c ^ r so that the 32 rows written or
+// read together fall on different banks. Lane l takes token tt * 32 + l % 32
+// and dims [64 (l / 32), 64 (l / 32) + 64): the lower half holds both members
+// (d, d + 32) of every rotated pair, the upper half none, and runs the same
+// code with cos = 1 and sin = 0, an exact identity. The values are read from
+// LDS as they are needed, so the 64 of them never live in registers as f64.
+struct TileRow {
+  const float* row;  // the token's row
+  int r;             // row index 0..31 (the swizzle key)
+  __device__ __forceinline__ float4 chunk(int c) const {  // dims 4c .. 4c + 3
+    return *reinterpret_cast<const float4*>(row + 4 * (c ^ r));
+  }
+  __device__ __forceinline__ float at(int d) const { return row[4 * ((d >> 2) ^ r) + (d & 3)]; }
+};
 
-// The epilogue's global inputs, all requested before the accumulators go to
-// LDS so that their latency overlaps that hand-off: the lane's 64 gamma values
-// and, for the lower half, the 32 cos and 32 sin values of its token.
+// The epilogue's per-token inputs, requested before the accumulators go to LDS
+// so that their latency overlaps that hand-off: for the lower half of the lanes
+// the 32 cos and 32 sin values of the token. (The head's gamma row is staged
+// in LDS when the CTA starts.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct EpiIn {
-  u32x4 g[8];   // gamma of dims dbase + 8j .. + 7
   u32x4 c[4];   // cos of rotary index 8j .. + 7
   u32x4 sn[4];  // sin of rotary index 8j .. + 7
 };
 
-__device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int h, int64_t pos) {
+__device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int64_t pos) {
   const int half = (threadIdx.x & 63) >> 5;
-  const int nkv = a.nkv;
-  const uint16_t* gam = h < 16 * nkv ? a.g_q : (h < 17 * nkv ? a.g_k : (h < 19 * nkv ? a.g_iq : a.g_ik));
   EpiIn in;
-  const u32x4* gp = reinterpret_cast<const u32x4*>(gam + 64 * half);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) in.g[j] = gp[j];
   if (half == 0) {
     const u32x4* cp = reinterpret_cast<const u32x4*>(a.cos_sin + pos * kRotary);
 #pragma unroll
@@ -391,6 +410,12 @@ __device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int h, int64_t po
                                 in.sn[j] = u32x4{0u, 0u, 0u, 0u};
   }
   return in;
+}
+
+// the gamma row of head h's role
+__device__ __forceinline__ const uint16_t* head_gamma(const Args& a, int h) {
+  const int nkv = a.nkv;
+  return h < 16 * nkv ? a.g_q : (h < 17 * nkv ? a.g_k : (h < 19 * nkv ? a.g_iq : a.g_ik));
 }
 
 // bf16 element e (0..7) of a 16-byte piece, widened exactly to f32 / f64
@@ -407,8 +432,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ void tile_epilogue(const Args& a, const float* __restrict__ x, int h, int tok, int64_t slot,
-                              const EpiIn& in) {
+__device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, const uint16_t* gam, int h, int tok,
+                                              int64_t slot, const EpiIn& in) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -416,7 +441,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
   const int nkv = a.nkv;
   const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
   const int dbase = 64 * half;
-  x += dbase;  // x[i] is dim dbase + i of the token
+  const int c0 = 16 * half;  // the lane's first chunk: dims dbase + 4 (c - c0) ..
 
   const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
   const int64_t page = slot_page(slot);
@@ -427,7 +452,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
     float am = 0.f;
 #pragma unroll 4
     for (int i = 0; i < 64; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(x + i);
+      const float4 v = x.chunk(c0 + (i >> 2));
       am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
                                                __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
     }
@@ -438,7 +463,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes + t + dbase * kPage;
 #pragma unroll 4
-      for (int i = 0; i < 64; ++i) vc[i * kPage] = static_cast<uint8_t>(e4m3_div(static_cast<double>(x[i]), sd, rcp));
+      for (int i = 0; i < 64; ++i) vc[i * kPage] = static_cast<uint8_t>(e4m3_div(static_cast<double>(x.at(dbase + i)), sd, rcp));
       if (lane < 32) a.v_scale[(page * nkv + j) * kPage + t] = s;
     }
     return;
@@ -447,7 +472,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
   double ssm[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 2
   for (int i = 0; i < 64; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    const float4 v = x.chunk(c0 + (i >> 2));
     ssm[0] += static_cast<double>(v.x) * static_cast<double>(v.x);
     ssm[1] += static_cast<double>(v.y) * static_cast<double>(v.y);
     ssm[2] += static_cast<double>(v.z) * static_cast<double>(v.z);
@@ -464,15 +489,17 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
     const float rf = static_cast<float>(rr);
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
-      const float4 a1 = *reinterpret_cast<const float4*>(x + i);
-      const float4 a2 = *reinterpret_cast<const float4*>(x + i + 32);
+      const float4 a1 = x.chunk(c0 + (i >> 2));
+      const float4 a2 = x.chunk(c0 + (i >> 2) + 8);
       const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
       float v1[4], v2[4];
+      const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + (i & ~7));       // dims of x1
+      const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + (i & ~7));  // dims of x2
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = i + e;  // 0..31
-        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(in.g[d >> 3], d & 7));
-        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(in.g[4 + (d >> 3)], d & 7));
+        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(ga, d & 7));
+        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(gb, d & 7));
         const float c = bf16_at_f32(in.c[d >> 3], d & 7), sn = bf16_at_f32(in.sn[d >> 3], d & 7);
         v1[e] = x1 * c - x2 * sn;
         v2[e] = x2 * c + x1 * sn;
@@ -514,9 +541,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
       *reinterpret_cast<uint32_t*>(cbase + (i >> 4) * cstride + (i & 15)) = w;
     }
   };
-  u32x4 g[8], c[4], sn[4];  // private copies the passes can mark as changed
-#pragma unroll
-  for (int j = 0; j < 8; ++j) g[j] = in.g[j];
+  u32x4 c[4], sn[4];  // private copies the passes can mark as changed
 #pragma unroll
   for (int j = 0; j < 4; ++j) c[j] = in.c[j], sn[j] = in.sn[j];
   double amax = 0.0;
@@ -524,22 +549,22 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const float* __rest
   for (;;) {
     // each pass recomputes the values: hoisted out of the loop, all 64 of them
     // would be live in f64 at once
-    asm volatile("" : "+v"(rr));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(g[j]));
+    asm volatile("" : "+v"(rr)::"memory");
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(c[j]), "+v"(sn[j]));
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
-      const float4 a1 = *reinterpret_cast<const float4*>(x + i);
-      const float4 a2 = *reinterpret_cast<const float4*>(x + i + 32);
+      const float4 a1 = x.chunk(c0 + (i >> 2));
+      const float4 a2 = x.chunk(c0 + (i >> 2) + 8);
       const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
+      const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + (i & ~7));
+      const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + (i & ~7));
       double v1[4], v2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = i + e;  // 0..31
-        const double x1 = (static_cast<double>(f1[e]) * rr) * (1.0 + bf16_at(g[d >> 3], d & 7));
-        const double x2 = (static_cast<double>(f2[e]) * rr) * (1.0 + bf16_at(g[4 + (d >> 3)], d & 7));
+        const double x1 = (static_cast<double>(f1[e]) * rr) * (1.0 + bf16_at(ga, d & 7));
+        const double x2 = (static_cast<double>(f2[e]) * rr) * (1.0 + bf16_at(gb, d & 7));
         const double cd = bf16_at(c[d >> 3], d & 7), sd2 = bf16_at(sn[d >> 3], d & 7);
         v1[e] = x1 * cd - x2 * sd2;
         v2[e] = x2 * cd + x1 * sd2;
@@ -578,8 +603,14 @@ struct HeadMap {
 template <int NTW>
 __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int mtiles, HeadMap map) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: panel bases stay scalar
+  // the weight ring; afterwards slot w holds wave w's output tile
+  __shared__ __align__(16) uint8_t ring0[kSlotBytes];
+  __shared__ __align__(16) uint8_t ring1[kSlotBytes];
+  __shared__ __align__(16) uint8_t ring2[kSlotBytes];
+  __shared__ __align__(16) uint8_t ring3[kSlotBytes];
+  __shared__ __align__(16) uint16_t gam_lds[kHeadDim];  // the head's gamma row
+  uint8_t* const ring[kSlots] = {ring0, ring1, ring2, ring3};
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: bases stay scalar
   const int b = blockIdx.x;
   const int xcd = b & 7, idx = b >> 3;
   const int hx0 = map.start[xcd];
@@ -590,6 +621,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
   const int tt0 = (mt * 4 + wave) * NTW;  // this wave's first 32-token tile
   stamp(a.timeline, a.timeline_slots, b, 0);
   const int lane = threadIdx.x & 63;
+  if (threadIdx.x < kHeadDim / 8)  // read before the epilogue: the main loop's barriers order it
+    reinterpret_cast<u32x4*>(gam_lds)[threadIdx.x] = reinterpret_cast<const u32x4*>(head_gamma(a, h))[threadIdx.x];
   // the tokens' slots and clamped positions, fetched now for the epilogue
   int64_t slot_n[NTW], pos_n[NTW];
 #pragma unroll
@@ -609,32 +642,40 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[n][m][r] = 0.f;
   if (precise_head(h, a.nkv))
-    mainloop<true, NTW>(a, h, tt0, xq, xs, lds, acc);
+    mainloop<true, NTW>(a, h, tt0, xq, xs, ring, wave, acc);
   else
-    mainloop<false, NTW>(a, h, tt0, xq, xs, lds, acc);
+    mainloop<false, NTW>(a, h, tt0, xq, xs, ring, wave, acc);
 #pragma unroll
   for (int n = 0; n < NTW; ++n)
 #pragma unroll
     for (int m = 0; m < 4; ++m) pin_registers(acc[n][m]);
   stamp(a.timeline, a.timeline_slots, b, 1);
-  // The main loop's last barrier follows its last LDS reads, so the ring can
-  // take the waves' output tiles. Lane l holds token l % 32 and dims
-  // 32m + 8(r/4) + 4(l/32) + r%4 in acc[n][m][r].
-  float* tile = reinterpret_cast<float*>(lds + wave * kEpiWaveBytes);
-#pragma unroll
-  for (int n = 0; n < NTW; ++n) {
-    const EpiIn in = epilogue_loads(a, h, pos_n[n]);
+  // The main loop ends with every load landed and every wave past its last LDS
+  // read. Lane l holds token l % 32 and dims 32m + 8(r/4) + 4(l/32) + r%4 in
+  // acc[n][m][r]: chunk 8m + 2(r/4) + l/32 of row l % 32.
+  float* tile = reinterpret_cast<float*>(wave == 0 ? ring0 : wave == 1 ? ring1 : wave == 2 ? ring2 : ring3);
+  const int row = lane & 31;
+  const TileRow tr{tile + row * kHeadDim, row};
+  // one token tile at a time (written out per tile: a loop over n would index
+  // the accumulators at run time)
+  auto epilogue = [&](const f32x16 (&accn)[4], int n, int64_t slot, int64_t pos) {
+    const EpiIn in = epilogue_loads(a, pos);
     if (n > 0) __syncthreads();  // the previous tile has been read
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(tile + (lane & 31) * kEpiStride + 32 * m + 8 * q + 4 * (lane >> 5)) =
-            f32x4{acc[n][m][4 * q], acc[n][m][4 * q + 1], acc[n][m][4 * q + 2], acc[n][m][4 * q + 3]};
+      for (int q = 0; q < 4; ++q) {
+        const int c = 8 * m + 2 * q + (lane >> 5);
+        *reinterpret_cast<f32x4*>(tile + row * kHeadDim + 4 * (c ^ row)) =
+            f32x4{accn[m][4 * q], accn[m][4 * q + 1], accn[m][4 * q + 2], accn[m][4 * q + 3]};
+      }
     __syncthreads();
     if (n == 0) stamp(a.timeline, a.timeline_slots, b, 3);
-    tile_epilogue(a, tile + (lane & 31) * kEpiStride, h, (tt0 + n) * 32 + (lane & 31), slot_n[n], in);
-  }
+    tile_epilogue(a, tr, gam_lds, h, (tt0 + n) * 32 + row, slot, in);
+  };
+  epilogue(acc[0], 0, slot_n[0], pos_n[0]);
+  if constexpr (NTW > 1) epilogue(acc[1], 1, slot_n[1], pos_n[1]);
+  static_assert(NTW <= 2, "the epilogue calls above cover two token tiles");
   stamp(a.timeline, a.timeline_slots, b, 2);
   stamp_place(a.timeline, a.timeline_slots, b, 7);
 }
@@ -725,6 +766,19 @@ size_t prefill_packed_weight_bytes(int N, int K) {
 }
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
+// Token tiles of 32 per wave: 1 (128-token CTAs) or 2 (256-token CTAs, half
+// the LDS and a quarter less L2 traffic per MFMA). A CU finishes about one CTA
+// per CTA-time however many it holds at once, so a launch of n CTAs takes
+// ceil(n / CUs) CTA-times; the larger tile is taken unless that quantization
+// costs it more than its per-flop gain (about 1.3x).
+int prefill_token_tiles_per_wave(int M, int heads, int cus) {
+  auto eff = [&](int tok) {
+    const double n = static_cast<double>(heads) * ((M + tok - 1) / tok) / cus;
+    return n / std::ceil(n);
+  };
+  return eff(256) * 1.3 >= eff(128) ? 2 : 1;
+}
+
 HeadMap make_head_map(int nkv) {
   const int H = 19 * nkv + 1;
   auto precise = [&](int h) { return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv; };
@@ -768,20 +822,23 @@ hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const int mtiles = (a.S + 127) / 128;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int ntw = prefill_token_tiles_per_wave(a.S, a.heads(), cus);
+  const int mtiles = (a.S + 128 * ntw - 1) / (128 * ntw);
   const HeadMap map = make_head_map(a.nkv);
   int most = 0;  // heads of the largest XCD list
   for (int x = 0; x < 8; ++x) most = map.start[x + 1] - map.start[x] > most ? map.start[x + 1] - map.start[x] : most;
   const int per_xcd = most * mtiles;
-  const size_t lds = 4 * kEpiWaveBytes;  // output tiles; the two A slots (2 x 16 KB) fit inside
-  // above the default 64 KB of dynamic LDS: raise the kernel's limit once
-  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_gemm<1>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       static_cast<int>(lds));
-  if (lds_ok != hipSuccess) return lds_ok;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_gemm<1>, dim3(8 * per_xcd), dim3(256), lds, a.stream, a,
-                     a.ws + p.off_xq, a.ws + p.off_xs, mtiles, map);
+  if (ntw == 2)
+    hipLaunchKernelGGL(prefill_gemm<2>, dim3(8 * per_xcd), dim3(256), 0, a.stream, a, a.ws + p.off_xq,
+                       a.ws + p.off_xs, mtiles, map);
+  else
+    hipLaunchKernelGGL(prefill_gemm<1>, dim3(8 * per_xcd), dim3(256), 0, a.stream, a, a.ws + p.off_xq,
+                       a.ws + p.off_xs, mtiles, map);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(a.ev_stop, a.stream);
 }
