@@ -412,11 +412,18 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   const int N = (19 * nkv + 1) * 128;
   const int nchk = K / 128;
   const int heads = N / kHeadDim;
+  // The largest chunk count that still gives every CU a CTA, among those whose
+  // whole grid is resident at once (a grid in two rounds streams its second
+  // half only after the first has finished). CTAs per CU allowed by the
+  // kernel's register allocation at 256 threads, for 1..4 chunks (the compiler
+  // reports about 70, 104, 168 and 262 registers a lane with two token tiles).
   static const int kCands[] = {4, 3, 2, 1};
+  static const int kPerCu[] = {0, 7, 4, 3, 1};
   int pick = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
     if (static_cast<size_t>(S) * (c * 128 + kLdsPad) > kMaxLds) continue;
+    if (heads * (nchk / c) > 256 * kPerCu[c]) continue;
     pick = c;  // smallest fitting candidate so far
     if (heads * (nchk / c) >= 256) break;
   }
