@@ -153,22 +153,14 @@ __global__ __launch_bounds__(kPreThreads) void prefill_prepass(
   }
 }
 
-// Packed weight, FP8 part (every head): head h, k step ks, 32-row tile m ->
-// 2 KB block at ((h * nks + ks) * 4 + m) * 2048 in the activation's lane order
-// (row 32m + l % 32). Scales: dword (h * nks + ks) * 64 + l holds tiles
-// m = 0..3 in bytes 0..3, each the row's E8M0 for block 2 ks + l / 32.
-// bf16 part (k, v and index_k heads, index p = 0 .. 2 nkv), after the N x K FP8
-// bytes: 1 KB block (((p * nks + ks) * 4 + m) * 4 + j) * 1024 for bf16 MFMA step
-// j of the k step; lane l's 8 values (row 32m + l % 32) sit at 16 l and are
-// k = 64 ks + 32 (j / 2) + 16 (l / 32) + 8 (j % 2) + [0, 8), times the block
-// scale: exactly the FP8 bytes 8 (j % 2) .. + 8 of region j / 2 of the lane.
+// Packed weight: head h, k step ks, 32-row tile m -> 2 KB block at
+// ((h * nks + ks) * 4 + m) * 2048 in the activation's lane order (row
+// 32m + l % 32). Scales: dword (h * nks + ks) * 64 + l holds tiles m = 0..3 in
+// bytes 0..3, each the row's E8M0 for block 2 ks + l / 32. The precise heads
+// (k, v, index_k) read the same FP8 tiles and widen them to bf16 themselves.
 
 __device__ __forceinline__ bool precise_head(int h, int nkv) {
   return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv;
-}
-
-__device__ __forceinline__ int precise_index(int h, int nkv) {
-  return h == 19 * nkv ? 2 * nkv : h - 16 * nkv;
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
@@ -184,22 +176,22 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 // MFMAs, so L2 and Infinity Cache latency (up to about a microsecond when a
 // load misses) overlaps that many steps of MFMA work.
 //
-// Per step, FP8 heads: weight 8 KB (4 row tiles x 2 KB) + one scale dword per
-// lane; activations per token tile 2 KB + one scale byte per lane. Precise
-// heads: the 16 KB bf16 weight copy (4 row tiles x 4 MFMA steps x 1 KB) and
-// the activations widened to bf16 with their two block scales.
+// Per step: weight 8 KB (4 row tiles x 2 KB) + one scale dword per lane;
+// activations per token tile 2 KB + one scale byte per lane. FP8 heads feed
+// them to the block-scaled FP8 MFMA; precise heads widen both operands exactly
+// to bf16 (the code times its block scale) for the bf16 MFMA.
 
 // k steps that a step's loads are issued ahead of its MFMAs; ring slots and
 // register sets: kPrefetch + 1
 constexpr int kPrefetch = 3;
 constexpr int kSlots = kPrefetch + 1;
-constexpr int kSlotBytes = 16384;  // one precise weight step; also one wave's 32 x 128 f32 output tile
+constexpr int kSlotBytes = 16384;  // a weight step uses 8 KB; a slot also holds one wave's 32 x 128 f32 output tile
 
 template <bool PRECISE, int NTW>
 struct Stage {
-  uint32_t sa;       // FP8: weight scale dword (row tiles in bytes 0..3)
+  uint32_t sa;       // weight scale dword (row tiles in bytes 0..3) for block lane / 32
   i32x4 b[NTW][2];   // activation bytes 0..15 and 16..31 of the lane
-  uint32_t sb[NTW];  // FP8: the lane's activation scale; precise: blocks 0 | 1 << 8
+  uint32_t sb[NTW];  // the lane's activation scale (its token, block lane / 32)
 };
 
 // Loads of one k step go through buffer resources, one per operand panel (the
@@ -220,14 +212,8 @@ template <bool PRECISE, int NTW>
 __device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
   const size_t nks = a.K / kKStep;
   Panels p;
-  if (PRECISE) {
-    const size_t pi = precise_index(h, a.nkv);
-    p.a = panel(a.w_packed + static_cast<size_t>(a.N()) * a.K + pi * nks * 16384, nks * 16384);
-    p.sa = p.a;  // unused
-  } else {
-    p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
-    p.sa = panel(a.s_packed + static_cast<size_t>(h) * nks * 256, nks * 256);
-  }
+  p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
+  p.sa = panel(a.s_packed + static_cast<size_t>(h) * nks * 256, nks * 256);
   p.b = panel(xq + static_cast<size_t>(tt0) * nks * kTileBytes, NTW * nks * kTileBytes);
   p.sb = panel(xs + static_cast<size_t>(tt0) * nks * 64, NTW * nks * 64);
   return p;
@@ -236,7 +222,7 @@ __device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, con
 // Vector-memory instructions one step issues per wave (the waits count them).
 template <bool PRECISE, int NTW>
 constexpr int step_vm_ops() {
-  return PRECISE ? 4 + 2 * NTW + 2 * NTW : 2 + 1 + 2 * NTW + NTW;
+  return 2 + 1 + 2 * NTW + NTW;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory instructions of
@@ -249,25 +235,21 @@ template <bool PRECISE, int NTW>
 __device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW>& st, const Panels& p, int nks, int ks,
                                             uint8_t* slot, int wave) {
   const int tid = threadIdx.x, lane = tid & 63;
-  if (!PRECISE) st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
+  st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
     const int blk = n * nks + ks;
     st.b[n][0] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes, 0);
     st.b[n][1] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes + 1024, 0);
-    st.sb[n] = PRECISE ? (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane & 31, blk * 64, 0)) |
-                          (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, (lane & 31) + 32, blk * 64, 0)) << 8))
-                       : static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
+    st.sb[n] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
   }
   // weight tile: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16,
   // which land at the same offset of the slot (16 bytes per lane)
-  constexpr int kPieces = PRECISE ? 4 : 2;
-  const int step_bytes = PRECISE ? 16384 : 4 * kTileBytes;
 #pragma unroll
-  for (int q = 0; q < kPieces; ++q)
+  for (int q = 0; q < 2; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         p.a, (__attribute__((address_space(3))) void*)(slot + q * 4096 + wave * 1024), 16, tid * 16,
-        ks * step_bytes + q * 4096, 0, 0);
+        ks * 4 * kTileBytes + q * 4096, 0, 0);
 }
 
 template <bool PRECISE, int NTW>
@@ -275,20 +257,29 @@ __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const 
                                            f32x16 (&acc)[NTW][4]) {
   const int lane = threadIdx.x & 63;
   if (PRECISE) {
-    // one bf16 MFMA step j at a time: its widened activation slice (4 registers
-    // per token tile) serves the four row tiles
+    // bf16 MFMA step j takes bytes 8j .. 8j + 7 of each lane's 32-byte fragment
+    // (k = 32 (j / 2) + 16 (lane / 32) + 8 (j % 2) + [0, 8)), widened exactly
+    // with the block scale; bytes 0..15 are MX block 0 and 16..31 block 1, and
+    // the lane ^ 32 partner holds the scales of the other block.
+    const uint32_t sa_x = __shfl_xor(st.sa, 32, 64);
+    uint32_t sb_x[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) sb_x[n] = __shfl_xor(st.sb[n], 32, 64);
+    const bool low = lane < 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const bool own = (j < 2) == low;  // this lane's own block
       bf16x8 B[NTW];
 #pragma unroll
       for (int n = 0; n < NTW; ++n) {
-        const float xsc = e8m0_to_f32(j < 2 ? (st.sb[n] & 0xffu) : (st.sb[n] >> 8));
         const i32x4& src = st.b[n][j >> 1];
-        B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], xsc);
+        B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], e8m0_to_f32((own ? st.sb[n] : sb_x[n]) & 0xffu));
       }
+      const uint32_t sw = own ? st.sa : sa_x;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(slot + (m * 4 + j) * 1024 + lane * 16);
+        const uint2 af = *reinterpret_cast<const uint2*>(slot + m * kTileBytes + (j >> 1) * 1024 + lane * 16 + (j & 1) * 8);
+        const bf16x8 A = fp8x8_to_bf16(af.x, af.y, e8m0_to_f32((sw >> (8 * m)) & 0xffu));
 #pragma unroll
         for (int n = 0; n < NTW; ++n) acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[n], acc[n][m], 0, 0, 0);
       }
@@ -701,41 +692,6 @@ __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __res
 }
 
 // bf16 copy of the k, v and index_k heads (one thread per 8 values).
-__global__ void pack_prefill_bf16(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
-                                  uint8_t* __restrict__ wb, int nkv, int K) {
-  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int nks = K / kKStep;
-  const size_t pieces = static_cast<size_t>(2 * nkv + 1) * nks * 4 * 4 * 64;
-  if (idx >= pieces) return;
-  const int l = static_cast<int>(idx & 63);
-  const int j = static_cast<int>((idx >> 6) & 3);
-  const int m = static_cast<int>((idx >> 8) & 3);
-  const size_t pk = idx >> 10;
-  const int p = static_cast<int>(pk / nks), ks = static_cast<int>(pk % nks);
-  const int head = p < 2 * nkv ? 16 * nkv + p : 19 * nkv;
-  const int row = head * 128 + m * 32 + (l & 31);
-  const int k = ks * kKStep + 32 * (j >> 1) + 16 * (l >> 5) + 8 * (j & 1);
-  const uint8_t* src = w + static_cast<size_t>(row) * K + k;
-  const int e = we[static_cast<size_t>(row) * (K / 32) + (k >> 5)];
-  uint32_t out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t two = 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t c = src[2 * i + q];
-      const uint32_t sgn = c & 0x80u, ex = (c >> 3) & 0xfu, mt = c & 7u;
-      // E4M3 value as float32, then times 2^(e - 127); exact in bf16
-      float v = ex ? __uint_as_float(((ex + 120u) << 23) | (mt << 20)) : static_cast<float>(mt) * 0x1p-9f;
-      v = __builtin_ldexpf(v, e - 127);
-      uint32_t bits = (__float_as_uint(v) >> 16) | (sgn << 8);
-      two |= bits << (16 * q);
-    }
-    out[i] = two;
-  }
-  *reinterpret_cast<uint4*>(wb + idx * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-}
-
 template <int NV>
 hipError_t launch_prepass(const Args& a, const PrefillPlan& p, int mpad) {
   hipLaunchKernelGGL(prefill_prepass<NV>, dim3(mpad), dim3(kPreThreads), 0, a.stream, a.ar, a.res,
@@ -760,10 +716,7 @@ PrefillPlan prefill_plan(int M, int K, int nkv) {
   return p;
 }
 
-size_t prefill_packed_weight_bytes(int N, int K) {
-  const int nkv = (N / 128 - 1) / 19;
-  return static_cast<size_t>(N) * K + static_cast<size_t>(2 * nkv + 1) * 128 * K * 2;
-}
+size_t prefill_packed_weight_bytes(int N, int K) { return static_cast<size_t>(N) * K; }
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
 // Token tiles of 32 per wave: 1 (128-token CTAs) or 2 (256-token CTAs, half
@@ -848,12 +801,6 @@ hipError_t launch_pack_prefill(const uint8_t* w, const uint8_t* we, uint8_t* wp,
   const size_t pieces = static_cast<size_t>(N) * K / 16;
   const unsigned blocks = static_cast<unsigned>((pieces + 255) / 256);
   hipLaunchKernelGGL(pack_prefill, dim3(blocks), dim3(256), 0, s, w, we, wp, sp, N, K);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkv = (N / 128 - 1) / 19;
-  const size_t pieces16 = static_cast<size_t>(2 * nkv + 1) * (K / kKStep) * 1024;
-  hipLaunchKernelGGL(pack_prefill_bf16, dim3(static_cast<unsigned>((pieces16 + 255) / 256)), dim3(256),
-                     0, s, w, we, wp + static_cast<size_t>(N) * K, nkv, K);
   return hipGetLastError();
 }
 
