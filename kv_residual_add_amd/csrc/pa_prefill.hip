@@ -586,9 +586,12 @@ constexpr int kMaxHeads = 19 * 4 + 1;  // 128-row heads at nkv = 4, the largest 
 struct HeadMap {
   uint8_t head[kMaxHeads];  // the XCDs' lists, one after another
   uint8_t start[9];         // XCD x owns head[start[x] .. start[x + 1])
+  uint8_t nprecise[8];      // its first nprecise[x] heads are precise heads
 };
 
-// One CTA = one head x (4 * NTW) 32-token tiles. Within an XCD the heads vary
+// One CTA = one head x (4 * NTW) 32-token tiles. An XCD first runs every tile
+// of its precise heads (the longest CTAs start first, so they do not form the
+// kernel's tail), then those of its FP8 heads; within each part the heads vary
 // fastest, so CTAs dispatched together share token tiles. The mapping is a
 // bijection onto the tiles whatever the hardware's placement.
 template <int NTW>
@@ -607,8 +610,16 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
   const int hx0 = map.start[xcd];
   const int hxn = map.start[xcd + 1] - hx0;
   if (idx >= hxn * mtiles) return;  // blocks beyond this XCD's share
-  const int h = map.head[hx0 + idx % hxn];
-  const int mt = idx / hxn;
+  const int np = map.nprecise[xcd];
+  int h, mt;
+  if (idx < np * mtiles) {
+    h = map.head[hx0 + idx % np];
+    mt = idx / np;
+  } else {
+    const int j = idx - np * mtiles, nf = hxn - np;
+    h = map.head[hx0 + np + j % nf];
+    mt = j / nf;
+  }
   const int tt0 = (mt * 4 + wave) * NTW;  // this wave's first 32-token tile
   stamp(a.timeline, a.timeline_slots, b, 0);
   const int lane = threadIdx.x & 63;
@@ -753,7 +764,10 @@ HeadMap make_head_map(int nkv) {
     m.start[x] = static_cast<uint8_t>(k);
     for (int pass = 0; pass < 2; ++pass)
       for (int h = 0; h < H; ++h)
-        if (owner[h] == x && precise(h) == (pass == 0)) m.head[k++] = static_cast<uint8_t>(h);
+        if (owner[h] == x && precise(h) == (pass == 0)) {
+          m.head[k++] = static_cast<uint8_t>(h);
+          if (pass == 0) ++m.nprecise[x];
+        }
   }
   m.start[8] = static_cast<uint8_t>(k);
   return m;
