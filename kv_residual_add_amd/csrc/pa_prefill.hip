@@ -460,6 +460,49 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
     return;
   }
 
+  if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: f32 norm and rotation, bf16 out
+    if (!live) return;  // both lanes of a token return together
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const float4 v = x.chunk(c0 + (i >> 2));
+      s4[0] = __builtin_fmaf(v.x, v.x, s4[0]);
+      s4[1] = __builtin_fmaf(v.y, v.y, s4[1]);
+      s4[2] = __builtin_fmaf(v.z, v.z, s4[2]);
+      s4[3] = __builtin_fmaf(v.w, v.w, s4[3]);
+    }
+    float ssf = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    ssf += __shfl_xor(ssf, 32, 64);
+    const float rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
+    uint16_t* dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
+                            : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {  // dims i .. i + 7 and their partners i + 32 .. i + 39
+      const float4 p0 = x.chunk(c0 + (i >> 2)), p1 = x.chunk(c0 + (i >> 2) + 1);
+      const float4 q0 = x.chunk(c0 + (i >> 2) + 8), q1 = x.chunk(c0 + (i >> 2) + 9);
+      const float f1[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const float f2[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + i);       // dims of x1
+      const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + i);  // dims of x2
+      float v1[8], v2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(ga, e));
+        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(gb, e));
+        const float c = bf16_at_f32(in.c[i >> 3], e), sn = bf16_at_f32(in.sn[i >> 3], e);
+        v1[e] = x1 * c - x2 * sn;
+        v2[e] = x2 * c + x1 * sn;
+      }
+      *reinterpret_cast<uint4*>(dst + i) = make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]),
+                                                      pack_bf16x2(v1[4], v1[5]), pack_bf16x2(v1[6], v1[7]));
+      *reinterpret_cast<uint4*>(dst + i + 32) = make_uint4(pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]),
+                                                           pack_bf16x2(v2[4], v2[5]), pack_bf16x2(v2[6], v2[7]));
+    }
+    return;
+  }
+
+  // K and index_k: the head norm in f64, so the FP8 decisions match the exact
+  // statement of the method
   double ssm[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 2
   for (int i = 0; i < 64; i += 4) {
@@ -472,34 +515,6 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   double ss = (ssm[0] + ssm[1]) + (ssm[2] + ssm[3]);
   ss += __shfl_xor(ss, 32, 64);
   double rr = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
-
-  if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: f32 norm and rotation, bf16 out
-    if (!live) return;
-    uint16_t* dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
-                            : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
-    const float rf = static_cast<float>(rr);
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) {  // the pair (i, i + 32) of the lane's dims
-      const float4 a1 = x.chunk(c0 + (i >> 2));
-      const float4 a2 = x.chunk(c0 + (i >> 2) + 8);
-      const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
-      float v1[4], v2[4];
-      const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + (i & ~7));       // dims of x1
-      const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + (i & ~7));  // dims of x2
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = i + e;  // 0..31
-        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(ga, d & 7));
-        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(gb, d & 7));
-        const float c = bf16_at_f32(in.c[d >> 3], d & 7), sn = bf16_at_f32(in.sn[d >> 3], d & 7);
-        v1[e] = x1 * c - x2 * sn;
-        v2[e] = x2 * c + x1 * sn;
-      }
-      *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
-      *reinterpret_cast<uint2*>(dst + i + 32) = make_uint2(pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]));
-    }
-    return;
-  }
 
   // K and index_k share one copy of the f64 group code: pass kAmax finds the K
   // row's scale, pass kCodes writes E4M3 codes (K with its scale into the
