@@ -35,7 +35,6 @@
 namespace pa {
 namespace {
 
-constexpr int kPreThreads = 256;
 constexpr int kTokAlign = 256;  // token rows of the packed activation (largest CTA tile)
 constexpr int kKStep = 64;      // k per MFMA
 constexpr int kTileBytes = 2048;  // one 32 x 64 FP8 operand tile
@@ -61,95 +60,95 @@ __device__ __forceinline__ size_t xs_offset(int m, int blk, int nks) {
   return (static_cast<size_t>(tt) * nks + ks) * 64 + tl + 32 * kg;
 }
 
-template <int NV>
-__global__ __launch_bounds__(kPreThreads) void prefill_prepass(
+// Norm pass, one CTA per token row, one 16-element chunk per thread (blockDim
+// = hidden / 16 rounded up to a wave; at most 1024 since hidden <= 16384).
+// The chunk's 16 codes are 16 contiguous bytes of the packed layout, written
+// with one store; an MX block is the chunk pair of lanes 2j, 2j + 1.
+__global__ __launch_bounds__(1024) void prefill_prepass(
     const uint16_t* __restrict__ ar, const uint16_t* __restrict__ res,
     uint16_t* __restrict__ h_out, const uint16_t* __restrict__ g_in,
     uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int M, int K, float eps) {
 #pragma clang fp contract(off)
-  __shared__ double red[kPreThreads / 64];
+  __shared__ double red[16];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int nvec = K >> 3;
+  const int nchunks = K >> 4;
   const int nks = K / kKStep;
+  const bool mine = tid < nchunks;  // threads past the row idle (hidden < 1024)
+  const int k = 16 * tid;
   if (row >= M) {  // padding rows of the last token tile: zero codes, unit scales
-    for (int v = tid; v < nvec; v += kPreThreads)
-      *reinterpret_cast<uint2*>(xq + xq_offset(row, 8 * v, nks)) = make_uint2(0u, 0u);
-    for (int b = tid; b < K / 32; b += kPreThreads) xs[xs_offset(row, b, nks)] = 127;
+    if (mine) {
+      *reinterpret_cast<uint4*>(xq + xq_offset(row, k, nks)) = make_uint4(0u, 0u, 0u, 0u);
+      if ((tid & 1) == 0) xs[xs_offset(row, tid >> 1, nks)] = 127;
+    }
     return;
   }
   const size_t base = static_cast<size_t>(row) * K;
-  double xn[NV][8];
-  double ss = 0.0;
+  uint4 av[2], bv[2], gv[2];  // every load in flight before any use
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kPreThreads;
-    if (v < nvec) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ar + base + 8 * v);
-      const uint4 b = *reinterpret_cast<const uint4*>(res + base + 8 * v);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-      uint32_t hw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
-        const float hi = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
-        hw[q] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-        xn[i][2 * q] = lo;
-        xn[i][2 * q + 1] = hi;
-        ss += static_cast<double>(lo) * lo;
-        ss += static_cast<double>(hi) * hi;
-      }
-      *reinterpret_cast<uint4*>(h_out + base + 8 * v) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xn[i][e] = 0.0;
+  for (int i = 0; i < 2; ++i) {
+    av[i] = bv[i] = gv[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (mine) {
+      av[i] = *reinterpret_cast<const uint4*>(ar + base + k + 8 * i);
+      bv[i] = *reinterpret_cast<const uint4*>(res + base + k + 8 * i);
+      gv[i] = *reinterpret_cast<const uint4*>(g_in + k + 8 * i);
     }
   }
-  ss = wave_sum_f64(ss);
-  const int lane = tid & 63, wave = tid >> 6;
+  float acc[16];
+  double ssp[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t aw[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+    const uint32_t bw[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
+    uint32_t hw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
+      const float hi = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
+      hw[q] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+      acc[8 * i + 2 * q] = lo;
+      acc[8 * i + 2 * q + 1] = hi;
+      ssp[q] += static_cast<double>(lo) * lo;
+      ssp[q] += static_cast<double>(hi) * hi;
+    }
+    if (mine) *reinterpret_cast<uint4*>(h_out + base + k + 8 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  }
+  // row sum of squares: DPP wave sums, then the waves' values in a fixed order
+  double ss = wave_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]));
+  const int lane = tid & 63, wave = tid >> 6, nw = static_cast<int>(blockDim.x >> 6);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   double tot = red[0];
-  for (int w = 1; w < kPreThreads / 64; ++w) tot += red[w];
+  for (int w = 1; w < nw; ++w) tot += red[w];
   const double rstd = 1.0 / __builtin_sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
+  double xn[16];
+  double amax = 0.0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kPreThreads;
-    // 8-element vectors 4b..4b+3 form MX block b: four consecutive lanes
-    double amax = 0.0;
-    if (v < nvec) {
-      const uint4 g = *reinterpret_cast<const uint4*>(g_in + 8 * v);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t gb = (e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffffu);
-        xn[i][e] = (xn[i][e] * rstd) * (1.0 + static_cast<double>(bf16_to_f32(gb)));
-        const double m = __builtin_fabs(xn[i][e]);
-        amax = amax > m ? amax : m;
-      }
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t gw = e < 8 ? (e < 4 ? (e < 2 ? gv[0].x : gv[0].y) : (e < 6 ? gv[0].z : gv[0].w))
+                              : (e < 12 ? (e < 10 ? gv[1].x : gv[1].y) : (e < 14 ? gv[1].z : gv[1].w));
+    const uint32_t gb = (e & 1) ? (gw >> 16) : (gw & 0xffffu);
+    xn[e] = (static_cast<double>(acc[e]) * rstd) * (1.0 + static_cast<double>(bf16_to_f32(gb)));
+    const double m = __builtin_fabs(xn[e]);
+    amax = amax > m ? amax : m;
+  }
+  {  // the block's other chunk is on the neighbouring lane
+    const double o = __shfl_xor(amax, 1, 64);
+    amax = amax > o ? amax : o;
+  }
+  if (mine) {
+    // X = 2^(floor(log2 amax) - 8); an all-zero block keeps X = 1
+    int code = 127;
+    if (amax != 0.0) {
+      const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(amax)) >> 52) & 0x7ff) - 1023;
+      code = e - 8 + 127;
+      code = code < 0 ? 0 : (code > 254 ? 254 : code);
     }
-    {
-      const double o1 = __shfl_xor(amax, 1, 64);
-      amax = amax > o1 ? amax : o1;
-      const double o2 = __shfl_xor(amax, 2, 64);
-      amax = amax > o2 ? amax : o2;
-    }
-    if (v < nvec) {
-      // X = 2^(floor(log2 amax) - 8); an all-zero block keeps X = 1
-      int code = 127;
-      if (amax != 0.0) {
-        const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(amax)) >> 52) & 0x7ff) - 1023;
-        code = e - 8 + 127;
-        code = code < 0 ? 0 : (code > 254 ? 254 : code);
-      }
-      const double inv = __longlong_as_double(static_cast<long long>(1023 - (code - 127)) << 52);
-      uint32_t w0 = 0, w1 = 0;
+    const double inv = __longlong_as_double(static_cast<long long>(1023 - (code - 127)) << 52);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w0 |= e4m3_from_f64(xn[i][e] * inv) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w1 |= e4m3_from_f64(xn[i][4 + e] * inv) << (8 * e);
-      *reinterpret_cast<uint2*>(xq + xq_offset(row, 8 * v, nks)) = make_uint2(w0, w1);
-      if ((v & 3) == 0) xs[xs_offset(row, v >> 2, nks)] = static_cast<uint8_t>(code);
-    }
+    for (int e = 0; e < 16; ++e) w[e >> 2] |= e4m3_from_f64(xn[e] * inv) << (8 * (e & 3));
+    *reinterpret_cast<uint4*>(xq + xq_offset(row, k, nks)) = make_uint4(w[0], w[1], w[2], w[3]);
+    if ((tid & 1) == 0) xs[xs_offset(row, tid >> 1, nks)] = static_cast<uint8_t>(code);
   }
 }
 
@@ -718,10 +717,10 @@ __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __res
 }
 
 // bf16 copy of the k, v and index_k heads (one thread per 8 values).
-template <int NV>
 hipError_t launch_prepass(const Args& a, const PrefillPlan& p, int mpad) {
-  hipLaunchKernelGGL(prefill_prepass<NV>, dim3(mpad), dim3(kPreThreads), 0, a.stream, a.ar, a.res,
-                     a.h_out, a.g_in, a.ws + p.off_xq, a.ws + p.off_xs, a.S, a.K, a.eps);
+  const int threads = ((a.K / 16 + 63) / 64) * 64;  // one 16-element chunk a thread
+  hipLaunchKernelGGL(prefill_prepass, dim3(mpad), dim3(threads), 0, a.stream, a.ar, a.res, a.h_out, a.g_in,
+                     a.ws + p.off_xq, a.ws + p.off_xs, a.S, a.K, a.eps);
   return hipGetLastError();
 }
 
@@ -790,19 +789,7 @@ HeadMap make_head_map(int nkv) {
 
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
   const int mpad = (a.S + kTokAlign - 1) / kTokAlign * kTokAlign;
-  const int nv = (a.K / 8 + kPreThreads - 1) / kPreThreads;
-  hipError_t e;
-  switch (nv) {
-    case 1: e = launch_prepass<1>(a, p, mpad); break;
-    case 2: e = launch_prepass<2>(a, p, mpad); break;
-    case 3: e = launch_prepass<3>(a, p, mpad); break;
-    case 4: e = launch_prepass<4>(a, p, mpad); break;
-    case 5: e = launch_prepass<5>(a, p, mpad); break;
-    case 6: e = launch_prepass<6>(a, p, mpad); break;
-    case 7: e = launch_prepass<7>(a, p, mpad); break;
-    case 8: e = launch_prepass<8>(a, p, mpad); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipError_t e = launch_prepass(a, p, mpad);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
