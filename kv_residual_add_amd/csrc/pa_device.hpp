@@ -57,23 +57,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 }
 
 // float64 -> E4M3 code, saturating round-to-nearest-even. Within a binade
-// [2^e, 2^(e+1)) (e >= -6) the codes are spaced 2^(e-3); below 2^-6 the step
-// is 2^-9. Scaling by a power of two is exact, so rint() on the scaled
-// magnitude is the exact RNE and the code is the grid index from zero.
+// [2^e, 2^(e+1)) (e >= -6) the codes are spaced 2^(e-3) and the binade starts
+// at code (e + 7) * 8; below 2^-6 the step is 2^-9, which is the same formula
+// with e clamped to -6. Scaling by a power of two is exact, so rint() on the
+// scaled magnitude is the exact RNE, and a rounding up to 2^(e+1) carries into
+// the next binade's first code. One path for every magnitude: no divergence.
 __device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
-  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint32_t sign = static_cast<uint32_t>(bits >> 56) & 0x80u;
+  const uint32_t sign = (static_cast<uint32_t>(__double2hiint(v)) >> 24) & 0x80u;
   double a = __builtin_fabs(v);
   a = a < kFp8Max ? a : kFp8Max;
-  uint32_t code;
-  if (a < 0x1p-6) {
-    code = static_cast<uint32_t>(__builtin_rint(a * 512.0));
-  } else {
-    const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(a)) >> 52) & 0x7ff) - 1023;
-    const double scale = __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
-    code = static_cast<uint32_t>((e + 6) * 8) + static_cast<uint32_t>(__builtin_rint(a * scale));
-  }
-  return sign | code;
+  int e = static_cast<int>((static_cast<uint32_t>(__double2hiint(a)) >> 20) & 0x7ffu) - 1023;
+  e = e < -6 ? -6 : e;
+  const double scale = __hiloint2double((1023 + 3 - e) << 20, 0);
+  return sign | static_cast<uint32_t>((e + 6) * 8 + static_cast<int>(__builtin_rint(a * scale)));
 }
 
 // E4M3 code of RN64(x / s) (s > 0) without a float64 division. q = x * rcp,
@@ -89,13 +85,9 @@ __device__ __forceinline__ uint32_t e4m3_div(double x, double s, double rcp) {
   double q = x * rcp;
   double a = __builtin_fabs(q);
   a = a < kFp8Max ? a : kFp8Max;
-  double up;  // grid steps per unit value (a power of two)
-  if (a < 0x1p-6) {
-    up = 512.0;
-  } else {
-    const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(a)) >> 52) & 0x7ff) - 1023;
-    up = __longlong_as_double(static_cast<long long>(1023 + 3 - e) << 52);
-  }
+  int e = static_cast<int>((static_cast<uint32_t>(__double2hiint(a)) >> 20) & 0x7ffu) - 1023;
+  e = e < -6 ? -6 : e;
+  const double up = __hiloint2double((1023 + 3 - e) << 20, 0);  // grid steps per unit value
   const double t = a * up;  // position on the code grid (exact)
   const double fl = __builtin_floor(t);
   if (__builtin_fabs((t - fl) - 0.5) < 0x1p-40) {
