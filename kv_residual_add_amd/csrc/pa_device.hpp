@@ -24,6 +24,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Eight E4M3 codes (two dwords, byte order = element order) -> eight bf16 values
 // times `scale` (a power of two). Every E4M3 value, and every such product in
@@ -42,6 +43,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
 template <typename T>
 __device__ __forceinline__ void pin_registers(T& v) {
   asm volatile("" : "+v"(v));
+}
+
+// bf16 element e (0..7) of a 16-byte piece, widened exactly to f32 / f64
+__device__ __forceinline__ float bf16_at_f32(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+__device__ __forceinline__ double bf16_at(const u32x4& v, int e) { return static_cast<double>(bf16_at_f32(v, e)); }
+
+// two floats to bf16 (round to nearest even, NaN quiet; the hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -98,6 +112,49 @@ __device__ __forceinline__ uint32_t e4m3_div(double x, double s, double rcp) {
     q = __builtin_copysign(pick, x);
   }
   return e4m3_from_f64(q);
+}
+
+// E4M3 codes of float64 values times a power of two 2^-s, made by the hardware
+// float32 -> FP8 conversion (v_cvt_pk_fp8_f32: OCP E4M3FN, round to nearest
+// even) from an exact stand-in. Rounding v 2^-s to float32 first and then to
+// E4M3 could round twice; rounding to odd instead (truncate, then set the last
+// bit if anything nonzero was dropped) keeps every value that is not already a
+// float32 strictly between the same two float32 neighbours, and float32 has
+// 20 more significand bits than E4M3, so the E4M3 rounding of the odd result
+// (ties included: an exact tie is exact in float32) is that of v 2^-s.
+// The magnitude is clamped to [2^-11, 448] 2^s first (below 2^-11 everything
+// rounds to a signed zero, above 448 saturates), so the float32 exponent is
+// 116..135 and can be built from the float64 one with 9-bit wrap-around
+// arithmetic: alignbit takes exponent bits 8..0 and the top 23 mantissa bits,
+// and adding (128 - s) << 23 turns exponent e into e - 1023 - s + 127 modulo 512.
+struct Fp8Scale {
+  double lo, hi;   // 2^(s - 11), 448 * 2^s
+  uint32_t bias;   // (128 - s) << 23, modulo 2^32
+};
+
+__device__ __forceinline__ Fp8Scale fp8_scale(int s) {
+  Fp8Scale f;
+  f.lo = __hiloint2double((1023 - 11 + s) << 20, 0);
+  f.hi = 448.0 * __hiloint2double((1023 + s) << 20, 0);
+  f.bias = static_cast<uint32_t>(128 - s) << 23;
+  return f;
+}
+
+__device__ __forceinline__ float f32_odd_scaled(double v, const Fp8Scale& f) {
+  const double a = __builtin_fmin(__builtin_fmax(__builtin_fabs(v), f.lo), f.hi);
+  const uint32_t h = static_cast<uint32_t>(__double2hiint(a)), l = static_cast<uint32_t>(__double2loint(a));
+  uint32_t t = __builtin_amdgcn_alignbit(h, l, 29) + f.bias;  // truncated magnitude
+  uint32_t sticky;  // dropped bits 28..0 nonzero -> 1 (one v_min_u32 on l << 3)
+  asm("v_min_u32_e32 %0, 1, %1" : "=v"(sticky) : "v"(l << 3));
+  t |= sticky | (static_cast<uint32_t>(__double2hiint(v)) & 0x80000000u);
+  return __uint_as_float(t);
+}
+
+// Four E4M3 codes (bytes in element order) of v[0..3] * 2^-s.
+__device__ __forceinline__ uint32_t e4m3x4_scaled(double v0, double v1, double v2, double v3, const Fp8Scale& f) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(f32_odd_scaled(v0, f), f32_odd_scaled(v1, f), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(f32_odd_scaled(v2, f), f32_odd_scaled(v3, f), w, true);
+  return static_cast<uint32_t>(w);
 }
 
 // Wave64 reductions of float64 with DPP row operations (no LDS traffic):

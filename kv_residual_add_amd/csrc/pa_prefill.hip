@@ -27,6 +27,8 @@
 // float64 with contraction off.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "pa_device.hpp"
@@ -38,6 +40,16 @@ namespace {
 constexpr int kTokAlign = 256;  // token rows of the packed activation (largest CTA tile)
 constexpr int kKStep = 64;      // k per MFMA
 constexpr int kTileBytes = 2048;  // one 32 x 64 FP8 operand tile
+
+// Raw, untyped buffer resource (gfx9 descriptor word 3) over `bytes` bytes at
+// `base`. A load whose per-lane offset is at or past the size returns zeros and
+// such a store is dropped (the kernels here rely on that with a zero scalar
+// offset only).
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
 
 // Operand order of the 32x32x64 FP8 MFMA (measured on gfx950): lane l holds
 // row / column l % 32; with h = l / 32 its bytes 0..15 are k = 16h + [0, 16)
@@ -60,95 +72,131 @@ __device__ __forceinline__ size_t xs_offset(int m, int blk, int nks) {
   return (static_cast<size_t>(tt) * nks + ks) * 64 + tl + 32 * kg;
 }
 
-// Norm pass, one CTA per token row, one 16-element chunk per thread (blockDim
-// = hidden / 16 rounded up to a wave; at most 1024 since hidden <= 16384).
-// The chunk's 16 codes are 16 contiguous bytes of the packed layout, written
-// with one store; an MX block is the chunk pair of lanes 2j, 2j + 1.
-__global__ __launch_bounds__(1024) void prefill_prepass(
+// Norm pass. A CTA walks the token rows blockIdx.x, + gridDim.x, ...; a thread
+// owns one 16-element chunk of every row (blockDim = hidden / 16 rounded up to
+// a wave; at most 1024 since hidden <= 16384). The chunk's 16 codes are 16
+// contiguous bytes of the packed layout, written with one store; an MX block is
+// the chunk pair of lanes 2j, 2j + 1. Up to hidden 8192 (WIDE false) a thread
+// keeps its chunk's 1 + g factors in float64 registers for all its rows and
+// issues the next row's loads before working on the current one; above that
+// the register budget of 1024 threads allows neither.
+//
+// Every global access goes through a buffer resource sized to what it may
+// touch: rows past the last token get size 0 (their loads read zeros and their
+// stores vanish), threads past the row and the odd lanes of the scale byte
+// store fall outside by offset. No access is predicated by a branch, so the
+// compiler's wait counts stay exact across the row loop.
+template <bool WIDE>
+__global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
     const uint16_t* __restrict__ ar, const uint16_t* __restrict__ res,
     uint16_t* __restrict__ h_out, const uint16_t* __restrict__ g_in,
-    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int M, int K, float eps) {
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int M, int mpad, int K, float eps) {
 #pragma clang fp contract(off)
-  __shared__ double red[16];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int nchunks = K >> 4;
+  __shared__ double red[2][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = static_cast<int>(blockDim.x >> 6);
   const int nks = K / kKStep;
-  const bool mine = tid < nchunks;  // threads past the row idle (hidden < 1024)
+  const uint32_t row_bytes = 2u * static_cast<uint32_t>(K);
+  const uint32_t voff = 32u * tid;  // at or past row_bytes for threads past the row
+  const auto row_rsrc = [&](const uint16_t* base, int r) {
+    const bool live = r < M;
+    return panel(base + static_cast<size_t>(live ? r : 0) * K, live ? row_bytes : 0u);
+  };
+  const auto gr = panel(g_in, row_bytes);
+  u32x4 gv[2] = {__builtin_amdgcn_raw_buffer_load_b128(gr, voff, 0, 0),
+                 __builtin_amdgcn_raw_buffer_load_b128(gr, voff + 16, 0, 0)};
+  double g1[16];
+  if constexpr (!WIDE) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) g1[e] = 1.0 + bf16_at(gv[e >> 3], e & 7);
+  }
+  // chunk offsets in the packed activation of a token tile (past the tile for
+  // threads past the row; the odd lane of a block pair stores no scale)
   const int k = 16 * tid;
-  if (row >= M) {  // padding rows of the last token tile: zero codes, unit scales
-    if (mine) {
-      *reinterpret_cast<uint4*>(xq + xq_offset(row, k, nks)) = make_uint4(0u, 0u, 0u, 0u);
-      if ((tid & 1) == 0) xs[xs_offset(row, tid >> 1, nks)] = 127;
+  const uint32_t xq_off = static_cast<uint32_t>(xq_offset(0, k, nks));
+  const uint32_t xs_off = (tid & 1) ? 0x7ffffff0u : static_cast<uint32_t>(xs_offset(0, tid >> 1, nks));
+  const uint32_t tile_q = static_cast<uint32_t>(nks) * kTileBytes, tile_s = static_cast<uint32_t>(nks) * 64;
+
+  int row = blockIdx.x;
+  u32x4 av[2], bv[2];
+  const auto load_row = [&](int r, u32x4* x, u32x4* y) {
+    const auto ra = row_rsrc(ar, r), rb = row_rsrc(res, r);
+    x[0] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff, 0, 0);
+    x[1] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff + 16, 0, 0);
+    y[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
+    y[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff + 16, 0, 0);
+  };
+  if constexpr (!WIDE) load_row(row, av, bv);
+  for (int it = 0; row < mpad; ++it) {
+    const int next = row + static_cast<int>(gridDim.x);
+    u32x4 an[2], bn[2];
+    if constexpr (WIDE) {
+      load_row(row, av, bv);
+      asm volatile("" : "+v"(gv[0]), "+v"(gv[1]));  // rebuilt every row, not hoisted
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g1[e] = 1.0 + bf16_at(gv[e >> 3], e & 7);
+    } else {
+      load_row(next, an, bn);
     }
-    return;
-  }
-  const size_t base = static_cast<size_t>(row) * K;
-  uint4 av[2], bv[2], gv[2];  // every load in flight before any use
+    // residual add in float32, bf16 residual out, sum of squares in float64
+    // (a float32 square is exact in float64, so the fma rounds only the sum)
+    double acc[16];  // the float32 sums, widened once
+    double ssp[4] = {0.0, 0.0, 0.0, 0.0};
+    u32x4 hv[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    av[i] = bv[i] = gv[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (mine) {
-      av[i] = *reinterpret_cast<const uint4*>(ar + base + k + 8 * i);
-      bv[i] = *reinterpret_cast<const uint4*>(res + base + k + 8 * i);
-      gv[i] = *reinterpret_cast<const uint4*>(g_in + k + 8 * i);
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bf16_at_f32(av[i], 2 * q) + bf16_at_f32(bv[i], 2 * q);
+        const float hi = bf16_at_f32(av[i], 2 * q + 1) + bf16_at_f32(bv[i], 2 * q + 1);
+        hv[i][q] = pack_bf16x2(lo, hi);
+        const double dl = static_cast<double>(lo), dh = static_cast<double>(hi);
+        acc[8 * i + 2 * q] = dl;
+        acc[8 * i + 2 * q + 1] = dh;
+        ssp[q] = __builtin_fma(dl, dl, ssp[q]);
+        ssp[q] = __builtin_fma(dh, dh, ssp[q]);
+      }
     }
-  }
-  float acc[16];
-  double ssp[4] = {0.0, 0.0, 0.0, 0.0};
+    const auto hr = row_rsrc(h_out, row);
+    __builtin_amdgcn_raw_buffer_store_b128(hv[0], hr, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(hv[1], hr, voff + 16, 0, 0);
+    // row sum: DPP wave sums, then the waves' values in a fixed order; the two
+    // halves of `red` alternate between rows, so one barrier per row suffices
+    const double ss = wave_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]));
+    double* part = red[it & 1];
+    if (lane == 0) part[wave] = ss;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    double tot = part[0];
+    for (int w = 1; w < nw; ++w) tot += part[w];
+    double rstd = 1.0 / __builtin_sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
+    const bool live = row < M;
+    rstd = live ? rstd : 0.0;
+    double xn[16];
+    double amax = 0.0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t aw[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-    const uint32_t bw[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
-    uint32_t hw[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float lo = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
-      const float hi = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
-      hw[q] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-      acc[8 * i + 2 * q] = lo;
-      acc[8 * i + 2 * q + 1] = hi;
-      ssp[q] += static_cast<double>(lo) * lo;
-      ssp[q] += static_cast<double>(hi) * hi;
+    for (int e = 0; e < 16; ++e) {
+      xn[e] = (acc[e] * rstd) * g1[e];
+      amax = __builtin_fmax(amax, __builtin_fabs(xn[e]));
     }
-    if (mine) *reinterpret_cast<uint4*>(h_out + base + k + 8 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-  }
-  // row sum of squares: DPP wave sums, then the waves' values in a fixed order
-  double ss = wave_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]));
-  const int lane = tid & 63, wave = tid >> 6, nw = static_cast<int>(blockDim.x >> 6);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  double tot = red[0];
-  for (int w = 1; w < nw; ++w) tot += red[w];
-  const double rstd = 1.0 / __builtin_sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
-  double xn[16];
-  double amax = 0.0;
+    amax = __builtin_fmax(amax, dpp_f64<0xB1, 0xf>(amax, 0.0));  // the block's other chunk: lane ^ 1
+    // X = 2^(floor(log2 amax) - 8) as an E8M0 code; an all-zero block keeps X = 1
+    int code = static_cast<int>((static_cast<uint32_t>(__double2hiint(amax)) >> 20) & 0x7ffu) - 1023 - 8 + 127;
+    code = code < 0 ? 0 : (code > 254 ? 254 : code);
+    code = amax != 0.0 ? code : 127;
+    const Fp8Scale f = fp8_scale(code - 127);
+    const uint32_t keep = live ? ~0u : 0u;  // a padding row stores zero codes (a mask, not a branch)
+    u32x4 w;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t gw = e < 8 ? (e < 4 ? (e < 2 ? gv[0].x : gv[0].y) : (e < 6 ? gv[0].z : gv[0].w))
-                              : (e < 12 ? (e < 10 ? gv[1].x : gv[1].y) : (e < 14 ? gv[1].z : gv[1].w));
-    const uint32_t gb = (e & 1) ? (gw >> 16) : (gw & 0xffffu);
-    xn[e] = (static_cast<double>(acc[e]) * rstd) * (1.0 + static_cast<double>(bf16_to_f32(gb)));
-    const double m = __builtin_fabs(xn[e]);
-    amax = amax > m ? amax : m;
-  }
-  {  // the block's other chunk is on the neighbouring lane
-    const double o = __shfl_xor(amax, 1, 64);
-    amax = amax > o ? amax : o;
-  }
-  if (mine) {
-    // X = 2^(floor(log2 amax) - 8); an all-zero block keeps X = 1
-    int code = 127;
-    if (amax != 0.0) {
-      const int e = static_cast<int>((static_cast<uint64_t>(__double_as_longlong(amax)) >> 52) & 0x7ff) - 1023;
-      code = e - 8 + 127;
-      code = code < 0 ? 0 : (code > 254 ? 254 : code);
+    for (int j = 0; j < 4; ++j) w[j] = e4m3x4_scaled(xn[4 * j], xn[4 * j + 1], xn[4 * j + 2], xn[4 * j + 3], f) & keep;
+    const size_t tt = static_cast<size_t>(row >> 5);
+    const uint32_t tl = static_cast<uint32_t>(row & 31);
+    __builtin_amdgcn_raw_buffer_store_b128(w, panel(xq + tt * tile_q, tile_q), xq_off + 16u * tl, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), panel(xs + tt * tile_s, tile_s), xs_off + tl, 0, 0);
+    if constexpr (!WIDE) {
+      av[0] = an[0], av[1] = an[1], bv[0] = bn[0], bv[1] = bn[1];
     }
-    const double inv = __longlong_as_double(static_cast<long long>(1023 - (code - 127)) << 52);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) w[e >> 2] |= e4m3_from_f64(xn[e] * inv) << (8 * (e & 3));
-    *reinterpret_cast<uint4*>(xq + xq_offset(row, k, nks)) = make_uint4(w[0], w[1], w[2], w[3]);
-    if ((tid & 1) == 0) xs[xs_offset(row, tid >> 1, nks)] = static_cast<uint8_t>(code);
+    row = next;
   }
 }
 
@@ -197,11 +245,6 @@ struct Stage {
 // head's weight rows, the wave's token tiles): the per-lane offset stays in one
 // vector register for the whole loop and the step's offset is a scalar. A
 // resource also bounds its panel: a read past its size returns zeros.
-constexpr int kBufWord3 = 0x00020000;  // raw, untyped buffer (gfx9 descriptor word 3)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
-}
 
 struct Panels {
   __amdgpu_buffer_rsrc_t a, sa, b, sb;
@@ -380,8 +423,6 @@ struct TileRow {
 // so that their latency overlaps that hand-off: for the lower half of the lanes
 // the 32 cos and 32 sin values of the token. (The head's gamma row is staged
 // in LDS when the CTA starts.)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 struct EpiIn {
   u32x4 c[4];   // cos of rotary index 8j .. + 7
   u32x4 sn[4];  // sin of rotary index 8j .. + 7
@@ -408,19 +449,6 @@ __device__ __forceinline__ const uint16_t* head_gamma(const Args& a, int h) {
   return h < 16 * nkv ? a.g_q : (h < 17 * nkv ? a.g_k : (h < 19 * nkv ? a.g_iq : a.g_ik));
 }
 
-// bf16 element e (0..7) of a 16-byte piece, widened exactly to f32 / f64
-__device__ __forceinline__ float bf16_at_f32(const u32x4& v, int e) {
-  const uint32_t w = v[e >> 1];
-  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-}
-__device__ __forceinline__ double bf16_at(const u32x4& v, int e) { return static_cast<double>(bf16_at_f32(v, e)); }
-
-// two floats to bf16 (round to nearest even; the hardware conversion)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, const uint16_t* gam, int h, int tok,
                                               int64_t slot, const EpiIn& in) {
@@ -716,12 +744,28 @@ __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __res
     sp[hk * 256 + l * 4 + m] = we[static_cast<size_t>(row) * (K / 32) + ks * 2 + (l >> 5)];
 }
 
-// bf16 copy of the k, v and index_k heads (one thread per 8 values).
-hipError_t launch_prepass(const Args& a, const PrefillPlan& p, int mpad) {
+// Norm pass launch: one CTA per resident slot (the CTAs per CU that the
+// kernel's registers allow, times the CUs), each walking the rows at the grid
+// stride, so the next row's loads overlap the current row's work.
+template <bool WIDE>
+hipError_t launch_prepass_t(const Args& a, const PrefillPlan& p, int mpad, int cus) {
   const int threads = ((a.K / 16 + 63) / 64) * 64;  // one 16-element chunk a thread
-  hipLaunchKernelGGL(prefill_prepass, dim3(mpad), dim3(threads), 0, a.stream, a.ar, a.res, a.h_out, a.g_in,
-                     a.ws + p.off_xq, a.ws + p.off_xs, a.S, a.K, a.eps);
+  static std::atomic<int> per_cu_cache[17];         // by waves per CTA
+  int per_cu = per_cu_cache[threads >> 6].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_prepass<WIDE>, threads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    per_cu_cache[threads >> 6].store(per_cu, std::memory_order_relaxed);
+  }
+  const int grid = std::min(mpad, per_cu * cus);
+  hipLaunchKernelGGL(prefill_prepass<WIDE>, dim3(grid), dim3(threads), 0, a.stream, a.ar, a.res, a.h_out, a.g_in,
+                     a.ws + p.off_xq, a.ws + p.off_xs, a.S, mpad, a.K, a.eps);
   return hipGetLastError();
+}
+
+hipError_t launch_prepass(const Args& a, const PrefillPlan& p, int mpad, int cus) {
+  return a.K > 8192 ? launch_prepass_t<true>(a, p, mpad, cus) : launch_prepass_t<false>(a, p, mpad, cus);
 }
 
 }  // namespace
@@ -789,12 +833,12 @@ HeadMap make_head_map(int nkv) {
 
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p) {
   const int mpad = (a.S + kTokAlign - 1) / kTokAlign * kTokAlign;
-  hipError_t e = launch_prepass(a, p, mpad);
-  if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
+  hipError_t e = launch_prepass(a, p, mpad, cus);
+  if (e != hipSuccess) return e;
   const int ntw = prefill_token_tiles_per_wave(a.S, a.heads(), cus);
   const int mtiles = (a.S + 128 * ntw - 1) / (128 * ntw);
   const HeadMap map = make_head_map(a.nkv);

@@ -75,10 +75,83 @@ def test_prefill_parity_small(S, K, nkv, kw):
     _say(f"prefill parity {wl.name} {kw}")
     inp = synth.make_workload(wl, seed=S * 5 + K)
     ref = oracle.prefill(inp)
-    _, got = _gpu(inp)
+    p, got = _gpu(inp)
     stats = parity.compare(inp, ref, got)
     parity.check_written_sets(inp, got)
+    parity.check_activation_codes(p.workspace.cpu().numpy(), ref, S, K)
     _say(f"  {stats}")
+
+
+def _tie_rows(M, K, seed):
+    """Rows whose MXFP8 quantization meets every E4M3 decision exactly.
+
+    With g_in = 0 and eps = 0, a row whose mean square is exactly 1 has
+    rstd = 1, so xn = acc exactly. Each of the first K / 32 - 4 blocks holds
+    1.0 (so amax lies in [1, 2) and the block scale is 2^-8) and 31 values
+    v = q 2^-8 with q from: every E4M3 grid value and every midpoint between
+    neighbours (the ties, subnormal ones included), values past 448 (464 is the
+    saturating tie), and values below half the smallest subnormal. The last
+    four blocks hold bf16 values whose squares bring the row's sum of squares
+    to exactly K; every partial sum of squares is exact in float64, so rstd is
+    exactly 1 in any summation order. Returns float64 values, each exact in
+    bf16, shape [M, K].
+    """
+    from fractions import Fraction
+    grid = [oracle.e4m3_decode(np.array([c], np.uint8))[0] for c in range(127)]
+    qs = list(grid) + [(grid[i] + grid[i + 1]) / 2 for i in range(126)]
+    qs += [464.0, 470.0, 480.0, 500.0, 510.0, 2.0 ** -11, 2.0 ** -12, 3 * 2.0 ** -11]
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    assert nb >= 16, "needs room for the tie set"
+    out = np.zeros((M, K))
+    unit = Fraction(1, 2 ** 20)  # every value here is a multiple of 2^-20
+    for r in range(M):
+        vals = np.array(qs)[rng.permutation(len(qs))] * 2.0 ** -8
+        body = np.zeros((nb - 4) * 32)
+        slots = [i for i in range(len(body)) if i % 32 != 0]
+        n = min(len(slots), len(vals))
+        body[slots[:n]] = vals[:n] * np.where(rng.random(n) < 0.5, -1.0, 1.0)
+        body[::32] = 1.0
+        ss = sum(Fraction(float(v)) ** 2 for v in body)
+        rem = Fraction(K) - ss
+        assert rem > 0
+        fill = []
+        while rem > 0:  # greedy: the largest bf16 value (multiple of 2^-20) whose square fits
+            x = Fraction(int(np.sqrt(float(rem / unit ** 2))), 1) * unit
+            while x * x > rem:
+                x -= unit
+            while (x + unit) ** 2 <= rem:
+                x += unit
+            n = int(x / unit)
+            shift = max(0, n.bit_length() - 8)  # keep 8 significant bits
+            x = Fraction((n >> shift) << shift) * unit
+            fill.append(x)
+            rem -= x * x
+        assert len(fill) <= 128, "filler does not fit"
+        row = np.concatenate([body, np.zeros(128)])
+        row[len(body):len(body) + len(fill)] = [float(x) for x in fill]
+        out[r] = row
+    assert np.all(out.astype(np.float32).view(np.uint32) & 0xFFFF == 0), "value not exact in bf16"
+    return out
+
+
+def test_prefill_activation_codes_every_tie():
+    # exact ties, subnormal midpoints and saturation in the MXFP8 activation
+    # quantization, bit-exact against the oracle; rows span two token tiles
+    M, K = 40, 1024
+    wl = _wl("prefill", M, K, 1, eps=0.0)
+    inp = synth.make_workload(wl, seed=11)
+    vals = _tie_rows(M, K, seed=5)
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    inp["ar"] = bits
+    inp["res"] = np.zeros_like(bits)
+    inp["g_in"] = np.zeros_like(inp["g_in"])
+    xn = oracle.input_norm(bits, inp["res"], inp["g_in"], inp["eps"])[2]
+    assert np.array_equal(xn, vals), "construction: rstd is not exactly 1"
+    ref = oracle.prefill(inp)
+    p, got = _gpu(inp)
+    assert np.array_equal(got["h_out"], ref["h_out"])
+    parity.check_activation_codes(p.workspace.cpu().numpy(), ref, M, K)
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
@@ -92,9 +165,11 @@ def test_degenerate_rows(mode):
     inp["positions"][2] = 63
     inp["slot_mapping"][3] = -1
     ref = oracle.decode(inp) if mode == "decode" else oracle.prefill(inp)
-    _, got = _gpu(inp)
+    p, got = _gpu(inp)
     parity.compare(inp, ref, got)
     parity.check_written_sets(inp, got)
+    if mode == "prefill":
+        parity.check_activation_codes(p.workspace.cpu().numpy(), ref, 6, 256)
     page, t = inp["slot_mapping"][0] // 16, inp["slot_mapping"][0] % 16
     assert got["k_scale"][page, 0, t] == 1.0 and got["v_scale"][page, 0, t] == 1.0
 
@@ -123,6 +198,7 @@ def test_prefill_parity_full_workloads_sampled(key):
     ref = oracle.prefill(parity.subset(inp, rows))
     stats = parity.compare(inp, ref, got, rows=rows)
     parity.check_written_sets(inp, got)
+    parity.check_activation_codes(p.workspace.cpu().numpy(), ref, S, wl.hidden, rows=rows)
     _say(f"  {stats}")
     del p
     torch.cuda.empty_cache()
