@@ -115,9 +115,10 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
     for (int q = 0; q < 4; ++q) {
       acc[i][2 * q] = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
       acc[i][2 * q + 1] = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
-      hw[q] = f32_to_bf16(acc[i][2 * q]) | (f32_to_bf16(acc[i][2 * q + 1]) << 16);
-      ssp[q] += static_cast<double>(acc[i][2 * q]) * acc[i][2 * q];
-      ssp[q] += static_cast<double>(acc[i][2 * q + 1]) * acc[i][2 * q + 1];
+      hw[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+      // a float32 square is exact in float64: the fma rounds only the sum
+      ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q]), static_cast<double>(acc[i][2 * q]), ssp[q]);
+      ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q + 1]), static_cast<double>(acc[i][2 * q + 1]), ssp[q]);
     }
     const int v = tid + i * nthreads;
     if (v < nvec)
@@ -149,11 +150,14 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
   const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
   const double sd = static_cast<double>(s);
   const double rcp = 1.0 / sd;
+  const Fp8Scale unit = fp8_scale(0);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll 1
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_div(xn[i][e], sd, rcp) << (8 * (e & 3));
+    uint32_t w[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      w[j] = e4m3x4_scaled(div_rn(xn[i][4 * j], sd, rcp), div_rn(xn[i][4 * j + 1], sd, rcp),
+                           div_rn(xn[i][4 * j + 2], sd, rcp), div_rn(xn[i][4 * j + 3], sd, rcp), unit);
     const int v = tid + i * nthreads;
     if (v < nvec) *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w[0], w[1]);
   }
@@ -309,8 +313,9 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes;
-      vc[d0 * kPage + t] = static_cast<uint8_t>(e4m3_div(y0, sd, rcp));
-      vc[d1 * kPage + t] = static_cast<uint8_t>(e4m3_div(y1, sd, rcp));
+      const uint32_t c2 = e4m3x2_scaled(div_rn(y0, sd, rcp), div_rn(y1, sd, rcp), fp8_scale(0));
+      vc[d0 * kPage + t] = static_cast<uint8_t>(c2);
+      vc[d1 * kPage + t] = static_cast<uint8_t>(c2 >> 8);
       if (lane == 0) a.v_scale[(page * nkv + j) * kPage + t] = s;
     }
     return;
@@ -341,8 +346,9 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* kc = a.k_cache + (page * nkv + j) * kPageBytes + t * 16;
-      kc[(d0 >> 4) * 256 + (d0 & 15)] = static_cast<uint8_t>(e4m3_div(o0, sd, rcp));
-      kc[(d1 >> 4) * 256 + (d1 & 15)] = static_cast<uint8_t>(e4m3_div(o1, sd, rcp));
+      const uint32_t c2 = e4m3x2_scaled(div_rn(o0, sd, rcp), div_rn(o1, sd, rcp), fp8_scale(0));
+      kc[(d0 >> 4) * 256 + (d0 & 15)] = static_cast<uint8_t>(c2);
+      kc[(d1 >> 4) * 256 + (d1 & 15)] = static_cast<uint8_t>(c2 >> 8);
       if (lane == 0) a.k_scale[(page * nkv + j) * kPage + t] = s;
     }
   } else if (h < ik0) {
@@ -352,8 +358,9 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
     q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
   } else if (store_cache) {  // index_k: unit-scale E4M3 into the slot's row
     uint8_t* ic = a.index_cache + slot * kHeadDim;
-    ic[d0] = static_cast<uint8_t>(e4m3_from_f64(o0));
-    ic[d1] = static_cast<uint8_t>(e4m3_from_f64(o1));
+    const uint32_t c2 = e4m3x2_scaled(o0, o1, fp8_scale(0));
+    ic[d0] = static_cast<uint8_t>(c2);
+    ic[d1] = static_cast<uint8_t>(c2 >> 8);
   }
 }
 

@@ -62,56 +62,10 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// float32 -> bf16 bits, round to nearest even, NaN kept quiet (the hardware
+// conversion, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
-  uint32_t b = __float_as_uint(x);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return ((b >> 16) | 0x40u) & 0xffffu;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return b >> 16;
-}
-
-// float64 -> E4M3 code, saturating round-to-nearest-even. Within a binade
-// [2^e, 2^(e+1)) (e >= -6) the codes are spaced 2^(e-3) and the binade starts
-// at code (e + 7) * 8; below 2^-6 the step is 2^-9, which is the same formula
-// with e clamped to -6. Scaling by a power of two is exact, so rint() on the
-// scaled magnitude is the exact RNE, and a rounding up to 2^(e+1) carries into
-// the next binade's first code. One path for every magnitude: no divergence.
-__device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
-  const uint32_t sign = (static_cast<uint32_t>(__double2hiint(v)) >> 24) & 0x80u;
-  double a = __builtin_fabs(v);
-  a = a < kFp8Max ? a : kFp8Max;
-  int e = static_cast<int>((static_cast<uint32_t>(__double2hiint(a)) >> 20) & 0x7ffu) - 1023;
-  e = e < -6 ? -6 : e;
-  const double scale = __hiloint2double((1023 + 3 - e) << 20, 0);
-  return sign | static_cast<uint32_t>((e + 6) * 8 + static_cast<int>(__builtin_rint(a * scale)));
-}
-
-// E4M3 code of RN64(x / s) (s > 0) without a float64 division. q = x * rcp,
-// rcp = RN64(1 / s), is within 2 ulp of the correctly rounded quotient, so both
-// round to the same code unless q lies within a few ulp of a midpoint m of the
-// code grid. There (tested with a margin of 2^-40 grid steps, far above the
-// 2^-50 bound) the side of m is decided exactly: fma(-m, s, |x|) rounds the
-// exact |x| - m s once, which keeps its sign, so it is positive, negative or
-// zero exactly when |x| / s is above, below or at m. The grid values on either
-// side and m itself are exact doubles; e4m3_from_f64 then rounds the chosen one
-// (a tie at m to the even code).
-__device__ __forceinline__ uint32_t e4m3_div(double x, double s, double rcp) {
-  double q = x * rcp;
-  double a = __builtin_fabs(q);
-  a = a < kFp8Max ? a : kFp8Max;
-  int e = static_cast<int>((static_cast<uint32_t>(__double2hiint(a)) >> 20) & 0x7ffu) - 1023;
-  e = e < -6 ? -6 : e;
-  const double up = __hiloint2double((1023 + 3 - e) << 20, 0);  // grid steps per unit value
-  const double t = a * up;  // position on the code grid (exact)
-  const double fl = __builtin_floor(t);
-  if (__builtin_fabs((t - fl) - 0.5) < 0x1p-40) {
-    const double step = 1.0 / up;  // exact
-    const double m = (fl + 0.5) * step;
-    const double r = __builtin_fma(-m, s, __builtin_fabs(x));
-    const double pick = r > 0.0 ? (fl + 1.0) * step : (r < 0.0 ? fl * step : m);
-    q = __builtin_copysign(pick, x);
-  }
-  return e4m3_from_f64(q);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // E4M3 codes of float64 values times a power of two 2^-s, made by the hardware
@@ -148,6 +102,24 @@ __device__ __forceinline__ float f32_odd_scaled(double v, const Fp8Scale& f) {
   asm("v_min_u32_e32 %0, 1, %1" : "=v"(sticky) : "v"(l << 3));
   t |= sticky | (static_cast<uint32_t>(__double2hiint(v)) & 0x80000000u);
   return __uint_as_float(t);
+}
+
+// Two E4M3 codes (bytes 0 and 1; the upper half is zero) of v0, v1 * 2^-s.
+__device__ __forceinline__ uint32_t e4m3x2_scaled(double v0, double v1, const Fp8Scale& f) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(f32_odd_scaled(v0, f), f32_odd_scaled(v1, f), 0, false));
+}
+
+// RN64(x / s) for s > 0 without a division, given rcp = RN64(1 / s). q = x rcp
+// is within two ulps of x / s; a step q + RN(r rcp) with the remainder
+// r = x - q s (one fma) brings it within an ulp, where r is exact, and from
+// there one more such step gives the correctly rounded quotient (Markstein's
+// theorem; a quotient of two doubles is never halfway between two doubles).
+// The magnitudes here are far from float64 underflow and overflow.
+__device__ __forceinline__ double div_rn(double x, double s, double rcp) {
+  double q = x * rcp;
+  q = __builtin_fma(__builtin_fma(-q, s, x), rcp, q);
+  return __builtin_fma(__builtin_fma(-q, s, x), rcp, q);
 }
 
 // Four E4M3 codes (bytes in element order) of v[0..3] * 2^-s.

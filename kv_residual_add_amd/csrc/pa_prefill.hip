@@ -480,8 +480,15 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
       uint8_t* vc = a.v_cache + (page * nkv + j) * kPageBytes + t + dbase * kPage;
-#pragma unroll 4
-      for (int i = 0; i < 64; ++i) vc[i * kPage] = static_cast<uint8_t>(e4m3_div(static_cast<double>(x.at(dbase + i)), sd, rcp));
+      const Fp8Scale unit = fp8_scale(0);
+#pragma nounroll
+      for (int i = 0; i < 64; i += 4) {
+        const float4 v = x.chunk(c0 + (i >> 2));
+        const uint32_t w = e4m3x4_scaled(div_rn(v.x, sd, rcp), div_rn(v.y, sd, rcp), div_rn(v.z, sd, rcp),
+                                         div_rn(v.w, sd, rcp), unit);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vc[(i + e) * kPage] = static_cast<uint8_t>(w >> (8 * e));
+      }
       if (lane < 32) a.v_scale[(page * nkv + j) * kPage + t] = s;
     }
     return;
@@ -551,7 +558,6 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   uint8_t* cbase = nullptr;
   int cstride = 0;  // bytes between 16-dim groups of the code row
   double sd = 1.0, rcp = 1.0;
-  bool unit = false;
   if (h < v0) {
     mode = kAmax;
     cbase = a.k_cache + (page * nkv + (h - k0)) * kPageBytes + t * 16 + (dbase >> 4) * 256;
@@ -559,7 +565,6 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   } else {
     if (!store_cache) return;
     mode = kCodes;
-    unit = true;
     cbase = a.index_cache + slot * kHeadDim + dbase;
     cstride = 16;
   }
@@ -568,9 +573,9 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
 #pragma unroll
       for (int e = 0; e < 4; ++e) amax = __builtin_fmax(amax, __builtin_fabs(v[e]));
     } else {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w |= (unit ? e4m3_from_f64(v[e]) : e4m3_div(v[e], sd, rcp)) << (8 * e);
+      // index_k keeps sd = rcp = 1, where div_rn returns v unchanged
+      const uint32_t w = e4m3x4_scaled(div_rn(v[0], sd, rcp), div_rn(v[1], sd, rcp), div_rn(v[2], sd, rcp),
+                                       div_rn(v[3], sd, rcp), fp8_scale(0));
       *reinterpret_cast<uint32_t*>(cbase + (i >> 4) * cstride + (i & 15)) = w;
     }
   };
