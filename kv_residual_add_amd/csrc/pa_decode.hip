@@ -39,6 +39,14 @@ namespace {
 
 constexpr int kLdsPad = 16;
 constexpr int kMaxLds = 64 * 1024;
+// one launch for norm + GEMV: up to this many tokens and hidden <= 8192 (the
+// norm at 256 threads then holds at most four 8-element vectors a thread)
+constexpr int kFusedMaxS = 16;
+constexpr int kFusedMaxK = 8192;
+constexpr int kFlagStride = 64;  // words per XCD counter block (256 bytes each)
+constexpr int kSxStride = 64;    // scale floats per XCD copy
+constexpr int kMaxKsplit = 64;   // slice flags per head
+constexpr size_t kFusedEpiMaxWeight = 4u << 20;  // weight bytes up to which whole heads per XCD pay
 
 // Block reductions over up to 16 waves: each wave's result goes to LDS, then
 // every thread combines the waves' values in the same fixed order (pairwise).
@@ -85,7 +93,8 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
 // instruction count, sets the time.
 template <int NV>
 __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __restrict__ x8,
-                                           float* __restrict__ sx, double* red, int tl) {
+                                           float* __restrict__ sx, double* red, int tl, bool write_h = true,
+                                           uint32_t* loaded = nullptr) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -106,26 +115,25 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
   stamp(a.timeline, a.timeline_slots, tl, 0);
   float acc[NV][8];
   double ssp[4] = {0.0, 0.0, 0.0, 0.0};  // four chains, combined pairwise
+  uint32_t hw[NV][4];  // the bf16 residual, stored with the codes at the end
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const uint32_t aw[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
     const uint32_t bw[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
-    uint32_t hw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[i][2 * q] = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
       acc[i][2 * q + 1] = bf16_to_f32(aw[q] >> 16) + bf16_to_f32(bw[q] >> 16);
-      hw[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+      hw[i][q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
       // a float32 square is exact in float64: the fma rounds only the sum
       ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q]), static_cast<double>(acc[i][2 * q]), ssp[q]);
       ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q + 1]), static_cast<double>(acc[i][2 * q + 1]), ssp[q]);
     }
-    const int v = tid + i * nthreads;
-    if (v < nvec)
-      *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   }
   stamp(a.timeline, a.timeline_slots, tl, 1);
   const double ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
+  // every wave is past its loads: a waiting GEMV may start its weight stream
+  if (loaded != nullptr && tid == 0) __hip_atomic_fetch_add(loaded, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   stamp(a.timeline, a.timeline_slots, tl, 2);
   const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(a.eps));
   double xn[NV][8];
@@ -160,6 +168,8 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
                            div_rn(xn[i][4 * j + 2], sd, rcp), div_rn(xn[i][4 * j + 3], sd, rcp), unit);
     const int v = tid + i * nthreads;
     if (v < nvec) *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w[0], w[1]);
+    if (v < nvec && write_h)
+      *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[i][0], hw[i][1], hw[i][2], hw[i][3]);
   }
   if (tid == 0) sx[row] = s;
   stamp(a.timeline, a.timeline_slots, tl, 5);
@@ -173,32 +183,65 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
 // k = 128c + 16j + 8 (l / 32) + [0, 8). The activation B operand takes the same
 // k from LDS, so the dot product needs no shuffles. Tokens past S reuse token
 // S-1 and are never stored. NT = 32-token tiles (1 or 2).
-template <int CPC, int NT>
-__global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
+// The x8 rows a GEMV CTA reads, published inside one launch: word t of an
+// XCD's flag block is set once that XCD's copy of token t is in its L2.
+struct Publish {
+  const uint32_t* flags;  // this XCD's S flags (nullptr: rows come from an earlier launch)
+  uint32_t* err;          // set if a wait gave up
+};
+
+constexpr int kSpinMax = 1 << 18;  // polls before a wait gives up (well under a second)
+
+// Waits until flags 0 .. n - 1 (n <= 64) are set: lane t polls flag t with an
+// agent-scope atomic load (not served by the CU's L1; it reads the XCD's L2,
+// where the setters' plain stores land). The wait is bounded: on giving up it
+// records the failure and returns, so every wave finishes.
+__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int t = lane < n ? lane : 0;
+  for (int it = 0;; ++it) {
+    const uint32_t f =
+        __hip_atomic_load(const_cast<uint32_t*>(flags) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_ballot_w64(lane < n && f == 0u) == 0ull) break;
+    if (it == kSpinMax) {
+      if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  asm volatile("" ::: "memory");  // the loads after the wait stay after it
+}
+
+// One GEMV CTA: head h, k chunks [ks * CPC, + CPC). With a Publish, the
+// weight stream goes out first and the activation rows are read once the
+// XCD's norm CTAs have published them (sc0 loads, from the XCD's L2).
+template <int CPC, int NT, bool FUSED>
+__device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
+                                          const Publish& pub) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, ks = blockIdx.y;
   const int S = a.S, K = a.K, N = a.N();
   const int nchk = K >> 7;
   constexpr int ldw = CPC * 128 + kLdsPad;
-  const uint8_t* x8 = a.ws + off_x8;
-  float* part = reinterpret_cast<float*>(a.ws + off_part);
-  const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   stamp(a.timeline, a.timeline_slots, tlb, 0);
 
-  // the activation slice first (small, L2), then the weight stream: the LDS
-  // stores below wait only for the former
   const int per_row = CPC * 8;  // 16-byte pieces per token row
   constexpr int kMaxPieces = 64 * CPC * 8 / 256;
   i32x4 xv[kMaxPieces];
+  const auto load_rows = [&]() {
+    const auto xr = panel(x8, static_cast<size_t>(S) * K);
 #pragma unroll
-  for (int r = 0; r < kMaxPieces; ++r) {
-    const int i = tid + r * 256;
-    if (i < S * per_row) {
+    for (int r = 0; r < kMaxPieces; ++r) {
+      const int i = tid + r * 256;
       const int s = i / per_row, j = i - s * per_row;
-      xv[r] = *reinterpret_cast<const i32x4*>(x8 + static_cast<size_t>(s) * K + ks * CPC * 128 + j * 16);
+      // past the S rows the offset is past the panel: the load reads zeros
+      const uint32_t off = i < S * per_row ? static_cast<uint32_t>(s * K + ks * CPC * 128 + j * 16) : 0x7ffffff0u;
+      xv[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, FUSED ? 1 : 0);
     }
-  }
+  };
+  // without a publisher the activation slice goes first (small, L2): the LDS
+  // stores below then wait only for it
+  if constexpr (!FUSED) load_rows();
   i32x4 wv[CPC][4];
   const uint8_t* wb = a.w_packed + ((static_cast<size_t>(h) * nchk + ks * CPC) * 4 + wave) * 4096 + lane * 16;
 #pragma unroll
@@ -206,6 +249,10 @@ __global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
+  if constexpr (FUSED) {
+    wait_flags(pub.flags, S, pub.err);
+    load_rows();
+  }
 #pragma unroll
   for (int r = 0; r < kMaxPieces; ++r) {
     const int i = tid + r * 256;
@@ -256,52 +303,83 @@ __global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t
   stamp(a.timeline, a.timeline_slots, tlb, 1);
 }
 
+template <int CPC, int NT>
+__global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
+  const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
+  gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
+                     Publish{nullptr, nullptr});
+}
+
 // ---------------------------------------------------------------------------
 // epilogue of head h for token tok, one wave. Lane l holds dims l and l + 64;
 // the RoPE partner of dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
-__global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, size_t off_sx,
-                                                     int ksplit) {
+// A partial sum written in this launch by another CTA of the same XCD: an
+// agent-scope load, which the CU's L1 does not serve.
+template <bool COHERENT>
+__device__ __forceinline__ float load_partial(const float* p) {
+  if constexpr (COHERENT)
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+  else
+    return *p;
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, const float* __restrict__ part,
+                                              const float* __restrict__ sx, int ksplit, int tlb) {
 #pragma clang fp contract(off)
-  const int H = a.heads();
-  const int h = blockIdx.x % H, tok = blockIdx.x / H;
-  const float* __restrict__ part = reinterpret_cast<const float*>(a.ws + off_part);
-  const float* __restrict__ sx = reinterpret_cast<const float*>(a.ws + off_sx);
   const int N = a.N();
   const int lane = threadIdx.x & 63;
   const int nkv = a.nkv;
   const int S = a.S;
   const int d0 = lane, d1 = lane + 64;
   const int n0 = h * kHeadDim + d0, n1 = h * kHeadDim + d1;
-  const int tlb = S + H * ksplit + blockIdx.x;  // timeline slot
   stamp(a.timeline, a.timeline_slots, tlb, 0);
 
-  // the slice partials, eight slices' loads in flight at a time, summed in
-  // slice order
+  // Everything the epilogue reads goes out before anything waits: the token's
+  // position first (cos / sin depend on it), then the slice partials (sixteen
+  // slices in flight at a time, summed in slice order), the scales, the slot
+  // and the gamma pair.
+  int64_t pos = a.positions[tok];
   double y0 = 0.0, y1 = 0.0;
   const size_t stride = static_cast<size_t>(S) * N;
   const float* p = part + static_cast<size_t>(tok) * N;
-  for (int k8 = 0; k8 < ksplit; k8 += 8) {
-    float v0[8], v1[8];
+  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
+  const uint16_t* g = h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik));
+  float sxf = 0.f, ws0 = 0.f, ws1 = 0.f;
+  int64_t slot = 0;
+  uint16_t g0 = 0, g1 = 0, cs0 = 0, cs1 = 0;
+  for (int k16 = 0; k16 < ksplit; k16 += 16) {
+    float v0f[16], v1f[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // clamped indices: every load is unconditional
-      const size_t ks = static_cast<size_t>(min(k8 + u, ksplit - 1));
-      v0[u] = p[ks * stride + n0];
-      v1[u] = p[ks * stride + n1];
+    for (int u = 0; u < 16; ++u) {  // clamped indices: every load is unconditional
+      const size_t ks = static_cast<size_t>(min(k16 + u, ksplit - 1));
+      v0f[u] = load_partial<COHERENT>(p + ks * stride + n0);
+      v1f[u] = load_partial<COHERENT>(p + ks * stride + n1);
+    }
+    if (k16 == 0) {
+      sxf = load_partial<COHERENT>(sx + tok);
+      ws0 = a.w_scale[n0];
+      ws1 = a.w_scale[n1];
+      slot = a.slot_mapping[tok];
+      g0 = g[d0];
+      g1 = g[d1];
+      pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
+      cs0 = a.cos_sin[pos * kRotary + (lane & 31)];
+      cs1 = a.cos_sin[pos * kRotary + 32 + (lane & 31)];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool in = k8 + u < ksplit;
-      y0 += in ? static_cast<double>(v0[u]) : 0.0;
-      y1 += in ? static_cast<double>(v1[u]) : 0.0;
+    for (int u = 0; u < 16; ++u) {
+      const bool in = k16 + u < ksplit;
+      y0 += in ? static_cast<double>(v0f[u]) : 0.0;
+      y1 += in ? static_cast<double>(v1f[u]) : 0.0;
     }
   }
   stamp(a.timeline, a.timeline_slots, tlb, 1);
-  const double sxv = static_cast<double>(sx[tok]);
-  y0 = (y0 * sxv) * static_cast<double>(a.w_scale[n0]);
-  y1 = (y1 * sxv) * static_cast<double>(a.w_scale[n1]);
+  const double sxv = static_cast<double>(sxf);
+  y0 = (y0 * sxv) * static_cast<double>(ws0);
+  y1 = (y1 * sxv) * static_cast<double>(ws1);
 
-  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
-  const int64_t slot = a.slot_mapping[tok];
   const bool store_cache = slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
@@ -321,16 +399,12 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
     return;
   }
 
-  const uint16_t* g = h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik));
   const double ss = wave_sum_f64(y0 * y0 + y1 * y1);
   const double r = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
-  const double nm0 = (y0 * r) * (1.0 + static_cast<double>(bf16_to_f32(g[d0])));
-  const double nm1 = (y1 * r) * (1.0 + static_cast<double>(bf16_to_f32(g[d1])));
-  int64_t pos = a.positions[tok];
-  pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
-  const int i = lane & 31;
-  const double c = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + i]));
-  const double sn = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + 32 + i]));
+  const double nm0 = (y0 * r) * (1.0 + static_cast<double>(bf16_to_f32(g0)));
+  const double nm1 = (y1 * r) * (1.0 + static_cast<double>(bf16_to_f32(g1)));
+  const double c = static_cast<double>(bf16_to_f32(cs0));
+  const double sn = static_cast<double>(bf16_to_f32(cs1));
   const double partner = __shfl_xor(nm0, 32, 64);
   const double o0 = lane < 32 ? nm0 * c - partner * sn : nm0 * c + partner * sn;
   const double o1 = nm1;
@@ -362,6 +436,90 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
     ic[d0] = static_cast<uint8_t>(c2);
     ic[d1] = static_cast<uint8_t>(c2 >> 8);
   }
+}
+
+__global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, size_t off_sx, int ksplit) {
+  const int H = a.heads();
+  head_epilogue<false>(a, blockIdx.x % H, blockIdx.x / H, reinterpret_cast<const float*>(a.ws + off_part),
+                       reinterpret_cast<const float*>(a.ws + off_sx), ksplit, a.S + H * ksplit + blockIdx.x);
+}
+
+// A GEMV CTA of XCD x is done with the XCD's rows: the last of the XCD's gx
+// GEMV CTAs (counted with a device-scope atomic) clears the row flags.
+__device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int x, int gx, uint32_t* flags) {
+  uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
+  if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(gx - 1)) {
+    for (int t = 0; t < a.S; ++t) flags[t] = 0u;
+    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The decode step in one or two launches for a few tokens.
+//  - Blocks b < 8 S are norm CTAs: token b / 8 for the XCD b % 8. Workgroups
+//    go to the XCDs round-robin, so blocks with equal b % 8 share an XCD and
+//    its L2 (with fewer XCDs the same holds for b % 4 or b % 2). Each XCD thus
+//    computes its own copy of every token's FP8 row and flags it in its L2.
+//  - The GEMV CTAs follow. They stream their weights at once, wait for their
+//    XCD's flags, take the rows from their own L2 and store partial sums.
+//  - With EPI, head h runs all its k slices on XCD h % 8, and the head's last
+//    slice (the last of its CTAs in block order) waits for the other slices'
+//    flags, sums the partials (all in its L2) and runs the head's epilogue for
+//    every token. Whole heads per XCD can load some XCDs with more weight
+//    than others, so without EPI the slices spread evenly and the epilogue is
+//    the next launch.
+// No cache write-back or invalidate is needed and nothing crosses XCDs. The
+// norm CTAs come first in block order, so they are placed before any CTA that
+// waits for them, and the only wait is bounded. The last GEMV CTA of an XCD
+// clears the XCD's row flags, a head's epilogue CTA the slice flags, for the
+// next call.
+template <int CPC, int NV, bool EPI>
+__global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
+  __shared__ double red[16];
+  const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + p.off_flag) + x * kFlagStride;
+  uint8_t* x8 = a.ws + p.off_x8 + static_cast<size_t>(x) * S * a.K;
+  float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
+  if (b < 8 * S) {
+    const int tok = b >> 3;
+    norm_token<NV>(a, tok, x8, sx, red, x == 0 ? tok : -1, x == 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's row stores have reached the L2
+    __syncthreads();
+    if (threadIdx.x == 0) flags[tok] = 1u;
+    return;
+  }
+  int h, ks;
+  if constexpr (EPI) {
+    const int j = (b - 8 * S) >> 3;  // this block's index among its XCD's GEMV blocks
+    h = x + 8 * (j / ksplit);
+    ks = j % ksplit;
+    if (h >= H) return;  // XCDs with fewer heads have idle blocks
+  } else {  // the slices spread evenly over the XCDs; the epilogue is a launch of its own
+    const int g = b - 8 * S;
+    h = g % H;
+    ks = g / H;
+  }
+  float* part = reinterpret_cast<float*>(a.ws + p.off_part);
+  gemv_tile<CPC, 1, true>(a, h, ks, x8, part, S + ks * H + h,
+                          Publish{flags, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
+  if constexpr (!EPI) {
+    if (threadIdx.x == 0) xcd_done(a, p, x, (H * ksplit - x + 7) / 8, flags);
+    return;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
+  __syncthreads();
+  uint32_t* hflags = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;
+  if (ks < ksplit - 1) {  // publish the slice to the head's epilogue CTA
+    if (threadIdx.x == 0) hflags[ks] = 1u;
+  } else {
+    // the head's epilogue CTA: dispatched after every other slice of the head
+    if (threadIdx.x < 64) wait_flags(hflags, ksplit - 1, reinterpret_cast<uint32_t*>(a.ws + p.off_err));
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    for (int tok = wave; tok < S; tok += 4)
+      head_epilogue<true>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
+    if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
+  }
+  if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,6 +570,27 @@ hipError_t launch_gemv_nt(const Args& a, const DecodePlan& p) {
   return a.S <= 32 ? launch_gemv<CPC, 1>(a, p) : launch_gemv<CPC, 2>(a, p);
 }
 
+template <int CPC, bool EPI>
+hipError_t launch_fused_e(const Args& a, const DecodePlan& p) {
+  const int nv = (a.K / 8 + 255) / 256;  // 8-element vectors a norm thread holds
+  const int gemv = EPI ? 8 * ((a.heads() + 7) / 8) * p.ksplit : a.heads() * p.ksplit;
+  const dim3 grid(8 * a.S + gemv);
+  const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
+  switch (nv) {
+    case 1: hipLaunchKernelGGL((decode_fused<CPC, 1, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 2: hipLaunchKernelGGL((decode_fused<CPC, 2, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 3: hipLaunchKernelGGL((decode_fused<CPC, 3, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 4: hipLaunchKernelGGL((decode_fused<CPC, 4, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int CPC>
+hipError_t launch_fused(const Args& a, const DecodePlan& p) {
+  return p.fused_epilogue ? launch_fused_e<CPC, true>(a, p) : launch_fused_e<CPC, false>(a, p);
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int S, int K, int nkv) {
@@ -436,19 +615,49 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   }
   p.chunks_per_cta = pick;
   p.ksplit = pick ? nchk / pick : 0;
+  p.fused = pick > 0 && S <= kFusedMaxS && K <= kFusedMaxK;
+  // the head's epilogue in the same launch: heads then sit whole on XCDs, which
+  // is balanced when they divide evenly, and cheap when the weight is small
+  p.fused_epilogue = p.fused && p.ksplit <= kMaxKsplit &&
+                     (heads % 8 == 0 || static_cast<size_t>(N) * K <= kFusedEpiMaxWeight);
+  const size_t copies = p.fused ? 8 : 1;  // FP8 rows and scales: one copy per XCD when fused
   size_t off = 0;
   p.off_x8 = off;
-  off = align_up(off + static_cast<size_t>(S) * K, 256);
+  off = align_up(off + copies * S * K, 256);
   p.off_sx = off;
-  off = align_up(off + sizeof(float) * S, 256);
+  off = align_up(off + sizeof(float) * (p.fused ? 8 * kSxStride : S), 256);
   p.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.ksplit) * S * N, 256);
-  p.off_cnt = off;
+  p.off_flag = off;
+  off += p.fused ? 8 * kFlagStride * sizeof(uint32_t) : 0;
+  p.off_done = off;
+  off += p.fused ? 8 * 128 : 0;
+  p.off_hdone = off;
+  off += p.fused ? static_cast<size_t>(heads) * kMaxKsplit * sizeof(uint32_t) : 0;  // slice flags per head
+  p.off_err = off;
+  off += p.fused ? 256 : 0;
   p.total = off;
   return p;
 }
 
 hipError_t launch_decode(const Args& a, const DecodePlan& p) {
+  hipError_t e;
+  if (p.fused) {
+    if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
+    switch (p.chunks_per_cta) {
+      case 1: e = launch_fused<1>(a, p); break;
+      case 2: e = launch_fused<2>(a, p); break;
+      case 3: e = launch_fused<3>(a, p); break;
+      case 4: e = launch_fused<4>(a, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
+    if (p.fused_epilogue) return hipSuccess;
+    hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part,
+                       p.off_sx, p.ksplit);
+    return hipGetLastError();
+  }
   // norm: one thread per 8-element vector up to 1024 threads, then loop
   const int vecs = a.K / 8;
   const int threads = vecs >= 1024 ? 1024 : (vecs + 63) / 64 * 64;
@@ -459,7 +668,7 @@ hipError_t launch_decode(const Args& a, const DecodePlan& p) {
     hipLaunchKernelGGL((decode_norm<2>), dim3(a.S), dim3(threads), 0, a.stream, a, p.off_x8, p.off_sx);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
   switch (p.chunks_per_cta) {

@@ -26,6 +26,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Raw, untyped buffer resource (gfx9 descriptor word 3) over `bytes` bytes at
+// `base`. A load whose per-lane offset is at or past the size returns zeros and
+// such a store is dropped (the kernels here rely on that with a zero scalar
+// offset only).
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+
 // Eight E4M3 codes (two dwords, byte order = element order) -> eight bf16 values
 // times `scale` (a power of two). Every E4M3 value, and every such product in
 // bf16's normal range, is a bf16 value, so the widening is exact.

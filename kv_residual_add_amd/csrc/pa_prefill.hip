@@ -41,15 +41,6 @@ constexpr int kTokAlign = 256;  // token rows of the packed activation (largest 
 constexpr int kKStep = 64;      // k per MFMA
 constexpr int kTileBytes = 2048;  // one 32 x 64 FP8 operand tile
 
-// Raw, untyped buffer resource (gfx9 descriptor word 3) over `bytes` bytes at
-// `base`. A load whose per-lane offset is at or past the size returns zeros and
-// such a store is dropped (the kernels here rely on that with a zero scalar
-// offset only).
-constexpr int kBufWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
-}
 
 // Operand order of the 32x32x64 FP8 MFMA (measured on gfx950): lane l holds
 // row / column l % 32; with h = l / 32 its bytes 0..15 are k = 16h + [0, 16)

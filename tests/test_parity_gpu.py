@@ -204,17 +204,29 @@ def test_prefill_parity_full_workloads_sampled(key):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", ["decode", "prefill"])
-def test_repeat_calls_bit_identical(mode):
-    wl = _wl(mode, 24, 1024, 2)
+# decode shapes for each launch structure: few tokens with a small weight (norm,
+# GEMV and head epilogue in one launch, flags handed over in each XCD's L2), few
+# tokens with a larger weight (norm + GEMV in one launch, epilogue in a second),
+# and more tokens (three launches). Repeated calls must reuse the in-launch
+# flags cleanly.
+REPEAT_CASES = [("decode", 4, 256, 1), ("decode", 8, 1024, 2), ("decode", 24, 1024, 2), ("prefill", 24, 1024, 2)]
+
+
+@pytest.mark.parametrize("mode,S,K,nkv", REPEAT_CASES, ids=lambda v: str(v))
+def test_repeat_calls_bit_identical(mode, S, K, nkv):
+    wl = _wl(mode, S, K, nkv)
+    _say(f"repeat {wl.name}")
     inp = synth.make_workload(wl, seed=9)
+    ref = oracle.decode(inp) if mode == "decode" else oracle.prefill(inp)
     p, first = _gpu(inp)
-    for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
-        p.t[k].copy_(torch.from_numpy(inp[k]).to(p.device))
-    p.run()
-    second = p.outputs()
-    for k in first:
-        assert np.array_equal(first[k].view(np.uint8), second[k].view(np.uint8)), k
+    parity.compare(inp, ref, first)
+    for _ in range(3):
+        for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
+            p.t[k].copy_(torch.from_numpy(inp[k]).to(p.device))
+        p.run()
+        again = p.outputs()
+        for k in first:
+            assert np.array_equal(first[k].view(np.uint8), again[k].view(np.uint8)), k
 
 
 def test_positions_out_of_range_are_clamped():
