@@ -61,18 +61,28 @@ def calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 10}))
 
 
-def algorithmic(wl):
-    """(bytes per call, bytes of the dominant kernel per launch, flops per call)."""
+def algorithmic(wl, launches=3):
+    """(bytes per call, bytes of the dominant kernel per launch, flops per call,
+    the dominant kernel's name).
+
+    Decode runs in 3, 2 or 1 launches (pa_decode_launches): the dominant kernel
+    is the GEMV (FP8 weight + FP8 activation codes), the norm + GEMV launch
+    (weight, the ar / res rows and gamma in, the bf16 residual out) or the
+    whole call."""
     S, K, nkv = wl.tokens, wl.hidden, wl.nkv
     N = (19 * nkv + 1) * 128
     call_bytes = (N * K + 4 * N + 4 * S * K + 2 * S * K + 2 * K + 4 * 256
                   + S * 16 * nkv * 256 + S * nkv * 256 + S * nkv * (256 + 8) + 128 * S
                   + 128 * S + 16 * S)
+    flops = 2 * S * N * K
     if wl.mode == "prefill":
         call_bytes += N * K // 32 - 4 * N  # E8M0 block scales instead of row scales
-    kernel_bytes = N * K + S * K  # FP8 weight + FP8 activation codes
-    flops = 2 * S * N * K
-    return call_bytes, kernel_bytes, flops
+        return call_bytes, N * K + S * K, flops, "prefill_gemm"
+    if launches == 1:
+        return call_bytes, call_bytes, flops, "decode_fused (norm + GEMV + head epilogue)"
+    if launches == 2:
+        return call_bytes, N * K + 4 * S * K + 2 * K + 2 * S * K, flops, "decode_fused (norm + GEMV)"
+    return call_bytes, N * K + S * K, flops, "decode_gemv"
 
 
 def source_sha(mode: str) -> str:
@@ -155,7 +165,8 @@ def main():
     dev = prob.device
     S, K = wl.tokens, wl.hidden
     N = prob.N
-    call_bytes, kernel_bytes, flops = algorithmic(wl)
+    launches = B.pa_decode_launches(prob.dims) if prob.mode == B.PA_MODE_DECODE else 0
+    call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, launches)
 
     # rotating pool of distinct weight + activation sets
     set_bytes = prob.w_packed.numel() + prob.w_scales.numel() * prob.w_scales.element_size() \
@@ -244,7 +255,7 @@ def main():
         achieved = kernel_bytes / (kern_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "decode_gemv", "kernel_ms": round(kern_ms, 5),
+                "kernel": kernel_name, "kernel_ms": round(kern_ms, 5),
                 "algorithmic_bytes_per_launch": kernel_bytes}
         extra = {"step_hbm_gbs": round(call_bytes * args.steps / elapsed / 1e9, 1),
                  "step_hbm_frac": round(call_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 4),
@@ -255,7 +266,7 @@ def main():
         achieved = flops / (kern_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "prefill_gemm", "kernel_ms": round(kern_ms, 5),
+                "traffic": traffic, "kernel": kernel_name, "kernel_ms": round(kern_ms, 5),
                 "algorithmic_flops_per_launch": flops}
         extra = {"step_tflops_frac": round(value / FP8_PEAK_TFLOPS, 4),
                  "tokens_per_s": round(S * args.steps / elapsed, 1)}

@@ -110,6 +110,13 @@ typedef struct pa_dims {
  * call whose requirement it meets, once pa_workspace_init has run on it. */
 size_t pa_workspace_bytes(const pa_dims* dims, int mode);
 
+/* How pre_attn_decode runs a call with these dims on the device, for
+ * reporting and tests (the outputs do not depend on it). 1: one launch (the
+ * input norm, the projection and the head epilogue); 2: the input norm with the
+ * projection, then the head epilogue; 3: norm, projection and epilogue
+ * launches. 0 on bad dims. */
+int pa_decode_launches(const pa_dims* dims);
+
 /* Prepares a freshly allocated workspace of `bytes` bytes for use (clears the
  * library's counters with a fill kernel on `stream`). Needed once per
  * allocation; calls leave it ready for the next call. */

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     pa_packed_scale_bytes,
     pa_packed_weight_bytes,
     pa_workspace_bytes,
+    pa_decode_launches,
     pa_workspace_init,
     pre_attn_decode,
     pre_attn_prefill,

@@ -25,6 +25,7 @@ DECODE_MAX_TOKENS = 64
 
 EXPORTS = (
     "pa_workspace_bytes",
+    "pa_decode_launches",
     "pa_workspace_init",
     "pa_packed_weight_bytes",
     "pa_packed_scale_bytes",
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
         dims_p = ctypes.POINTER(pa_dims)
         lib.pa_workspace_bytes.argtypes = [dims_p, ctypes.c_int]
         lib.pa_workspace_bytes.restype = sz
+        lib.pa_decode_launches.argtypes = [dims_p]
+        lib.pa_decode_launches.restype = ctypes.c_int
         lib.pa_workspace_init.argtypes = [P, sz, P]
         lib.pa_workspace_init.restype = ctypes.c_int
         lib.pa_packed_weight_bytes.argtypes = [ctypes.c_int, i32, i32]
@@ -157,6 +160,10 @@ def pa_set_timeline(buffer) -> None:
 
 def pa_workspace_bytes(dims: pa_dims, mode: int) -> int:
     return load().pa_workspace_bytes(ctypes.byref(dims), mode)
+
+
+def pa_decode_launches(dims: pa_dims) -> int:
+    return load().pa_decode_launches(ctypes.byref(dims))
 
 
 def pa_workspace_init(workspace: torch.Tensor, stream=None) -> None:

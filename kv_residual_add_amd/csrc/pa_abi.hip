@@ -172,6 +172,13 @@ size_t pa_workspace_bytes(const pa_dims* dims, int mode) {
   return workspace_for(dims, mode);
 }
 
+int pa_decode_launches(const pa_dims* d) {
+  if (check_dims(d, PA_MODE_DECODE) != PA_OK) return 0;
+  const pa::DecodePlan p = pa::decode_plan(d->tokens, d->hidden, d->nkv);
+  if (p.chunks_per_cta == 0) return 0;
+  return p.fused ? (p.fused_epilogue ? 1 : 2) : 3;
+}
+
 int pa_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return PA_ERR_NULL;
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;

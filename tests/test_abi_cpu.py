@@ -51,6 +51,21 @@ def test_workspace_sizes():
     assert K.pa_workspace_bytes(_dims(), 7) == 0
 
 
+def test_decode_launch_structure():
+    # few tokens with a small weight: one launch; few tokens with a larger
+    # weight whose heads do not divide over the 8 XCDs: two; more tokens: three
+    assert K.pa_decode_launches(_dims(tokens=1, hidden=1024)) == 1
+    assert K.pa_decode_launches(_dims(tokens=8)) == 2
+    assert K.pa_decode_launches(_dims(tokens=16, hidden=8192)) == 2
+    assert K.pa_decode_launches(_dims(tokens=17)) == 3
+    assert K.pa_decode_launches(_dims(tokens=64, nkv=2)) == 3
+    assert K.pa_decode_launches(_dims(tokens=8, hidden=8320)) == 3  # hidden past the fused norm's reach
+    assert K.pa_decode_launches(_dims(tokens=65)) == 0
+    assert K.pa_decode_launches(_dims(nkv=3)) == 0
+    # the fused structures keep a copy of the FP8 rows per XCD
+    assert K.pa_workspace_bytes(_dims(tokens=8), K.PA_MODE_DECODE) >= 8 * 8 * 6144
+
+
 def test_packed_sizes():
     assert K.pa_packed_weight_bytes(0, 2560, 6144) == 2560 * 6144
     # FP8 codes of every row + bf16 copies of the k, v and index_k heads
