@@ -486,7 +486,8 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   }
 
   if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: f32 norm and rotation, bf16 out
-    if (!live) return;  // both lanes of a token return together
+    // Every lane computes (rows past the last token too: their rows are not
+    // stored), so the whole wave takes part in the row stores at the end.
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 64; i += 4) {
@@ -499,8 +500,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
     float ssf = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     ssf += __shfl_xor(ssf, 32, 64);
     const float rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
-    uint16_t* dst = (h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
-                            : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim) + dbase;
+    u32x4 o1[4], o2[4];  // bf16 dims i .. i + 7 and i + 32 .. i + 39 for i = 0, 8, 16, 24
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {  // dims i .. i + 7 and their partners i + 32 .. i + 39
       const float4 p0 = x.chunk(c0 + (i >> 2)), p1 = x.chunk(c0 + (i >> 2) + 1);
@@ -518,10 +518,32 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
         v1[e] = x1 * c - x2 * sn;
         v2[e] = x2 * c + x1 * sn;
       }
-      *reinterpret_cast<uint4*>(dst + i) = make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]),
-                                                      pack_bf16x2(v1[4], v1[5]), pack_bf16x2(v1[6], v1[7]));
-      *reinterpret_cast<uint4*>(dst + i + 32) = make_uint4(pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]),
-                                                           pack_bf16x2(v2[4], v2[5]), pack_bf16x2(v2[6], v2[7]));
+      o1[i >> 3] = u32x4{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
+                         pack_bf16x2(v1[6], v1[7])};
+      o2[i >> 3] = u32x4{pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]), pack_bf16x2(v2[4], v2[5]),
+                         pack_bf16x2(v2[6], v2[7])};
+    }
+    // The wave's reads of its tile are done (one instruction stream, LDS in
+    // order): the token's bf16 row goes into the first 256 bytes of its f32 row,
+    // then the wave stores whole rows, 16 lanes (256 contiguous bytes) a row
+    // and 4 rows an instruction, instead of 64 scattered 16-byte pieces.
+    uint8_t* rowb = reinterpret_cast<uint8_t*>(const_cast<float*>(x.row));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(rowb + 2 * (dbase + 8 * j)) = o1[j];
+      *reinterpret_cast<u32x4*>(rowb + 2 * (dbase + 32 + 8 * j)) = o2[j];
+    }
+    const uint8_t* tileb = rowb - x.r * kHeadDim * 4;
+    const int tok0 = tok - x.r;  // the tile's first token
+    const int piece = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = (lane >> 4) + 4 * k;
+      const int t = tok0 + rr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tileb + rr * kHeadDim * 4 + 16 * piece);
+      uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(t) * k0 + h) * kHeadDim
+                             : a.iq_out + (static_cast<size_t>(t) * nkv + (h - iq0)) * kHeadDim;
+      if (t < a.S) *reinterpret_cast<u32x4*>(dst + 8 * piece) = v;
     }
     return;
   }
