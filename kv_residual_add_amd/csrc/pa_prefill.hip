@@ -210,9 +210,11 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 // four waves share the head's weight tile of each 64-wide k step, which the
 // buffer unit writes straight into a four-slot LDS ring (no registers on the
 // way), while each wave keeps its own activation tiles and the scales in one of
-// four register sets. A step's loads are issued kPrefetch steps ahead of its
+// four register sets. A stage (SUB k steps: two in one-tile CTAs, whose
+// registers allow it, one otherwise) is issued kPrefetch stages ahead of its
 // MFMAs, so L2 and Infinity Cache latency (up to about a microsecond when a
-// load misses) overlaps that many steps of MFMA work.
+// load misses) overlaps that many stages of MFMA work; the barrier and the
+// wait come once a stage.
 //
 // Per step: weight 8 KB (4 row tiles x 2 KB) + one scale dword per lane;
 // activations per token tile 2 KB + one scale byte per lane. FP8 heads feed
@@ -224,12 +226,15 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
 constexpr int kPrefetch = 3;
 constexpr int kSlots = kPrefetch + 1;
 constexpr int kSlotBytes = 16384;  // a weight step uses 8 KB; a slot also holds one wave's 32 x 128 f32 output tile
+constexpr int kSubSingle = 2;      // k steps per stage in one-tile CTAs
 
-template <bool PRECISE, int NTW>
+// A stage is SUB consecutive k steps: their weight tiles share one ring slot
+// (8 KB each) and their register loads one set.
+template <bool PRECISE, int NTW, int SUB>
 struct Stage {
-  uint32_t sa;       // weight scale dword (row tiles in bytes 0..3) for block lane / 32
-  i32x4 b[NTW][2];   // activation bytes 0..15 and 16..31 of the lane
-  uint32_t sb[NTW];  // the lane's activation scale (its token, block lane / 32)
+  uint32_t sa[SUB];       // weight scale dword (row tiles in bytes 0..3) for block lane / 32
+  i32x4 b[SUB][NTW][2];   // activation bytes 0..15 and 16..31 of the lane
+  uint32_t sb[SUB][NTW];  // the lane's activation scale (its token, block lane / 32)
 };
 
 // Loads of one k step go through buffer resources, one per operand panel (the
@@ -241,7 +246,7 @@ struct Panels {
   __amdgpu_buffer_rsrc_t a, sa, b, sb;
 };
 
-template <bool PRECISE, int NTW>
+template <int NTW>
 __device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
   const size_t nks = a.K / kKStep;
   Panels p;
@@ -252,10 +257,10 @@ __device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, con
   return p;
 }
 
-// Vector-memory instructions one step issues per wave (the waits count them).
-template <bool PRECISE, int NTW>
+// Vector-memory instructions one stage issues per wave (the waits count them).
+template <int NTW, int SUB>
 constexpr int step_vm_ops() {
-  return 2 + 1 + 2 * NTW + NTW;
+  return SUB * (2 + 1 + 2 * NTW + NTW);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory instructions of
@@ -263,41 +268,50 @@ constexpr int step_vm_ops() {
 // export and LDS/scalar counters left at their no-wait maxima)
 constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Issues step ks: the register loads first, then the weight tile's LDS writes.
-template <bool PRECISE, int NTW>
-__device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW>& st, const Panels& p, int nks, int ks,
+// Issues stage st (k steps SUB st ..): the register loads first, then the
+// weight tiles' LDS writes.
+template <bool PRECISE, int NTW, int SUB>
+__device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW, SUB>& st, const Panels& p, int nks, int stage,
                                             uint8_t* slot, int wave) {
   const int tid = threadIdx.x, lane = tid & 63;
-  st.sa = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
 #pragma unroll
-  for (int n = 0; n < NTW; ++n) {
-    const int blk = n * nks + ks;
-    st.b[n][0] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes, 0);
-    st.b[n][1] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes + 1024, 0);
-    st.sb[n] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
+  for (int u = 0; u < SUB; ++u) {
+    const int ks = stage * SUB + u;
+    st.sa[u] = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+      const int blk = n * nks + ks;
+      st.b[u][n][0] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes, 0);
+      st.b[u][n][1] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes + 1024, 0);
+      st.sb[u][n] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
+    }
   }
-  // weight tile: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16,
-  // which land at the same offset of the slot (16 bytes per lane)
+  // weight tiles: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16
+  // of step u's tile, which land at the same offset of the slot's half u
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        p.a, (__attribute__((address_space(3))) void*)(slot + q * 4096 + wave * 1024), 16, tid * 16,
-        ks * 4 * kTileBytes + q * 4096, 0, 0);
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          p.a, (__attribute__((address_space(3))) void*)(slot + u * 8192 + q * 4096 + wave * 1024), 16, tid * 16,
+          (stage * SUB + u) * 4 * kTileBytes + q * 4096, 0, 0);
 }
 
+// The MFMAs of one k step: weight scale dword sa0, activation fragments b0 and
+// scales sb0, the weight tile at `slot`.
 template <bool PRECISE, int NTW>
-__device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const uint8_t* slot,
-                                           f32x16 (&acc)[NTW][4]) {
+__device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2], const uint32_t (&sb0)[NTW],
+                                          const uint8_t* slot, f32x16 (&acc)[NTW][4]) {
   const int lane = threadIdx.x & 63;
   if (PRECISE) {
     // bf16 MFMA step j takes bytes 8j .. 8j + 7 of each lane's 32-byte fragment
     // (k = 32 (j / 2) + 16 (lane / 32) + 8 (j % 2) + [0, 8)), widened exactly
     // with the block scale; bytes 0..15 are MX block 0 and 16..31 block 1, and
     // the lane ^ 32 partner holds the scales of the other block.
-    const uint32_t sa_x = __shfl_xor(st.sa, 32, 64);
+    const uint32_t sa_x = __shfl_xor(sa0, 32, 64);
     uint32_t sb_x[NTW];
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) sb_x[n] = __shfl_xor(st.sb[n], 32, 64);
+    for (int n = 0; n < NTW; ++n) sb_x[n] = __shfl_xor(sb0[n], 32, 64);
     const bool low = lane < 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -305,10 +319,10 @@ __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const 
       bf16x8 B[NTW];
 #pragma unroll
       for (int n = 0; n < NTW; ++n) {
-        const i32x4& src = st.b[n][j >> 1];
-        B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], e8m0_to_f32((own ? st.sb[n] : sb_x[n]) & 0xffu));
+        const i32x4& src = b0[n][j >> 1];
+        B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], e8m0_to_f32((own ? sb0[n] : sb_x[n]) & 0xffu));
       }
-      const uint32_t sw = own ? st.sa : sa_x;
+      const uint32_t sw = own ? sa0 : sa_x;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint2 af = *reinterpret_cast<const uint2*>(slot + m * kTileBytes + (j >> 1) * 1024 + lane * 16 + (j & 1) * 8);
@@ -325,47 +339,55 @@ __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW>& st, const 
       const i32x8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
       for (int n = 0; n < NTW; ++n) {
-        const i32x8 B = {st.b[n][0][0], st.b[n][0][1], st.b[n][0][2], st.b[n][0][3],
-                         st.b[n][1][0], st.b[n][1][1], st.b[n][1][2], st.b[n][1][3]};
+        const i32x8 B = {b0[n][0][0], b0[n][0][1], b0[n][0][2], b0[n][0][3],
+                         b0[n][1][0], b0[n][1][1], b0[n][1][2], b0[n][1][3]};
         switch (m) {  // the scale byte of row tile m (op_sel is an immediate)
-          case 0: acc[n][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][0], 0, 0, 0, st.sa, 0, st.sb[n]); break;
-          case 1: acc[n][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][1], 0, 0, 1, st.sa, 0, st.sb[n]); break;
-          case 2: acc[n][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][2], 0, 0, 2, st.sa, 0, st.sb[n]); break;
-          default: acc[n][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][3], 0, 0, 3, st.sa, 0, st.sb[n]); break;
+          case 0: acc[n][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][0], 0, 0, 0, sa0, 0, sb0[n]); break;
+          case 1: acc[n][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][1], 0, 0, 1, sa0, 0, sb0[n]); break;
+          case 2: acc[n][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][2], 0, 0, 2, sa0, 0, sb0[n]); break;
+          default: acc[n][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[n][3], 0, 0, 3, sa0, 0, sb0[n]); break;
         }
       }
     }
   }
 }
 
-// One step of the pipeline: wait until this wave's loads of step s have landed
-// (the two later steps' loads may still fly), barrier so every wave's part of
-// the weight tile is in LDS and every wave is done with step s - 1, then issue
-// step s + kPrefetch into the slot and register set step s - 1 used, and run
-// step s. The scheduling barriers keep each step's loads in issue order, which
-// the wait count relies on.
-template <bool PRECISE, int NTW, int I>
-__device__ __forceinline__ void pipeline_step(Stage<PRECISE, NTW> (&st)[kSlots], uint8_t* const (&ring)[kSlots],
+template <bool PRECISE, int NTW, int SUB>
+__device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW, SUB>& st, const uint8_t* slot,
+                                           f32x16 (&acc)[NTW][4]) {
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) step_mfma<PRECISE, NTW>(st.sa[u], st.b[u], st.sb[u], slot + u * 8192, acc);
+}
+
+// One stage of the pipeline: wait until this wave's loads of stage s have
+// landed (the two later stages' loads may still fly), barrier so every wave's
+// part of the weight tiles is in LDS and every wave is done with stage s - 1,
+// then issue stage s + kPrefetch into the slot and register set stage s - 1
+// used, and run stage s. The scheduling barriers keep each stage's loads in
+// issue order, which the wait count relies on.
+template <bool PRECISE, int NTW, int SUB, int I>
+__device__ __forceinline__ void pipeline_step(Stage<PRECISE, NTW, SUB> (&st)[kSlots], uint8_t* const (&ring)[kSlots],
                                               const Panels& p, int nks, int s, int wave, f32x16 (&acc)[NTW][4]) {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kPrefetch - 1) * step_vm_ops<PRECISE, NTW>()));
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kPrefetch - 1) * step_vm_ops<NTW, SUB>()));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  const int last = nks - 1;
+  const int last = nks / SUB - 1;
   const int ahead = s + kPrefetch < last ? s + kPrefetch : last;  // clamped; extra steps are never used
   stage_issue(st[(I + kPrefetch) % kSlots], p, nks, ahead, ring[(I + kPrefetch) % kSlots], wave);
   __builtin_amdgcn_sched_barrier(0);
   stage_mfma(st[I], ring[I], acc);
 }
 
-template <bool PRECISE, int NTW>
+template <bool PRECISE, int NTW, int SUB>
 __device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const uint8_t* __restrict__ xq,
                                          const uint8_t* __restrict__ xs, uint8_t* const (&ring)[kSlots], int wave,
                                          f32x16 (&acc)[NTW][4]) {
   const int nks = a.K / kKStep;
-  const int last = nks - 1;
-  const Panels p = make_panels<PRECISE, NTW>(a, h, tt0, xq, xs);
-  Stage<PRECISE, NTW> st[kSlots];
+  const int nst = nks / SUB;  // stages (hidden is a multiple of 128: nks is even)
+  const int last = nst - 1;
+  const Panels p = make_panels<NTW>(a, h, tt0, xq, xs);
+  Stage<PRECISE, NTW, SUB> st[kSlots];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
     stage_issue(st[i], p, nks, i < last ? i : last, ring[i], wave);
@@ -374,15 +396,15 @@ __device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const ui
   // Whole groups of kSlots steps keep ring slot and register set indices
   // static; the tail covers nks % kSlots steps.
   int s0 = 0;
-  for (; s0 + kSlots <= nks; s0 += kSlots) {
-    pipeline_step<PRECISE, NTW, 0>(st, ring, p, nks, s0 + 0, wave, acc);
-    pipeline_step<PRECISE, NTW, 1>(st, ring, p, nks, s0 + 1, wave, acc);
-    pipeline_step<PRECISE, NTW, 2>(st, ring, p, nks, s0 + 2, wave, acc);
-    pipeline_step<PRECISE, NTW, 3>(st, ring, p, nks, s0 + 3, wave, acc);
+  for (; s0 + kSlots <= nst; s0 += kSlots) {
+    pipeline_step<PRECISE, NTW, SUB, 0>(st, ring, p, nks, s0 + 0, wave, acc);
+    pipeline_step<PRECISE, NTW, SUB, 1>(st, ring, p, nks, s0 + 1, wave, acc);
+    pipeline_step<PRECISE, NTW, SUB, 2>(st, ring, p, nks, s0 + 2, wave, acc);
+    pipeline_step<PRECISE, NTW, SUB, 3>(st, ring, p, nks, s0 + 3, wave, acc);
   }
-  if (s0 + 0 < nks) pipeline_step<PRECISE, NTW, 0>(st, ring, p, nks, s0 + 0, wave, acc);
-  if (s0 + 1 < nks) pipeline_step<PRECISE, NTW, 1>(st, ring, p, nks, s0 + 1, wave, acc);
-  if (s0 + 2 < nks) pipeline_step<PRECISE, NTW, 2>(st, ring, p, nks, s0 + 2, wave, acc);
+  if (s0 + 0 < nst) pipeline_step<PRECISE, NTW, SUB, 0>(st, ring, p, nks, s0 + 0, wave, acc);
+  if (s0 + 1 < nst) pipeline_step<PRECISE, NTW, SUB, 1>(st, ring, p, nks, s0 + 1, wave, acc);
+  if (s0 + 2 < nst) pipeline_step<PRECISE, NTW, SUB, 2>(st, ring, p, nks, s0 + 2, wave, acc);
   static_assert(kSlots == 4, "the group above is written out for four slots");
   // every load (including the clamped extra steps) has landed and every wave
   // is past its last LDS read before the ring is reused
@@ -703,10 +725,12 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[n][m][r] = 0.f;
+  // one-tile CTAs have the registers for two k steps a stage: twice the lookahead
+  constexpr int SUB = NTW == 1 ? kSubSingle : 1;
   if (precise_head(h, a.nkv))
-    mainloop<true, NTW>(a, h, tt0, xq, xs, ring, wave, acc);
+    mainloop<true, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
   else
-    mainloop<false, NTW>(a, h, tt0, xq, xs, ring, wave, acc);
+    mainloop<false, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
 #pragma unroll
   for (int n = 0; n < NTW; ++n)
 #pragma unroll
