@@ -91,10 +91,12 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
 // t owns the 8-element vectors t, t + blockDim.x, ... (NV of them). The element
 // loops stay rolled: each wave runs this code once, so its size, not its
 // instruction count, sets the time.
-template <int NV>
+// With CODES false the row's FP8 codes are left to the GEMV CTAs (codes8), and
+// rstd goes to rstd_out[row] beside the scale.
+template <int NV, bool CODES = true>
 __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __restrict__ x8,
                                            float* __restrict__ sx, double* red, int tl, bool write_h = true,
-                                           uint32_t* loaded = nullptr) {
+                                           double* rstd_out = nullptr) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -132,8 +134,6 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
   }
   stamp(a.timeline, a.timeline_slots, tl, 1);
   const double ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
-  // every wave is past its loads: a waiting GEMV may start its weight stream
-  if (loaded != nullptr && tid == 0) __hip_atomic_fetch_add(loaded, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   stamp(a.timeline, a.timeline_slots, tl, 2);
   const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(a.eps));
   double xn[NV][8];
@@ -167,12 +167,34 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
       w[j] = e4m3x4_scaled(div_rn(xn[i][4 * j], sd, rcp), div_rn(xn[i][4 * j + 1], sd, rcp),
                            div_rn(xn[i][4 * j + 2], sd, rcp), div_rn(xn[i][4 * j + 3], sd, rcp), unit);
     const int v = tid + i * nthreads;
-    if (v < nvec) *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w[0], w[1]);
+    if (CODES && v < nvec) *reinterpret_cast<uint2*>(x8 + base + 8 * v) = make_uint2(w[0], w[1]);
     if (v < nvec && write_h)
       *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[i][0], hw[i][1], hw[i][2], hw[i][3]);
   }
-  if (tid == 0) sx[row] = s;
+  if (tid == 0) {
+    sx[row] = s;
+    if (rstd_out != nullptr) rstd_out[row] = rstd;
+  }
   stamp(a.timeline, a.timeline_slots, tl, 5);
+}
+
+// The FP8 codes of eight consecutive row elements from their 16-byte pieces of
+// ar, res and g_in, given the row's rstd and scale: the norm's own expressions,
+// so the codes are the ones norm_token would store.
+__device__ __forceinline__ uint2 codes8(const u32x4& av, const u32x4& bv, const u32x4& gv, double rstd, double sd,
+                                        double rcp) {
+#pragma clang fp contract(off)
+  double xn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float acc = bf16_at_f32(av, e) + bf16_at_f32(bv, e);
+    xn[e] = (static_cast<double>(acc) * rstd) * (1.0 + static_cast<double>(bf16_at_f32(gv, e)));
+  }
+  const Fp8Scale unit = fp8_scale(0);
+  return make_uint2(e4m3x4_scaled(div_rn(xn[0], sd, rcp), div_rn(xn[1], sd, rcp), div_rn(xn[2], sd, rcp),
+                                  div_rn(xn[3], sd, rcp), unit),
+                    e4m3x4_scaled(div_rn(xn[4], sd, rcp), div_rn(xn[5], sd, rcp), div_rn(xn[6], sd, rcp),
+                                  div_rn(xn[7], sd, rcp), unit));
 }
 
 // ---------------------------------------------------------------------------
@@ -187,6 +209,8 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
 // XCD's flag block is set once that XCD's copy of token t is in its L2.
 struct Publish {
   const uint32_t* flags;  // this XCD's S flags (nullptr: rows come from an earlier launch)
+  const double* rstd;     // this XCD's per-token rstd ...
+  const float* sx;        // ... and FP8 scale
   uint32_t* err;          // set if a wait gave up
 };
 
@@ -212,9 +236,10 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_
   asm volatile("" ::: "memory");  // the loads after the wait stay after it
 }
 
-// One GEMV CTA: head h, k chunks [ks * CPC, + CPC). With a Publish, the
-// weight stream goes out first and the activation rows are read once the
-// XCD's norm CTAs have published them (sc0 loads, from the XCD's L2).
+// One GEMV CTA: head h, k chunks [ks * CPC, + CPC). With a Publish (FUSED),
+// the weight stream and the CTA's slice of ar, res and g_in go out first;
+// once the XCD's norm CTAs have published each token's rstd and scale, the CTA
+// forms its slice's FP8 codes itself (codes8) straight into LDS.
 template <int CPC, int NT, bool FUSED>
 __device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
                                           const Publish& pub) {
@@ -236,12 +261,29 @@ __device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const ui
       const int s = i / per_row, j = i - s * per_row;
       // past the S rows the offset is past the panel: the load reads zeros
       const uint32_t off = i < S * per_row ? static_cast<uint32_t>(s * K + ks * CPC * 128 + j * 16) : 0x7ffffff0u;
-      xv[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, FUSED ? 1 : 0);
+      xv[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
     }
   };
   // without a publisher the activation slice goes first (small, L2): the LDS
   // stores below then wait only for it
   if constexpr (!FUSED) load_rows();
+  // with one, the raw slice: 8-element groups i = tid + 256 r, token i / (16 CPC)
+  constexpr int kGroups = CPC;  // per thread: at most 16 tokens x 16 CPC groups over 256 threads
+  u32x4 ga[FUSED ? kGroups : 1], gb[FUSED ? kGroups : 1], gg[FUSED ? kGroups : 1];
+  if constexpr (FUSED) {
+    const auto pa = panel(a.ar, static_cast<size_t>(S) * K * 2), pr = panel(a.res, static_cast<size_t>(S) * K * 2);
+    const auto pg = panel(a.g_in, static_cast<size_t>(K) * 2);
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+      const int i = tid + 256 * r;
+      const int s = i / (16 * CPC), j = i - s * 16 * CPC;
+      const bool in = i < S * 16 * CPC;
+      const uint32_t k = static_cast<uint32_t>(ks * CPC * 128 + j * 8);
+      ga[r] = __builtin_amdgcn_raw_buffer_load_b128(pa, in ? 2u * (s * K + k) : 0x7ffffff0u, 0, 0);
+      gb[r] = __builtin_amdgcn_raw_buffer_load_b128(pr, in ? 2u * (s * K + k) : 0x7ffffff0u, 0, 0);
+      gg[r] = __builtin_amdgcn_raw_buffer_load_b128(pg, in ? 2u * k : 0x7ffffff0u, 0, 0);
+    }
+  }
   i32x4 wv[CPC][4];
   const uint8_t* wb = a.w_packed + ((static_cast<size_t>(h) * nchk + ks * CPC) * 4 + wave) * 4096 + lane * 16;
 #pragma unroll
@@ -251,14 +293,26 @@ __device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const ui
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
   if constexpr (FUSED) {
     wait_flags(pub.flags, S, pub.err);
-    load_rows();
-  }
 #pragma unroll
-  for (int r = 0; r < kMaxPieces; ++r) {
-    const int i = tid + r * 256;
-    if (i < S * per_row) {
-      const int s = i / per_row, j = i - s * per_row;
-      *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = xv[r];
+    for (int r = 0; r < kGroups; ++r) {
+      const int i = tid + 256 * r;
+      if (i < S * 16 * CPC) {
+        const int s = i / (16 * CPC), j = i - s * 16 * CPC;
+        const double rstd = __longlong_as_double(static_cast<long long>(__hip_atomic_load(
+            reinterpret_cast<uint64_t*>(const_cast<double*>(pub.rstd)) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+        const double sd = static_cast<double>(__uint_as_float(__hip_atomic_load(
+            reinterpret_cast<uint32_t*>(const_cast<float*>(pub.sx)) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+        *reinterpret_cast<uint2*>(lds + s * ldw + j * 8) = codes8(ga[r], gb[r], gg[r], rstd, sd, 1.0 / sd);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kMaxPieces; ++r) {
+      const int i = tid + r * 256;
+      if (i < S * per_row) {
+        const int s = i / per_row, j = i - s * per_row;
+        *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = xv[r];
+      }
     }
   }
   __syncthreads();
@@ -307,7 +361,7 @@ template <int CPC, int NT>
 __global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
   const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
-                     Publish{nullptr, nullptr});
+                     Publish{nullptr, nullptr, nullptr, nullptr});
 }
 
 // ---------------------------------------------------------------------------
@@ -477,11 +531,11 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
   __shared__ double red[16];
   const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + p.off_flag) + x * kFlagStride;
-  uint8_t* x8 = a.ws + p.off_x8 + static_cast<size_t>(x) * S * a.K;
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
+  double* rstd = reinterpret_cast<double*>(a.ws + p.off_rstd) + x * kSxStride;
   if (b < 8 * S) {
     const int tok = b >> 3;
-    norm_token<NV>(a, tok, x8, sx, red, x == 0 ? tok : -1, x == 0);
+    norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, rstd);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's row stores have reached the L2
     __syncthreads();
     if (threadIdx.x == 0) flags[tok] = 1u;
@@ -499,8 +553,8 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
     ks = g / H;
   }
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
-  gemv_tile<CPC, 1, true>(a, h, ks, x8, part, S + ks * H + h,
-                          Publish{flags, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
+  gemv_tile<CPC, 1, true>(a, h, ks, nullptr, part, S + ks * H + h,
+                          Publish{flags, rstd, sx, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
   if constexpr (!EPI) {
     if (threadIdx.x == 0) xcd_done(a, p, x, (H * ksplit - x + 7) / 8, flags);
     return;
@@ -620,12 +674,13 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   // is balanced when they divide evenly, and cheap when the weight is small
   p.fused_epilogue = p.fused && p.ksplit <= kMaxKsplit &&
                      (heads % 8 == 0 || static_cast<size_t>(N) * K <= kFusedEpiMaxWeight);
-  const size_t copies = p.fused ? 8 : 1;  // FP8 rows and scales: one copy per XCD when fused
   size_t off = 0;
-  p.off_x8 = off;
-  off = align_up(off + copies * S * K, 256);
-  p.off_sx = off;
+  p.off_x8 = off;  // the FP8 rows (the three-launch path)
+  off = align_up(off + (p.fused ? 0 : static_cast<size_t>(S) * K), 256);
+  p.off_sx = off;  // per-token scales: one copy per XCD when fused, with rstd
   off = align_up(off + sizeof(float) * (p.fused ? 8 * kSxStride : S), 256);
+  p.off_rstd = off;
+  off += p.fused ? sizeof(double) * 8 * kSxStride : 0;
   p.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.ksplit) * S * N, 256);
   p.off_flag = off;
