@@ -43,7 +43,6 @@ constexpr int kMaxLds = 64 * 1024;
 // norm at 256 threads then holds at most four 8-element vectors a thread)
 constexpr int kFusedMaxS = 16;
 constexpr int kFusedMaxK = 8192;
-constexpr int kFlagStride = 64;  // words per XCD counter block (256 bytes each)
 constexpr int kSxStride = 64;    // scale floats per XCD copy
 constexpr int kMaxKsplit = 64;   // slice flags per head
 constexpr size_t kFusedEpiMaxWeight = 4u << 20;  // weight bytes up to which whole heads per XCD pay
@@ -91,12 +90,13 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
 // t owns the 8-element vectors t, t + blockDim.x, ... (NV of them). The element
 // loops stay rolled: each wave runs this code once, so its size, not its
 // instruction count, sets the time.
-// With CODES false the row's FP8 codes are left to the GEMV CTAs (codes8), and
-// rstd goes to rstd_out[row] beside the scale.
+// With CODES false the row's FP8 codes are left to the GEMV CTAs (codes8),
+// which take the row's rstd and scale from *rstd_out and *s_out (every thread
+// receives them).
 template <int NV, bool CODES = true>
 __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __restrict__ x8,
                                            float* __restrict__ sx, double* red, int tl, bool write_h = true,
-                                           double* rstd_out = nullptr) {
+                                           double* rstd_out = nullptr, float* s_out = nullptr) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -171,10 +171,9 @@ __device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __re
     if (v < nvec && write_h)
       *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[i][0], hw[i][1], hw[i][2], hw[i][3]);
   }
-  if (tid == 0) {
-    sx[row] = s;
-    if (rstd_out != nullptr) rstd_out[row] = rstd;
-  }
+  if (tid == 0) sx[row] = s;
+  if (rstd_out != nullptr) *rstd_out = rstd;
+  if (s_out != nullptr) *s_out = s;
   stamp(a.timeline, a.timeline_slots, tl, 5);
 }
 
@@ -205,16 +204,42 @@ __device__ __forceinline__ uint2 codes8(const u32x4& av, const u32x4& bv, const 
 // k = 128c + 16j + 8 (l / 32) + [0, 8). The activation B operand takes the same
 // k from LDS, so the dot product needs no shuffles. Tokens past S reuse token
 // S-1 and are never stored. NT = 32-token tiles (1 or 2).
-// The x8 rows a GEMV CTA reads, published inside one launch: word t of an
-// XCD's flag block is set once that XCD's copy of token t is in its L2.
+// What a GEMV CTA of the single-launch decode takes from the norm CTAs of its
+// XCD: each token's rstd and FP8 scale, published in the XCD's L2.
+constexpr int kSpinMax = 1 << 18;  // polls before a wait gives up (well under a second)
+
 struct Publish {
-  const uint32_t* flags;  // this XCD's S flags (nullptr: rows come from an earlier launch)
-  const double* rstd;     // this XCD's per-token rstd ...
-  const float* sx;        // ... and FP8 scale
-  uint32_t* err;          // set if a wait gave up
+  const uint64_t* rstd;  // this XCD's per-token rstd bits (0: not yet; a real rstd is > 0)
+  const uint64_t* srec;  // this XCD's per-token scale bits, tagged 1 in the upper half (0: not yet)
+  uint32_t* err;         // set if a wait gave up
 };
 
-constexpr int kSpinMax = 1 << 18;  // polls before a wait gives up (well under a second)
+// Waits until the XCD's S tokens are published and returns this lane's token's
+// rstd and scale (lanes t < S; the others get token 0's). Each value is one
+// naturally aligned 8-byte word written once per call, and it carries its own
+// readiness, so no flag and no store order is needed; a lane polls its token's
+// two words with agent-scope loads (not served by the CU's L1; they read the
+// XCD's L2, where the norm CTAs' plain stores land). Bounded like wait_flags.
+__device__ __forceinline__ void wait_stats(const Publish& pub, int S, double& rstd, float& sc) {
+  const int lane = threadIdx.x & 63;
+  const int t = lane < S ? lane : 0;
+  uint64_t r = 0, c = 0;
+  for (int it = 0;; ++it) {
+    r = __hip_atomic_load(const_cast<uint64_t*>(pub.rstd) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c = __hip_atomic_load(const_cast<uint64_t*>(pub.srec) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool ready = r != 0 && (c >> 32) == 1;
+    if (__builtin_amdgcn_ballot_w64(lane < S && !ready) == 0ull) break;
+    if (it == kSpinMax) {
+      if (lane == 0) __hip_atomic_store(pub.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  asm volatile("" ::: "memory");
+  rstd = __longlong_as_double(static_cast<long long>(r));
+  sc = __uint_as_float(static_cast<uint32_t>(c));
+}
+
 
 // Waits until flags 0 .. n - 1 (n <= 64) are set: lane t polls flag t with an
 // agent-scope atomic load (not served by the CU's L1; it reads the XCD's L2,
@@ -292,18 +317,18 @@ __device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const ui
     for (int q = 0; q < 4; ++q)
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
   if constexpr (FUSED) {
-    wait_flags(pub.flags, S, pub.err);
+    double rstd_l;
+    float sc_l;
+    wait_stats(pub, S, rstd_l, sc_l);  // lane t holds token t's values
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
       const int i = tid + 256 * r;
-      if (i < S * 16 * CPC) {
-        const int s = i / (16 * CPC), j = i - s * 16 * CPC;
-        const double rstd = __longlong_as_double(static_cast<long long>(__hip_atomic_load(
-            reinterpret_cast<uint64_t*>(const_cast<double*>(pub.rstd)) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
-        const double sd = static_cast<double>(__uint_as_float(__hip_atomic_load(
-            reinterpret_cast<uint32_t*>(const_cast<float*>(pub.sx)) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+      const int s = i / (16 * CPC), j = i - s * 16 * CPC;
+      const int src = s < S ? s : 0;
+      const double rstd = __shfl(rstd_l, src, 64);
+      const double sd = static_cast<double>(__shfl(sc_l, src, 64));
+      if (i < S * 16 * CPC)
         *reinterpret_cast<uint2*>(lds + s * ldw + j * 8) = codes8(ga[r], gb[r], gg[r], rstd, sd, 1.0 / sd);
-      }
     }
   } else {
 #pragma unroll
@@ -361,7 +386,7 @@ template <int CPC, int NT>
 __global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
   const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
-                     Publish{nullptr, nullptr, nullptr, nullptr});
+                     Publish{nullptr, nullptr, nullptr});
 }
 
 // ---------------------------------------------------------------------------
@@ -498,12 +523,13 @@ __global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, s
                        reinterpret_cast<const float*>(a.ws + off_sx), ksplit, a.S + H * ksplit + blockIdx.x);
 }
 
-// A GEMV CTA of XCD x is done with the XCD's rows: the last of the XCD's gx
-// GEMV CTAs (counted with a device-scope atomic) clears the row flags.
-__device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int x, int gx, uint32_t* flags) {
+// A GEMV CTA of XCD x is done with the XCD's published values: the last of the
+// XCD's gx GEMV CTAs (counted with a device-scope atomic) clears them.
+__device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int x, int gx, uint64_t* pub_r,
+                                         uint64_t* pub_s) {
   uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
   if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(gx - 1)) {
-    for (int t = 0; t < a.S; ++t) flags[t] = 0u;
+    for (int t = 0; t < a.S; ++t) pub_r[t] = 0u, pub_s[t] = 0u;
     __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -512,9 +538,11 @@ __device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int
 //  - Blocks b < 8 S are norm CTAs: token b / 8 for the XCD b % 8. Workgroups
 //    go to the XCDs round-robin, so blocks with equal b % 8 share an XCD and
 //    its L2 (with fewer XCDs the same holds for b % 4 or b % 2). Each XCD thus
-//    computes its own copy of every token's FP8 row and flags it in its L2.
-//  - The GEMV CTAs follow. They stream their weights at once, wait for their
-//    XCD's flags, take the rows from their own L2 and store partial sums.
+//    computes every token's norm statistics (rstd and the FP8 scale) and
+//    publishes them in its L2.
+//  - The GEMV CTAs follow. They stream their weights and their slice of ar,
+//    res and g_in at once, wait for their XCD's statistics, form the slice's
+//    FP8 codes (the norm's expressions) and store partial sums.
 //  - With EPI, head h runs all its k slices on XCD h % 8, and the head's last
 //    slice (the last of its CTAs in block order) waits for the other slices'
 //    flags, sums the partials (all in its L2) and runs the head's epilogue for
@@ -524,21 +552,25 @@ __device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int
 // No cache write-back or invalidate is needed and nothing crosses XCDs. The
 // norm CTAs come first in block order, so they are placed before any CTA that
 // waits for them, and the only wait is bounded. The last GEMV CTA of an XCD
-// clears the XCD's row flags, a head's epilogue CTA the slice flags, for the
+// clears the XCD's published values, a head's epilogue CTA the slice flags, for the
 // next call.
 template <int CPC, int NV, bool EPI>
 __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
   __shared__ double red[16];
   const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
-  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + p.off_flag) + x * kFlagStride;
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
-  double* rstd = reinterpret_cast<double*>(a.ws + p.off_rstd) + x * kSxStride;
+  uint64_t* pub_r = reinterpret_cast<uint64_t*>(a.ws + p.off_rstd) + x * 2 * kSxStride;
+  uint64_t* pub_s = pub_r + kSxStride;
   if (b < 8 * S) {
     const int tok = b >> 3;
-    norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, rstd);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's row stores have reached the L2
-    __syncthreads();
-    if (threadIdx.x == 0) flags[tok] = 1u;
+    double rstd;
+    float sc;
+    norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, &rstd, &sc);
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_s_waitcnt(0);  // sx (read by the epilogue) is in the L2 before the values are
+      pub_r[tok] = static_cast<uint64_t>(__double_as_longlong(rstd));
+      pub_s[tok] = (uint64_t{1} << 32) | __float_as_uint(sc);
+    }
     return;
   }
   int h, ks;
@@ -554,9 +586,9 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
   }
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   gemv_tile<CPC, 1, true>(a, h, ks, nullptr, part, S + ks * H + h,
-                          Publish{flags, rstd, sx, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
+                          Publish{pub_r, pub_s, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
   if constexpr (!EPI) {
-    if (threadIdx.x == 0) xcd_done(a, p, x, (H * ksplit - x + 7) / 8, flags);
+    if (threadIdx.x == 0) xcd_done(a, p, x, (H * ksplit - x + 7) / 8, pub_r, pub_s);
     return;
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
@@ -573,7 +605,7 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
       head_epilogue<true>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
     if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
   }
-  if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, flags);
+  if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, pub_r, pub_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,11 +712,9 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   p.off_sx = off;  // per-token scales: one copy per XCD when fused, with rstd
   off = align_up(off + sizeof(float) * (p.fused ? 8 * kSxStride : S), 256);
   p.off_rstd = off;
-  off += p.fused ? sizeof(double) * 8 * kSxStride : 0;
+  off += p.fused ? 2 * sizeof(uint64_t) * 8 * kSxStride : 0;  // published rstd and scale words
   p.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.ksplit) * S * N, 256);
-  p.off_flag = off;
-  off += p.fused ? 8 * kFlagStride * sizeof(uint32_t) : 0;
   p.off_done = off;
   off += p.fused ? 8 * 128 : 0;
   p.off_hdone = off;

@@ -40,7 +40,7 @@ struct DecodePlan {
   int ksplit;          // CTAs along k
   bool fused;          // norm and GEMV in one launch (a per-XCD copy of the FP8 rows)
   bool fused_epilogue; // the head epilogue in that launch too
-  size_t off_x8, off_sx, off_rstd, off_part, off_flag, off_done, off_hdone, off_err, total;
+  size_t off_x8, off_sx, off_rstd, off_part, off_done, off_hdone, off_err, total;
 };
 DecodePlan decode_plan(int S, int K, int nkv);
 hipError_t launch_decode(const Args& a, const DecodePlan& p);
