@@ -688,9 +688,9 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   // whole grid is resident at once (a grid in two rounds streams its second
   // half only after the first has finished). CTAs per CU allowed by the
   // kernel's register allocation at 256 threads, for 1..4 chunks (the compiler
-  // reports about 70, 104, 168 and 262 registers a lane with two token tiles).
+  // reports 70, 94, 114 and 150 registers a lane with two token tiles).
   static const int kCands[] = {4, 3, 2, 1};
-  static const int kPerCu[] = {0, 7, 4, 3, 1};
+  static const int kPerCu[] = {0, 7, 5, 4, 3};
   int pick = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
