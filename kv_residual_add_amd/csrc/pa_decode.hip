@@ -1,27 +1,29 @@
 // Decode prologue on gfx950: per-token FP8 activations against a per-row
 // scaled FP8 weight, for up to 64 tokens.
 //
-// Three kernels on the caller's stream (the K1 mono_pre page,
-// vllm.models.minimax_m3.amd.mono.kernels.pre_attn, emit_pre_attn: norm tasks,
-// GEMV tasks, head tasks):
-//   decode_norm      per token, one CTA of up to 1024 threads: residual add (f32)
-//                    + bf16 residual out, Gemma RMSNorm, per-token FP8
-//                    quantization into a workspace row (norm_quant).
-//   decode_gemv      the fused projection as an HBM-bound GEMV: a CTA owns one
-//                    128-row head x a k slice; every wave streams its 32 rows'
-//                    packed weight with dwordx4 loads issued before anything
-//                    waits on them, the FP8 activation slice sits in LDS, and
-//                    32x32x16 bf16 MFMAs take up to 32 tokens a tile on exactly
-//                    widened FP8 codes. k-slice partial sums go to the workspace.
-//   decode_epilogue  per (token, head), one wave: sums the k-slice partials in
-//                    a fixed order, applies the activation and row scales, then
-//                    the head's role (head tasks; head_norm_rope; the epilogue
-//                    page vllm.models.minimax_m3.nvidia.ops.qkv_index_fused_epilogue,
-//                    per-role branches).
-// The kernel boundaries carry the results from one stage to the next: measured
-// on MI355X, a device-scope hand-off between CTAs inside one launch (L2
-// write-back on publish, invalidate on acquire, on every CTA) cost more than the
-// two boundaries under graph replay.
+// The stages (the K1 mono_pre page, vllm.models.minimax_m3.amd.mono.kernels.
+// pre_attn, emit_pre_attn: norm tasks, GEMV tasks, head tasks):
+//   norm      per token: residual add (f32) + bf16 residual out, Gemma RMSNorm,
+//             per-token FP8 quantization (norm_quant).
+//   GEMV      the fused projection as an HBM-bound GEMV: a CTA owns one 128-row
+//             head x a k slice; every wave streams its 32 rows' packed weight
+//             with dwordx4 loads issued before anything waits on them, the FP8
+//             activation slice sits in LDS, and 32x32x16 bf16 MFMAs take up to
+//             32 tokens a tile on exactly widened FP8 codes. k-slice partial
+//             sums go to the workspace.
+//   epilogue  per (token, head), one wave: sums the k-slice partials in a fixed
+//             order, applies the activation and row scales, then the head's role
+//             (head tasks; head_norm_rope; the epilogue page
+//             vllm.models.minimax_m3.nvidia.ops.qkv_index_fused_epilogue,
+//             per-role branches).
+// Launches (decode_plan): up to 16 tokens, norm and GEMV share one launch
+// (decode_fused: each XCD computes the tokens' norm statistics, and its GEMV
+// CTAs take them from that XCD's L2 while their weights stream), and the
+// epilogue joins it when the weight is small; otherwise decode_norm,
+// decode_gemv and decode_epilogue are launches of their own. A hand-off across
+// XCDs inside a launch (L2 write-back on publish, invalidate on acquire)
+// measured slower than kernel boundaries under graph replay; one inside an
+// XCD's L2 did not.
 //
 // Numerics: the input norm, its FP8 decision and the head epilogue run in
 // float64 with contraction off, so a code is decided from the same value the

@@ -1,12 +1,14 @@
 // Prefill prologue on gfx950: MXFP8 activations against an MXFP8 weight.
 //
 // Two kernels on the caller's stream:
-//   1. prefill_prepass  one CTA per token: residual add (f32) + bf16 residual
-//                       out, Gemma RMSNorm, then OCP-MX quantization (E8M0
-//                       scale per 32-wide k block, E4M3 elements) into the
-//                       GEMM's packed activation layout in the workspace.
+//   1. prefill_prepass  token rows walked by one CTA per resident slot:
+//                       residual add (f32) + bf16 residual out, Gemma RMSNorm,
+//                       then OCP-MX quantization (E8M0 scale per 32-wide k
+//                       block, E4M3 elements) into the GEMM's packed activation
+//                       layout in the workspace.
 //   2. prefill_gemm     C^T = W . X^T on MFMA. One CTA owns one 128-wide head
-//                       x 128 tokens; each wave 32 tokens x the whole head.
+//                       x 128 NTW tokens; each wave 32 NTW tokens x the whole
+//                       head.
 //                       q and index_q heads run block-scaled FP8 MFMAs
 //                       (v_mfma_scale_f32_32x32x64_f8f6f4); the k, v and
 //                       index_k heads, whose per-token scales and codes must
