@@ -61,27 +61,34 @@ def calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 10}))
 
 
-def algorithmic(wl, launches=3):
+def algorithmic(wl, structure=0):
     """(bytes per call, bytes of the dominant kernel per launch, flops per call,
     the dominant kernel's name).
 
-    Decode runs in 3, 2 or 1 launches (pa_decode_launches): the dominant kernel
-    is the GEMV (FP8 weight + FP8 activation codes), the norm + GEMV launch
-    (weight, the ar / res rows and gamma in, the bf16 residual out) or the
-    whole call."""
+    The decode projection always has a launch of its own; the input norm, the
+    head epilogue or both may share it (pa_decode_structure flags). Its launch
+    is the dominant kernel: the FP8 weight and activation codes, plus the
+    ar / res rows, gamma and the bf16 residual out when the norm is in it, or
+    the outputs, cache inserts and per-token inputs of the epilogue when that
+    is in it (in place of the activation codes from the norm launch)."""
     S, K, nkv = wl.tokens, wl.hidden, wl.nkv
     N = (19 * nkv + 1) * 128
-    call_bytes = (N * K + 4 * N + 4 * S * K + 2 * S * K + 2 * K + 4 * 256
+    norm_bytes = 4 * S * K + 2 * S * K + 2 * K  # ar + res in, h_out out, g_in
+    call_bytes = (N * K + 4 * N + norm_bytes + 4 * 256
                   + S * 16 * nkv * 256 + S * nkv * 256 + S * nkv * (256 + 8) + 128 * S
                   + 128 * S + 16 * S)
     flops = 2 * S * N * K
     if wl.mode == "prefill":
         call_bytes += N * K // 32 - 4 * N  # E8M0 block scales instead of row scales
         return call_bytes, N * K + S * K, flops, "prefill_gemm"
-    if launches == 1:
+    norm_fused = bool(structure & 1)
+    epi_fused = bool(structure & 2)
+    if norm_fused and epi_fused:
         return call_bytes, call_bytes, flops, "decode_fused (norm + GEMV + head epilogue)"
-    if launches == 2:
-        return call_bytes, N * K + 4 * S * K + 2 * K + 2 * S * K, flops, "decode_fused (norm + GEMV)"
+    if norm_fused:
+        return call_bytes, N * K + norm_bytes, flops, "decode_fused (norm + GEMV)"
+    if epi_fused:
+        return call_bytes, call_bytes - norm_bytes + S * K, flops, "decode_gemv_epi (GEMV + head epilogue)"
     return call_bytes, N * K + S * K, flops, "decode_gemv"
 
 
@@ -165,8 +172,8 @@ def main():
     dev = prob.device
     S, K = wl.tokens, wl.hidden
     N = prob.N
-    launches = B.pa_decode_launches(prob.dims) if prob.mode == B.PA_MODE_DECODE else 0
-    call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, launches)
+    structure = B.pa_decode_structure(prob.dims) if prob.mode == B.PA_MODE_DECODE else 0
+    call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, structure)
 
     # rotating pool of distinct weight + activation sets
     set_bytes = prob.w_packed.numel() + prob.w_scales.numel() * prob.w_scales.element_size() \
@@ -246,6 +253,7 @@ def main():
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     eager_s = e0.elapsed_time(e1) / 1e3
+    B.pa_workspace_status(prob.workspace)  # raises if an in-kernel wait gave up
 
     key = args.config
     traffic = measured_traffic(key, wl.mode)

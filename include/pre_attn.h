@@ -89,7 +89,8 @@ typedef enum pa_status {
   PA_ERR_DIMS = -7,      /* num_pages < 1, max_pos < 1 or eps not finite >= 0 */
   PA_ERR_HIP = -8,       /* a HIP runtime call or launch failed */
   PA_ERR_DEVICE = -9,    /* the current device is not a gfx950 GPU */
-  PA_ERR_MODE = -10      /* unknown mode argument */
+  PA_ERR_MODE = -10,     /* unknown mode argument */
+  PA_ERR_SYNC = -11      /* a kernel's bounded wait for another CTA gave up */
 } pa_status;
 
 /* Problem size of one call. */
@@ -107,20 +108,34 @@ typedef struct pa_dims {
 
 /* Bytes of device workspace a call with these dims needs (0 on bad dims or
  * mode). The workspace is caller-owned scratch; it may be reused by any later
- * call whose requirement it meets, once pa_workspace_init has run on it. */
+ * call, of either mode and any dims, whose requirement it meets, once
+ * pa_workspace_init has run on it: the words the kernels synchronize through
+ * sit at the same offsets for every call, and each call leaves them cleared. */
 size_t pa_workspace_bytes(const pa_dims* dims, int mode);
 
 /* How pre_attn_decode runs a call with these dims on the device, for
- * reporting and tests (the outputs do not depend on it). 1: one launch (the
- * input norm, the projection and the head epilogue); 2: the input norm with the
- * projection, then the head epilogue; 3: norm, projection and epilogue
- * launches. 0 on bad dims. */
-int pa_decode_launches(const pa_dims* dims);
+ * reporting and tests (the outputs do not depend on it): a set of flags.
+ * The projection always has a launch of its own; PA_DECODE_NORM_FUSED puts the
+ * input norm into it and PA_DECODE_EPILOGUE_FUSED the head epilogue (per-head
+ * norm, RoPE, outputs and cache inserts). Launches per call: 3 minus the
+ * flags set. Negative pa_status on bad dims. */
+#define PA_DECODE_NORM_FUSED 1
+#define PA_DECODE_EPILOGUE_FUSED 2
+int pa_decode_structure(const pa_dims* dims);
 
 /* Prepares a freshly allocated workspace of `bytes` bytes for use (clears the
  * library's counters with a fill kernel on `stream`). Needed once per
  * allocation; calls leave it ready for the next call. */
 int pa_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Whether every call on this workspace since pa_workspace_init ran to
+ * completion inside the kernels. A CTA that waits for another CTA's result
+ * (the one-launch decode paths) gives up after a bounded spin, so that no
+ * launch can hang, and then marks the workspace; the outputs of that call are
+ * not valid. Returns PA_OK, or PA_ERR_SYNC once marked (until the next
+ * pa_workspace_init). Unlike the other entry points this one synchronizes:
+ * it waits for `stream` to finish, then reads one word of the workspace. */
+int pa_workspace_status(const void* workspace, void* stream);
 
 /* Bytes of the packed weight (and packed block scales) for N rows x hidden. */
 size_t pa_packed_weight_bytes(int mode, int32_t n_rows, int32_t hidden);

@@ -9,6 +9,9 @@ from ._binding import (  # noqa: F401
     DECODE_MAX_TOKENS,
     EXPORTS,
     LIB_PATH,
+    PA_DECODE_EPILOGUE_FUSED,
+    PA_DECODE_NORM_FUSED,
+    PA_ERR_SYNC,
     PA_MODE_DECODE,
     PA_MODE_PREFILL,
     PaError,
@@ -22,8 +25,9 @@ from ._binding import (  # noqa: F401
     pa_packed_scale_bytes,
     pa_packed_weight_bytes,
     pa_workspace_bytes,
-    pa_decode_launches,
+    pa_decode_structure,
     pa_workspace_init,
+    pa_workspace_status,
     pre_attn_decode,
     pre_attn_prefill,
 )

@@ -22,11 +22,15 @@ HEAD_DIM = 128
 PAGE = 16
 PAGE_BYTES = 2048
 DECODE_MAX_TOKENS = 64
+PA_DECODE_NORM_FUSED = 1
+PA_DECODE_EPILOGUE_FUSED = 2
+PA_ERR_SYNC = -11
 
 EXPORTS = (
     "pa_workspace_bytes",
-    "pa_decode_launches",
+    "pa_decode_structure",
     "pa_workspace_init",
+    "pa_workspace_status",
     "pa_packed_weight_bytes",
     "pa_packed_scale_bytes",
     "pa_pack_weight_decode",
@@ -78,8 +82,10 @@ def load() -> ctypes.CDLL:
         dims_p = ctypes.POINTER(pa_dims)
         lib.pa_workspace_bytes.argtypes = [dims_p, ctypes.c_int]
         lib.pa_workspace_bytes.restype = sz
-        lib.pa_decode_launches.argtypes = [dims_p]
-        lib.pa_decode_launches.restype = ctypes.c_int
+        lib.pa_decode_structure.argtypes = [dims_p]
+        lib.pa_decode_structure.restype = ctypes.c_int
+        lib.pa_workspace_status.argtypes = [P, P]
+        lib.pa_workspace_status.restype = ctypes.c_int
         lib.pa_workspace_init.argtypes = [P, sz, P]
         lib.pa_workspace_init.restype = ctypes.c_int
         lib.pa_packed_weight_bytes.argtypes = [ctypes.c_int, i32, i32]
@@ -162,8 +168,17 @@ def pa_workspace_bytes(dims: pa_dims, mode: int) -> int:
     return load().pa_workspace_bytes(ctypes.byref(dims), mode)
 
 
-def pa_decode_launches(dims: pa_dims) -> int:
-    return load().pa_decode_launches(ctypes.byref(dims))
+def pa_decode_structure(dims: pa_dims) -> int:
+    """PA_DECODE_* flags of a decode call with these dims (negative status on bad dims)."""
+    return load().pa_decode_structure(ctypes.byref(dims))
+
+
+def pa_workspace_status(workspace: torch.Tensor, stream=None) -> None:
+    """Raises PaError(PA_ERR_SYNC) if a bounded in-kernel wait gave up on this
+    workspace since it was initialised (synchronizes the stream)."""
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    _check(load().pa_workspace_status(workspace.data_ptr(), _stream(stream)), "pa_workspace_status")
 
 
 def pa_workspace_init(workspace: torch.Tensor, stream=None) -> None:

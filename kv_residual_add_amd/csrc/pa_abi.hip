@@ -172,11 +172,25 @@ size_t pa_workspace_bytes(const pa_dims* dims, int mode) {
   return workspace_for(dims, mode);
 }
 
-int pa_decode_launches(const pa_dims* d) {
-  if (check_dims(d, PA_MODE_DECODE) != PA_OK) return 0;
+int pa_decode_structure(const pa_dims* d) {
+  const int st = check_dims(d, PA_MODE_DECODE);
+  if (st != PA_OK) return st;
   const pa::DecodePlan p = pa::decode_plan(d->tokens, d->hidden, d->nkv);
-  if (p.chunks_per_cta == 0) return 0;
-  return p.fused ? (p.fused_epilogue ? 1 : 2) : 3;
+  if (p.chunks_per_cta == 0) return PA_ERR_HIDDEN;
+  return (p.fused ? PA_DECODE_NORM_FUSED : 0) |
+         (p.fused_epilogue || p.gemv_epilogue ? PA_DECODE_EPILOGUE_FUSED : 0);
+}
+
+int pa_workspace_status(const void* workspace, void* stream) {
+  if (!workspace) return PA_ERR_NULL;
+  if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  uint32_t word = 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&word, static_cast<const uint8_t*>(workspace) + pa::kSyncErr, sizeof(word),
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "pa_workspace_status");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "pa_workspace_status");
+  return word ? PA_ERR_SYNC : PA_OK;
 }
 
 int pa_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -267,6 +281,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_HIP: return "HIP runtime error (see pa_last_error_detail)";
     case PA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case PA_ERR_MODE: return "unknown mode";
+    case PA_ERR_SYNC: return "a kernel's bounded wait gave up: that call's outputs are not valid";
     default: return "unknown status";
   }
 }

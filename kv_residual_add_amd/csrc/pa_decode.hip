@@ -45,9 +45,12 @@ constexpr int kMaxLds = 64 * 1024;
 // norm at 256 threads then holds at most four 8-element vectors a thread)
 constexpr int kFusedMaxS = 16;
 constexpr int kFusedMaxK = 8192;
-constexpr int kSxStride = 64;    // scale floats per XCD copy
-constexpr int kMaxKsplit = 64;   // slice flags per head
+constexpr int kSxStride = 64;    // scale floats per XCD copy (and published words per XCD)
+constexpr int kMaxKsplit = kSyncMaxSlices;  // slice flags per head
 constexpr size_t kFusedEpiMaxWeight = 4u << 20;  // weight bytes up to which whole heads per XCD pay
+// GEMV + epilogue launch: a head's slices wait for each other, so they must be
+// resident together on the head's XCD: at most one slice per CU of an XCD
+constexpr int kGemvEpiMaxKsplit = 32;
 
 // Block reductions over up to 16 waves: each wave's result goes to LDS, then
 // every thread combines the waves' values in the same fixed order (pairwise).
@@ -610,6 +613,41 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
   if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, pub_r, pub_s);
 }
 
+// The GEMV with the head epilogue in the same launch, after a norm launch (more
+// tokens than the fused launch takes). Head h runs all its k slices on XCD
+// h % 8 (blocks with equal b % 8 share an XCD), so its partial sums stay in
+// that XCD's L2. Each slice stores its partial, sets its flag, waits for the
+// head's other flags, and then runs the head's epilogue for its share of the
+// tokens (ks, ks + ksplit, ...), reading the partials from the L2. The last
+// slice past the wait (a per-head counter) clears the flags for the next call.
+// A head's slices are dispatched together (a contiguous run of its XCD's
+// blocks, at most one per CU of the XCD), and every wait is bounded.
+template <int CPC, int NT>
+__global__ __launch_bounds__(256) void decode_gemv_epi(Args a, DecodePlan p) {
+  const int b = blockIdx.x, x = b & 7, j = b >> 3, H = a.heads(), ksplit = p.ksplit;
+  const int h = x + 8 * (j / ksplit), ks = j % ksplit;
+  if (h >= H) return;  // XCDs with fewer heads have idle blocks
+  float* part = reinterpret_cast<float*>(a.ws + p.off_part);
+  const float* sx = reinterpret_cast<const float*>(a.ws + p.off_sx);
+  uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + p.off_err);
+  gemv_tile<CPC, NT, false>(a, h, ks, a.ws + p.off_x8, part, a.S + ks * H + h, Publish{nullptr, nullptr, nullptr});
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
+  __syncthreads();
+  uint32_t* hflags = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(a.ws + p.off_hcnt) + h;
+  if (threadIdx.x == 0) hflags[ks] = 1u;
+  if (threadIdx.x < 64) wait_flags(hflags, ksplit, err);
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit - 1)) {
+    for (int f = 0; f < ksplit; ++f) hflags[f] = 0u;  // every slice is past its wait
+    __hip_atomic_store(hcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int wave = threadIdx.x >> 6;
+  for (int tok = ks + ksplit * wave; tok < a.S; tok += 4 * ksplit)
+    head_epilogue<true>(a, h, tok, part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+}
+
 // ---------------------------------------------------------------------------
 // norm kernel: blockDim.x threads (a multiple of 64, at most 1024)
 template <int NV>
@@ -653,8 +691,17 @@ hipError_t launch_gemv(const Args& a, const DecodePlan& p) {
   return hipGetLastError();
 }
 
+template <int CPC, int NT>
+hipError_t launch_gemv_epi(const Args& a, const DecodePlan& p) {
+  const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
+  const dim3 grid(8 * ((a.heads() + 7) / 8) * p.ksplit);
+  hipLaunchKernelGGL((decode_gemv_epi<CPC, NT>), grid, dim3(256), lds, a.stream, a, p);
+  return hipGetLastError();
+}
+
 template <int CPC>
 hipError_t launch_gemv_nt(const Args& a, const DecodePlan& p) {
+  if (p.gemv_epilogue) return a.S <= 32 ? launch_gemv_epi<CPC, 1>(a, p) : launch_gemv_epi<CPC, 2>(a, p);
   return a.S <= 32 ? launch_gemv<CPC, 1>(a, p) : launch_gemv<CPC, 2>(a, p);
 }
 
@@ -691,16 +738,20 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   // half only after the first has finished). CTAs per CU allowed by the
   // kernel's register allocation at 256 threads, for 1..4 chunks (the compiler
   // reports 70, 94, 114 and 150 registers a lane with two token tiles).
+  // When no grid is resident at once (many heads and a long k), the largest
+  // chunk count, i.e. the fewest CTAs, is taken.
   static const int kCands[] = {4, 3, 2, 1};
   static const int kPerCu[] = {0, 7, 5, 4, 3};
-  int pick = 0;
+  int pick = 0, fewest = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
     if (static_cast<size_t>(S) * (c * 128 + kLdsPad) > kMaxLds) continue;
+    if (fewest == 0) fewest = c;
     if (heads * (nchk / c) > 256 * kPerCu[c]) continue;
     pick = c;  // smallest fitting candidate so far
     if (heads * (nchk / c) >= 256) break;
   }
+  if (pick == 0) pick = fewest;  // c = 1 always fits the LDS: S * 144 bytes
   p.chunks_per_cta = pick;
   p.ksplit = pick ? nchk / pick : 0;
   p.fused = pick > 0 && S <= kFusedMaxS && K <= kFusedMaxK;
@@ -708,21 +759,21 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   // is balanced when they divide evenly, and cheap when the weight is small
   p.fused_epilogue = p.fused && p.ksplit <= kMaxKsplit &&
                      (heads % 8 == 0 || static_cast<size_t>(N) * K <= kFusedEpiMaxWeight);
-  size_t off = 0;
-  p.off_x8 = off;  // the FP8 rows (the three-launch path)
+  // more tokens: the epilogue joins the GEMV's launch, which saves the partial
+  // sums' round trip through memory (ksplit x S x N floats)
+  p.gemv_epilogue = pick > 0 && !p.fused && p.ksplit <= kGemvEpiMaxKsplit;
+  p.off_err = kSyncErr;
+  p.off_done = kSyncDone;
+  p.off_rstd = kSyncPub;  // published rstd and scale words
+  p.off_hdone = kSyncHeadFlags;
+  p.off_hcnt = kSyncHeadCnt;
+  size_t off = kSyncBytes;
+  p.off_x8 = off;  // the FP8 rows (not fused)
   off = align_up(off + (p.fused ? 0 : static_cast<size_t>(S) * K), 256);
-  p.off_sx = off;  // per-token scales: one copy per XCD when fused, with rstd
+  p.off_sx = off;  // per-token scales: one copy per XCD when fused
   off = align_up(off + sizeof(float) * (p.fused ? 8 * kSxStride : S), 256);
-  p.off_rstd = off;
-  off += p.fused ? 2 * sizeof(uint64_t) * 8 * kSxStride : 0;  // published rstd and scale words
   p.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p.ksplit) * S * N, 256);
-  p.off_done = off;
-  off += p.fused ? 8 * 128 : 0;
-  p.off_hdone = off;
-  off += p.fused ? static_cast<size_t>(heads) * kMaxKsplit * sizeof(uint32_t) : 0;  // slice flags per head
-  p.off_err = off;
-  off += p.fused ? 256 : 0;
   p.total = off;
   return p;
 }
@@ -767,6 +818,7 @@ hipError_t launch_decode(const Args& a, const DecodePlan& p) {
   }
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
+  if (p.gemv_epilogue) return hipSuccess;
   hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part,
                      p.off_sx, p.ksplit);
   return hipGetLastError();

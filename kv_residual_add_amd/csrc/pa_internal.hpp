@@ -34,13 +34,30 @@ struct Args {
   __host__ __device__ int heads() const { return 19 * nkv + 1; }
 };
 
+// The words kernels synchronize through (flags, counters, published
+// statistics, the failure word) sit at the start of every workspace at fixed
+// offsets, whatever the call's dims and mode, and every call leaves them zero.
+// Data regions start past them, so one workspace can serve calls of any shape
+// in turn without a stale data byte ever reading as a flag.
+constexpr size_t kSyncErr = 0;             // failure word: a bounded wait gave up
+constexpr size_t kSyncDone = 256;          // per-XCD GEMV counters, 128 bytes apart
+constexpr size_t kSyncPub = 1280;          // per-XCD published rstd and scale words
+constexpr size_t kSyncPubBytes = 2 * 8 * 64 * sizeof(uint64_t);
+constexpr size_t kSyncHeadFlags = kSyncPub + kSyncPubBytes;  // per-head slice flags
+constexpr int kSyncMaxHeads = 19 * 4 + 1;  // heads at the largest nkv
+constexpr int kSyncMaxSlices = 64;         // slice flags per head
+constexpr size_t kSyncHeadCnt = kSyncHeadFlags + kSyncMaxHeads * kSyncMaxSlices * sizeof(uint32_t);
+constexpr size_t kSyncBytes = 32768;
+static_assert(kSyncHeadCnt + kSyncMaxHeads * sizeof(uint32_t) <= kSyncBytes, "synchronization words overflow");
+
 // Decode: split of the GEMV's k range and the workspace carve-up.
 struct DecodePlan {
   int chunks_per_cta;  // 128-wide k chunks per CTA
   int ksplit;          // CTAs along k
   bool fused;          // norm and GEMV in one launch (a per-XCD copy of the FP8 rows)
   bool fused_epilogue; // the head epilogue in that launch too
-  size_t off_x8, off_sx, off_rstd, off_part, off_done, off_hdone, off_err, total;
+  bool gemv_epilogue;  // not fused: the head epilogue in the GEMV's launch
+  size_t off_x8, off_sx, off_rstd, off_part, off_done, off_hdone, off_hcnt, off_err, total;
 };
 DecodePlan decode_plan(int S, int K, int nkv);
 hipError_t launch_decode(const Args& a, const DecodePlan& p);
@@ -48,7 +65,7 @@ hipError_t launch_pack_decode(const uint8_t* w, uint8_t* wp, int N, int K, hipSt
 
 // Prefill.
 struct PrefillPlan {
-  size_t off_xq, off_xs, off_cnt, total;
+  size_t off_xq, off_xs, total;
 };
 PrefillPlan prefill_plan(int M, int K, int nkv);
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p);

@@ -818,13 +818,11 @@ PrefillPlan prefill_plan(int M, int K, int nkv) {
   (void)nkv;
   PrefillPlan p{};
   const size_t mpad = (static_cast<size_t>(M) + kTokAlign - 1) / kTokAlign * kTokAlign;
-  size_t off = 0;
+  size_t off = kSyncBytes;  // the synchronization words stay untouched
   p.off_xq = off;
   off = align_up(off + mpad * K, 256);
   p.off_xs = off;
   off = align_up(off + mpad * K / 32, 256);
-  p.off_cnt = off;
-  off += 1024;
   p.total = off;
   return p;
 }

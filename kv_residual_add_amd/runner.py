@@ -65,22 +65,24 @@ class Problem:
             self.w_scales = torch.empty(ns, dtype=torch.uint8, device=dev)
             B.pa_pack_weight_prefill(w, we, self.w_packed, self.w_scales)
 
-    def args(self, w_packed=None, w_scales=None, **over):
+    def args(self, w_packed=None, w_scales=None, workspace=None, **over):
         t = dict(self.t, **over)
         return (self.dims, t["ar"], t["res"], t["h_out"], t["g_in"],
                 self.w_packed if w_packed is None else w_packed,
                 self.w_scales if w_scales is None else w_scales,
                 t["g_q"], t["g_k"], t["g_iq"], t["g_ik"], t["cos_sin"], t["positions"],
                 t["slot_mapping"], t["k_cache"], t["v_cache"], t["k_scale"], t["v_scale"],
-                t["index_cache"], t["q_out"], t["iq_out"], self.workspace)
+                t["index_cache"], t["q_out"], t["iq_out"], self.workspace if workspace is None else workspace)
 
     def run(self, stream=None, **over) -> None:
         fn = B.pre_attn_decode if self.mode == B.PA_MODE_DECODE else B.pre_attn_prefill
         fn(*self.args(**over), stream=stream)
 
     def outputs(self) -> dict:
-        """Outputs and caches as numpy raw bits (synchronizes)."""
+        """Outputs and caches as numpy raw bits (synchronizes). Raises if an
+        in-kernel wait gave up on the workspace since it was initialised."""
         torch.cuda.synchronize(self.device)
+        B.pa_workspace_status(self.workspace)
         out = {}
         for k in ("h_out", "q_out", "iq_out"):
             out[k] = self.t[k].view(torch.int16).cpu().numpy().view(np.uint16)

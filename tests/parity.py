@@ -144,29 +144,33 @@ def check_written_sets(inp: dict, got: dict) -> None:
         assert np.all(np.isfinite(got[name][masks[name]])), f"{name}: non-finite scale"
 
 
+SYNC_BYTES = 32768  # the workspace's leading synchronization words
+
+
 def prefill_activation_codes(workspace: np.ndarray, M: int, K: int):
     """The MXFP8 activation codes and block scales the prefill norm pass leaves
     in the workspace, unpacked to [Mpad, K] and [Mpad, K // 32] (Mpad = M
     rounded up to 256 token rows).
 
-    The packed layout is the prefill MFMA's operand order: token tile
-    tt = m // 32 and k step ks = k // 64 own the 2 KB block at
-    (tt * nks + ks) * 2048; in it, lane l = m % 32 + 32 * ((k % 32) // 16) holds
-    16 consecutive codes at region * 1024 + 16 l, region = (k % 64) // 32.
-    The scale of block b = k // 32 is byte (tt * nks + b // 2) * 64 + m % 32 +
-    32 (b % 2) of the region that starts at the next 256-byte boundary after
-    the codes.
+    The codes start past the workspace's 32 KB of synchronization words, in
+    the prefill MFMA's operand order: token tile tt = m // 32 and k step
+    ks = k // 64 own the 2 KB block at (tt * nks + ks) * 2048; in it, lane
+    l = m % 32 + 32 * ((k % 32) // 16) holds 16 consecutive codes at
+    region * 1024 + 16 l, region = (k % 64) // 32. The scale of block
+    b = k // 32 is byte (tt * nks + b // 2) * 64 + m % 32 + 32 (b % 2) of the
+    region that starts at the next 256-byte boundary after the codes.
     """
+    base = SYNC_BYTES
     mpad = -(-M // 256) * 256
     nks = K // 64
     m = np.arange(mpad)[:, None]
     k = np.arange(K)[None, :]
     tt, tl = m // 32, m % 32
     ks, kk = k // 64, k % 64
-    off = (tt * nks + ks) * 2048 + (kk // 32) * 1024 + (tl + 32 * ((kk // 16) % 2)) * 16 + kk % 16
+    off = base + (tt * nks + ks) * 2048 + (kk // 32) * 1024 + (tl + 32 * ((kk // 16) % 2)) * 16 + kk % 16
     xq = workspace[off]
     b = np.arange(K // 32)[None, :]
-    xs_base = -(-(mpad * K) // 256) * 256
+    xs_base = base + -(-(mpad * K) // 256) * 256
     soff = xs_base + (tt * nks + b // 2) * 64 + tl + 32 * (b % 2)
     xs = workspace[soff]
     return xq, xs

@@ -52,18 +52,39 @@ def test_workspace_sizes():
 
 
 def test_decode_launch_structure():
-    # few tokens with a small weight: one launch; few tokens with a larger
-    # weight whose heads do not divide over the 8 XCDs: two; more tokens: three
-    assert K.pa_decode_launches(_dims(tokens=1, hidden=1024)) == 1
-    assert K.pa_decode_launches(_dims(tokens=8)) == 2
-    assert K.pa_decode_launches(_dims(tokens=16, hidden=8192)) == 2
-    assert K.pa_decode_launches(_dims(tokens=17)) == 3
-    assert K.pa_decode_launches(_dims(tokens=64, nkv=2)) == 3
-    assert K.pa_decode_launches(_dims(tokens=8, hidden=8320)) == 3  # hidden past the fused norm's reach
-    assert K.pa_decode_launches(_dims(tokens=65)) == 0
-    assert K.pa_decode_launches(_dims(nkv=3)) == 0
-    # the fused structures keep a copy of the FP8 rows per XCD
-    assert K.pa_workspace_bytes(_dims(tokens=8), K.PA_MODE_DECODE) >= 8 * 8 * 6144
+    NORM, EPI = K.PA_DECODE_NORM_FUSED, K.PA_DECODE_EPILOGUE_FUSED
+    # few tokens with a small weight: norm, projection and epilogue in one
+    # launch; few tokens with a larger weight whose heads do not divide over
+    # the 8 XCDs: norm with the projection; more tokens, or a hidden size past
+    # the fused norm's reach: the epilogue with the projection (when a head's
+    # k slices are few enough to wait for each other)
+    assert K.pa_decode_structure(_dims(tokens=1, hidden=1024)) == NORM | EPI
+    assert K.pa_decode_structure(_dims(tokens=8)) == NORM
+    assert K.pa_decode_structure(_dims(tokens=16, hidden=8192)) == NORM
+    assert K.pa_decode_structure(_dims(tokens=17)) == EPI
+    assert K.pa_decode_structure(_dims(tokens=64, nkv=2)) == EPI
+    # 65 k slices of one chunk each (8320 = 65 x 128): too many for a head's
+    # slices to wait for each other, so the epilogue is a launch of its own
+    assert K.pa_decode_structure(_dims(tokens=8, hidden=8320)) == 0
+    assert K.pa_decode_structure(_dims(tokens=20, hidden=4736)) == 0  # 37 slices
+    assert K.pa_decode_structure(_dims(tokens=8, hidden=16384)) == EPI  # 32 slices
+    assert K.pa_decode_structure(_dims(tokens=65)) < 0
+    assert K.pa_decode_structure(_dims(nkv=3)) < 0
+    # every valid shape has a plan, also where no grid is resident at once
+    for nkv in (1, 2, 4):
+        for hidden in (128, 1024, 6144, 8192, 16384):
+            for tokens in (1, 16, 17, 64):
+                d = _dims(tokens=tokens, hidden=hidden, nkv=nkv)
+                assert K.pa_decode_structure(d) >= 0, (nkv, hidden, tokens)
+                assert K.pa_workspace_bytes(d, K.PA_MODE_DECODE) > 0
+
+
+def test_workspace_sync_words_fixed():
+    # the synchronization words sit in the first 32 KB of every workspace, so
+    # every decode and prefill workspace holds them
+    for mode in (K.PA_MODE_DECODE, K.PA_MODE_PREFILL):
+        for tokens in (1, 8, 64):
+            assert K.pa_workspace_bytes(_dims(tokens=tokens, hidden=128), mode) > 32768
 
 
 def test_packed_sizes():

@@ -45,6 +45,9 @@ DECODE_SMALL = [
     (17, 768, 1, {}),
     (33, 1536, 2, {"outlier_frac": 0.01}),
     (64, 2048, 1, {"skip_frac": 0.1}),
+    (20, 4736, 1, {}),  # 37 k slices: the epilogue in a launch of its own
+    (8, 16384, 1, {}),  # hidden past the fused norm's reach, 32 k slices
+    (4, 16384, 2, {}),  # more CTAs than are resident at once
 ]
 
 
@@ -174,6 +177,48 @@ def test_degenerate_rows(mode):
     assert got["k_scale"][page, 0, t] == 1.0 and got["v_scale"][page, 0, t] == 1.0
 
 
+def test_decode_parity_nkv4_full_hidden():
+    # 77 heads x 12 k slices at hidden 6144: more GEMV CTAs than are resident
+    # at once, heads spread unevenly over the XCDs
+    wl = _wl("decode", 64, 6144, 4, outlier_frac=0.01)
+    _say(f"decode parity {wl.name}")
+    inp = synth.make_workload(wl, seed=41)
+    ref = oracle.decode(inp)
+    _, got = _gpu(inp)
+    stats = parity.compare(inp, ref, got)
+    parity.check_written_sets(inp, got)
+    _say(f"  {stats}")
+
+
+def test_workspace_shared_across_shapes():
+    # one workspace serves decode and prefill calls of every launch structure
+    # in turn; each call matches the oracle
+    from kv_residual_add_amd import _binding as B
+    from kv_residual_add_amd.runner import Problem
+
+    shapes = [("decode", 64, 1024, 2), ("decode", 8, 1024, 1), ("prefill", 40, 512, 1),
+              ("decode", 20, 4736, 1), ("decode", 4, 256, 1), ("decode", 16, 6144, 1)]
+    probs = []
+    for i, (mode, S, K, nkv) in enumerate(shapes):
+        inp = synth.make_workload(_wl(mode, S, K, nkv), seed=100 + i)
+        ref = oracle.decode(inp) if mode == "decode" else oracle.prefill(inp)
+        probs.append((inp, ref, Problem(inp)))
+    need = max(p.workspace.numel() for _, _, p in probs)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    B.pa_workspace_init(ws)
+    for rnd in range(2):
+        for (mode, S, K, nkv), (inp, ref, p) in zip(shapes, probs):
+            _say(f"shared workspace: round {rnd} {mode} S={S} K={K} nkv={nkv}")
+            for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
+                p.t[k].copy_(torch.from_numpy(inp[k]).to(p.device))
+            p.run(workspace=ws)
+            torch.cuda.synchronize()
+            B.pa_workspace_status(ws)
+            got = p.outputs()
+            parity.compare(inp, ref, got)
+            parity.check_written_sets(inp, got)
+
+
 @pytest.mark.parametrize("key", ["c1", "c2", "c3"])
 def test_decode_parity_full_workloads(key):
     wl = synth.named_config(key)
@@ -207,9 +252,10 @@ def test_prefill_parity_full_workloads_sampled(key):
 # decode shapes for each launch structure: few tokens with a small weight (norm,
 # GEMV and head epilogue in one launch, flags handed over in each XCD's L2), few
 # tokens with a larger weight (norm + GEMV in one launch, epilogue in a second),
-# and more tokens (three launches). Repeated calls must reuse the in-launch
-# flags cleanly.
-REPEAT_CASES = [("decode", 4, 256, 1), ("decode", 8, 1024, 2), ("decode", 24, 1024, 2), ("prefill", 24, 1024, 2)]
+# more tokens (norm, then GEMV + epilogue), and 37 k slices (three launches).
+# Repeated calls must reuse the in-launch flags cleanly.
+REPEAT_CASES = [("decode", 4, 256, 1), ("decode", 8, 1024, 2), ("decode", 24, 1024, 2), ("decode", 20, 4736, 1),
+                ("prefill", 24, 1024, 2)]
 
 
 @pytest.mark.parametrize("mode,S,K,nkv", REPEAT_CASES, ids=lambda v: str(v))
