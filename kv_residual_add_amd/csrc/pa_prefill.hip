@@ -662,9 +662,10 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
 // (workgroups are dispatched round-robin over the eight XCDs), and each XCD
 // takes a list of heads across every token tile, so the CTAs running together
 // re-read those heads' weight panels and the token tiles' activation panels
-// from that XCD's L2. A precise head (bf16 MFMA) costs two FP8 heads; the lists
-// balance that cost (longest first, each to the least loaded XCD) and put the
-// precise heads first, so the longest CTAs of an XCD start earliest.
+// from that XCD's L2. A precise head (bf16 MFMA) costs 2.2 FP8 heads (measured
+// main loop 146 vs 67 us at 256 tokens); the lists balance that cost (longest
+// first, each to the least loaded XCD) and put the precise heads first, so the
+// longest CTAs of an XCD start earliest.
 constexpr int kMaxHeads = 19 * 4 + 1;  // 128-row heads at nkv = 4, the largest nkv accepted
 
 struct HeadMap {
@@ -748,7 +749,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
   // the accumulators at run time)
   auto epilogue = [&](const f32x16 (&accn)[4], int n, int64_t slot, int64_t pos) {
     const EpiIn in = epilogue_loads(a, pos);
-    if (n > 0) __syncthreads();  // the previous tile has been read
+    // Each wave hands its tile over through its own ring slot (every wave is
+    // past its last read of the ring), reading it back in the same instruction
+    // stream: LDS keeps one wave's accesses in order, so no CTA barrier (which
+    // would also wait for the previous tile's global stores).
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -757,7 +762,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
         *reinterpret_cast<f32x4*>(tile + row * kHeadDim + 4 * (c ^ row)) =
             f32x4{accn[m][4 * q], accn[m][4 * q + 1], accn[m][4 * q + 2], accn[m][4 * q + 3]};
       }
-    __syncthreads();
+    asm volatile("" ::: "memory");
     if (n == 0) stamp(a.timeline, a.timeline_slots, b, 3);
     tile_epilogue(a, tr, gam_lds, h, (tt0 + n) * 32 + row, slot, in);
   };
@@ -846,16 +851,16 @@ int prefill_token_tiles_per_wave(int M, int heads, int cus) {
 HeadMap make_head_map(int nkv) {
   const int H = 19 * nkv + 1;
   auto precise = [&](int h) { return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv; };
-  int load[8] = {0}, count[8] = {0};
+  int load[8] = {0}, count[8] = {0};  // in tenths of an FP8 head
   int owner[kMaxHeads];
-  for (int pass = 0; pass < 2; ++pass)  // precise heads (cost 2) first, then FP8 heads (cost 1)
+  for (int pass = 0; pass < 2; ++pass)  // precise heads (cost 22) first, then FP8 heads (cost 10)
     for (int h = 0; h < H; ++h) {
       if (precise(h) != (pass == 0)) continue;
       int best = 0;
       for (int x = 1; x < 8; ++x)
         if (load[x] < load[best] || (load[x] == load[best] && count[x] < count[best])) best = x;
       owner[h] = best;
-      load[best] += precise(h) ? 2 : 1;
+      load[best] += precise(h) ? 22 : 10;
       ++count[best];
     }
   HeadMap m{};
