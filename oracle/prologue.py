@@ -37,10 +37,21 @@ Per token (decode):
 Prefill replaces a3/a4 by MXFP8: per (row, 32-wide k block) an E8M0 scale
 2^(floor(log2 amax) - 8) and E4M3 elements, and the block-scaled dot product.
 
+Two variants of the head step, both optional inputs:
+  static K/V scale  K and V take the unit scale instead of max / 448, and the
+      scale entries hold 1.0 (the pre_attn page's STATIC_KV_SCALE config, in the
+      K and V branches of the head tasks).
+  FP8 q             besides (or instead of) bf16 q, the E4M3 code of the float32
+      product q * inv, inv = float32(1 / q_fp8_scale), saturating at 448 (the
+      epilogue page's q_fp8_out / q_fp8_scale, q branch: x * qfp8_inv cast to
+      e4m3).
+
 Readings where the pages leave a point open (each also listed in the design
 notes): the activation norm and the FP8 decisions that follow it are taken in
 float64; eps is the float32 value the library receives; K and index_k are
-quantized from the unrounded head output; MXFP8 follows the OCP MX rule.
+quantized from the unrounded head output; MXFP8 follows the OCP MX rule; the
+FP8 q code takes the float32 image of the head output times the float32
+reciprocal, rounded once to E4M3.
 """
 
 from __future__ import annotations
@@ -141,13 +152,23 @@ def head_norm_rope(yh, g, cos, sin, eps):
     return o, n
 
 
-def _scaled_codes(v):
-    """Per-row scale max|v| / 448 as float32 (1.0 for an all-zero row) and the
-    E4M3 codes of v / scale (steps a7, a8)."""
+def _scaled_codes(v, static=False):
+    """Per-row scale max|v| / 448 as float32 (1.0 for an all-zero row, and for
+    every row with the static scale) and the E4M3 codes of v / scale (steps a7,
+    a8)."""
+    if static:
+        return e4m3_encode(v), np.ones(v.shape[0], np.float32)
     amax = np.abs(v).max(axis=1)
     s = np.where(amax == 0.0, np.float32(1.0), (amax / E4M3_MAX).astype(np.float32))
     s = s.astype(np.float32)
     return e4m3_encode(v / s.astype(np.float64)[:, None]), s
+
+
+def q_fp8_codes(o_q, q_fp8_scale):
+    """FP8 q: E4M3 of float32(float32(o) * float32(1 / q_fp8_scale))."""
+    inv = np.float32(np.float32(1.0) / np.float32(q_fp8_scale))
+    x = o_q.astype(np.float32) * inv  # one float32 rounding of the product
+    return e4m3_encode(x.astype(np.float64))
 
 
 def _epilogue(y, inp):
@@ -180,8 +201,11 @@ def _epilogue(y, inp):
         "q_out": f32_to_bf16_bits(o_q.astype(np.float32)),
         "iq_out": f32_to_bf16_bits(o_iq.astype(np.float32)),
     }
-    k_codes, k_s = _scaled_codes(o_k.reshape(S * nkv, HEAD_DIM))
-    v_codes, v_s = _scaled_codes(y_v.reshape(S * nkv, HEAD_DIM))
+    if inp.get("q_fp8_scale") is not None:
+        out["q_fp8"] = q_fp8_codes(o_q, inp["q_fp8_scale"])
+    static = bool(inp.get("static_kv_scale", False))
+    k_codes, k_s = _scaled_codes(o_k.reshape(S * nkv, HEAD_DIM), static)
+    v_codes, v_s = _scaled_codes(y_v.reshape(S * nkv, HEAD_DIM), static)
     k_codes = k_codes.reshape(S, nkv, HEAD_DIM)
     v_codes = v_codes.reshape(S, nkv, HEAD_DIM)
     k_s = k_s.reshape(S, nkv)

@@ -97,7 +97,15 @@ def run(inp, mode: str):
     """The prologue on a tiny input dict (same keys as synth workloads).
 
     Returns a dict with h_out, q_out, iq_out (nested lists of bf16 bits) and the
-    final caches as flat Python lists / dicts of written bytes."""
+    final caches as flat Python lists / dicts of written bytes. Optional inputs:
+    static_kv_scale (K and V with the unit scale, the pre_attn page's
+    STATIC_KV_SCALE) and q_fp8_scale (adds q_fp8: E4M3 codes of the float32
+    product of q and the float32 reciprocal of the scale, the epilogue page's
+    q_fp8_out)."""
+    static = bool(inp.get("static_kv_scale", False))
+    qs = inp.get("q_fp8_scale")
+    q_inv = None if qs is None else f32(1.0 / f32(float(qs)))
+    q_fp8 = []
     S, K = inp["ar"].shape
     nkv = int(inp["nkv"])
     eps = float(inp["eps"])
@@ -159,8 +167,11 @@ def run(inp, mode: str):
                 o[i + 32] = n_[i + 32] * cos[i] + n_[i] * sin[i]
             return o
 
-        q_out.append([[bf16_round_bits(f32(v)) for v in head(h, "g_q")]
-                      for h in range(16 * nkv)])
+        q_heads = [head(h, "g_q") for h in range(16 * nkv)]
+        q_out.append([[bf16_round_bits(f32(v)) for v in o] for o in q_heads])
+        if q_inv is not None:
+            # product of two float32 values: exact in a double, then one rounding
+            q_fp8.append([[e4m3_round(f32(f32(v) * q_inv)) for v in o] for o in q_heads])
         iq_out.append([[bf16_round_bits(f32(v)) for v in head(18 * nkv + j, "g_iq")]
                        for j in range(nkv)])
         slot = int(inp["slot_mapping"][s])
@@ -169,9 +180,9 @@ def run(inp, mode: str):
         page, t = slot // 16, slot % 16
         for j in range(nkv):
             ok = head(16 * nkv + j, "g_k")
-            ks = _scale(ok)
             yv = y[(17 * nkv + j) * HEAD_DIM:(17 * nkv + j + 1) * HEAD_DIM]
-            vs = _scale(yv)
+            ks = 1.0 if static else _scale(ok)
+            vs = 1.0 if static else _scale(yv)
             writes[("k_scale", (page * nkv + j) * 16 + t)] = ks
             writes[("v_scale", (page * nkv + j) * 16 + t)] = vs
             base = (page * nkv + j) * 2048
@@ -183,4 +194,4 @@ def run(inp, mode: str):
         oik = head(19 * nkv, "g_ik")
         for d in range(HEAD_DIM):
             writes[("index_cache", slot * HEAD_DIM + d)] = e4m3_round(oik[d])
-    return {"h_out": h_out, "q_out": q_out, "iq_out": iq_out, "writes": writes}
+    return {"h_out": h_out, "q_out": q_out, "iq_out": iq_out, "q_fp8": q_fp8, "writes": writes}

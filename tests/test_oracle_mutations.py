@@ -76,7 +76,22 @@ def _skip_mx_sat(xn):
     return codecs.e4m3_encode(blk / X[:, :, None]).reshape(M, K), code.astype(np.uint8)
 
 
+def _q_inv_f64(o_q, q_fp8_scale):
+    x = o_q.astype(np.float32).astype(np.float64) / float(q_fp8_scale)  # true quotient, no float32 product
+    return codecs.e4m3_encode(x)
+
+
+def _q_no_inverse(o_q, q_fp8_scale):
+    x = o_q.astype(np.float32) * np.float32(q_fp8_scale)  # multiplied by the scale itself
+    return codecs.e4m3_encode(x.astype(np.float64))
+
+
+def _static_v_dynamic(v, static=False):
+    return _orig["_scaled_codes"](v, False)  # the static flag ignored
+
+
 _orig = {
+    "_scaled_codes": prologue._scaled_codes,
     "head_norm_rope": prologue.head_norm_rope,
     "input_norm": prologue.input_norm,
     "quantize_per_token": prologue.quantize_per_token,
@@ -92,6 +107,9 @@ CASES = {
     "e4m3_ties_away": ("e4m3_encode", _ties_away),
     "mx_scale_ceil": ("mxfp8_quantize", _mx_ceil),
     "mx_emax_7": ("mxfp8_quantize", _skip_mx_sat),
+    "q_fp8_float64_quotient": ("q_fp8_codes", _q_inv_f64),
+    "q_fp8_times_scale": ("q_fp8_codes", _q_no_inverse),
+    "static_scale_ignored": ("_scaled_codes", _static_v_dynamic),
 }
 
 PINS = [
@@ -102,6 +120,9 @@ PINS = [
     pins_codecs.test_e4m3_encode_equals_bruteforce_nearest_even,
     pins.test_decode_matches_scalar_bruteforce,
     pins.test_prefill_matches_scalar_bruteforce,
+    pins.test_static_scale_equals_dynamic_at_full_scale_rows,
+    pins.test_q_fp8_codes_equal_bruteforce_near_midpoints,
+    lambda: pins.test_variants_match_scalar_bruteforce("decode"),
 ]
 
 
@@ -120,7 +141,7 @@ def test_planted_mistake_is_caught(case, monkeypatch):
         try:
             pin()
         except AssertionError:
-            failed.append(pin.__name__)
+            failed.append(getattr(pin, "__name__", "pin"))
             break
     assert failed, f"no pin caught the planted mistake {case!r}"
 

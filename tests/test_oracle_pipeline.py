@@ -281,6 +281,80 @@ def test_prefill_matches_scalar_bruteforce():
     _check_against_brute(inp, oracle.prefill(inp), "prefill")
 
 
+# ------------------------------------------------- variants of the head step
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_variants_match_scalar_bruteforce(mode):
+    # the unit K/V scale and the scaled FP8 q, against the separately written
+    # scalar statement (a scale that is not a power of two, so the float32
+    # reciprocal rounds)
+    wl = TINY_DECODE if mode == "decode" else TINY_PREFILL
+    inp = dict(synth.make_workload(wl, seed=21), static_kv_scale=True, q_fp8_scale=0.0371)
+    out = oracle.decode(inp) if mode == "decode" else oracle.prefill(inp)
+    _check_against_brute(inp, out, mode)
+    b = brute.run(inp, mode)
+    want = np.array(b["q_fp8"], np.uint8)
+    got = out["q_fp8"]
+    assert got.shape == want.shape
+    # equal, or one code apart where float64 head sums round differently
+    d = np.abs(codecs_ord(got) - codecs_ord(want))
+    assert d.max() <= 1 and (d > 0).mean() < 0.01
+
+
+def codecs_ord(c):
+    c = c.astype(np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def test_static_scale_equals_dynamic_at_full_scale_rows():
+    # a row whose max magnitude is exactly 448 has the dynamic scale 448 / 448
+    # = 1, so its codes are the static ones; other rows saturate or not by the
+    # static rule (|v| >= 464 -> 0x7E)
+    rng = np.random.default_rng(5)
+    v = rng.normal(0, 100, (6, 128))
+    v[:3] *= 448.0 / np.abs(v[:3]).max(axis=1, keepdims=True)
+    c_dyn, s_dyn = prologue._scaled_codes(v[:3])
+    c_sta, s_sta = prologue._scaled_codes(v[:3], static=True)
+    assert np.all(s_dyn == 1.0) and np.all(s_sta == 1.0)
+    assert np.array_equal(c_dyn, c_sta)
+    big = np.array([[500.0, -464.0, 463.9, -1e6] + [0.0] * 124])
+    c, s = prologue._scaled_codes(big, static=True)
+    assert s[0] == 1.0 and list(c[0, :4]) == [0x7E, 0xFE, 0x7E, 0xFE]
+
+
+def test_q_fp8_codes_equal_bruteforce_near_midpoints():
+    # float32 head outputs within two ulps of (E4M3 midpoint) * scale, where the
+    # float32 product with the float32 reciprocal decides the rounding: the
+    # codes equal the scalar statement's (exhaustive search, exact rationals)
+    scale = 0.0371
+    inv = brute.f32(1.0 / brute.f32(scale))
+    tab = codecs.e4m3_decode_table()
+    grid = np.sort(tab[:127])
+    mids = (grid[:-1] + grid[1:]) / 2
+    base = (mids * np.float64(np.float32(scale))).astype(np.float32)
+    xs = np.concatenate([base + k * np.spacing(base) for k in (-2, -1, 0, 1, 2)]).astype(np.float32)
+    xs = np.concatenate([xs, -xs])
+    got = prologue.q_fp8_codes(xs.astype(np.float64), scale)
+    want = np.array([brute.e4m3_round(brute.f32(float(x) * inv)) for x in xs], np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_q_fp8_dequant_within_half_step():
+    # code * scale is within half an E4M3 step (times the scale) of the float32
+    # head output, below saturation; above it the code is +-448
+    rng = np.random.default_rng(6)
+    o = rng.normal(0, 3, (4, 2, 128)) * np.exp(rng.normal(0, 2, (4, 2, 128)))
+    scale = 0.013
+    c = oracle.prologue.q_fp8_codes(o, scale)
+    x = o.astype(np.float32).astype(np.float64) / np.float64(np.float32(scale))
+    dq = oracle.e4m3_decode(c)
+    mag = np.abs(x)
+    step = np.where(mag < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3))
+    inside = mag <= 448
+    # the float32 rounding of the product moves x by at most 2^-24 relative
+    assert np.all(np.abs(dq - x)[inside] <= 0.5 * step[inside] + mag[inside] * 2.0 ** -23)
+    assert np.all(np.abs(dq[~inside]) == 448.0)
+
+
 def test_head_order_roles():
     # N = (19 nkv + 1) * 128 and the role offsets of the head list
     for nkv, n in ((1, 2560), (2, 4992), (4, 9856)):
