@@ -135,7 +135,7 @@ def cpu_baseline(wl, inp, budget_s: float):
         t0 = time.perf_counter()
         fn(sub)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+        if time.perf_counter() - t_start > budget_s or len(times) >= 1000:
             break
     t = float(np.median(times))
     N = (19 * wl.nkv + 1) * 128

@@ -90,7 +90,9 @@ typedef enum pa_status {
   PA_ERR_HIP = -8,       /* a HIP runtime call or launch failed */
   PA_ERR_DEVICE = -9,    /* the current device is not a gfx950 GPU */
   PA_ERR_MODE = -10,     /* unknown mode argument */
-  PA_ERR_SYNC = -11      /* a kernel's bounded wait for another CTA gave up */
+  PA_ERR_SYNC = -11,     /* a kernel's bounded wait for another CTA gave up */
+  PA_ERR_OPTIONS = -12   /* pa_head_options: q_fp8_scale not finite and > 0, or its
+                            float32 reciprocal not finite */
 } pa_status;
 
 /* Problem size of one call. */
@@ -182,6 +184,53 @@ int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* re
                      uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
                      uint8_t* index_cache, uint16_t* q_out, uint16_t* iq_out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Variants of the head step, for pre_attn_decode_ex / pre_attn_prefill_ex.
+ * A NULL options pointer, or all fields zero, gives the plain calls' results.
+ *
+ * static_kv_scale  nonzero: K and V take the unit scale instead of the
+ *     per-token max / 448: their codes are E4M3 (saturating) of the values
+ *     themselves, and every k_scale / v_scale entry the call writes is 1.0.
+ *     Source: the pre_attn page's STATIC_KV_SCALE config, read in the K and V
+ *     branches of the head tasks of emit_pre_attn.
+ * q_fp8_out        NULL, or an extra q output: uint8 E4M3 codes
+ *     [tokens][16 nkv][128] (16-byte aligned, caller-owned, written in full):
+ *     code = E4M3(float32(q) * float32(1 / q_fp8_scale)), one float32
+ *     rounding of the product, saturating at +-448, where q is the normed and
+ *     roped head before its bf16 rounding. Source: the epilogue page's
+ *     q_fp8_out / q_fp8_scale (the q branch of the per-role epilogue and the
+ *     argument list of minimax_m3_qkv_index_fused_epilogue).
+ * q_fp8_scale      the dequantization scale of q_fp8_out; with q_fp8_out set it
+ *     must be finite and > 0 with a finite float32 reciprocal (else
+ *     PA_ERR_OPTIONS). Ignored when q_fp8_out is NULL. */
+typedef struct pa_head_options {
+  int32_t static_kv_scale;
+  float q_fp8_scale;
+  uint8_t* q_fp8_out;
+} pa_head_options;
+
+/* pre_attn_decode with head-step options. Same arguments and results, except:
+ * with opts->q_fp8_out set, q_out may be NULL (then only the FP8 q is
+ * written; the epilogue page requires at least one of the two q outputs),
+ * and K / V follow opts->static_kv_scale. */
+int pre_attn_decode_ex(const pa_dims* dims, const pa_head_options* opts, const uint16_t* ar,
+                       const uint16_t* res, uint16_t* h_out, const uint16_t* g_in,
+                       const uint8_t* w_packed, const float* w_scale, const uint16_t* g_q,
+                       const uint16_t* g_k, const uint16_t* g_iq, const uint16_t* g_ik,
+                       const uint16_t* cos_sin, const int64_t* positions,
+                       const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                       float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
+                       uint16_t* iq_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pre_attn_prefill with head-step options, as pre_attn_decode_ex. */
+int pre_attn_prefill_ex(const pa_dims* dims, const pa_head_options* opts, const uint16_t* ar,
+                        const uint16_t* res, uint16_t* h_out, const uint16_t* g_in,
+                        const uint8_t* w_packed, const uint8_t* s_packed, const uint16_t* g_q,
+                        const uint16_t* g_k, const uint16_t* g_iq, const uint16_t* g_ik,
+                        const uint16_t* cos_sin, const int64_t* positions,
+                        const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                        float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
+                        uint16_t* iq_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Instrumentation: from now on, calls on this host thread record `start` and
  * `stop` (hipEvent_t, created by the caller) on their stream immediately

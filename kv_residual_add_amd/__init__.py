@@ -9,8 +9,10 @@ from ._binding import (  # noqa: F401
     DECODE_MAX_TOKENS,
     EXPORTS,
     LIB_PATH,
+    HeadOptions,
     PA_DECODE_EPILOGUE_FUSED,
     PA_DECODE_NORM_FUSED,
+    PA_ERR_OPTIONS,
     PA_ERR_SYNC,
     PA_MODE_DECODE,
     PA_MODE_PREFILL,
@@ -18,6 +20,7 @@ from ._binding import (  # noqa: F401
     load,
     make_dims,
     pa_dims,
+    pa_head_options,
     pa_pack_weight_decode,
     pa_pack_weight_prefill,
     pa_set_kernel_events,
@@ -30,6 +33,8 @@ from ._binding import (  # noqa: F401
     pa_workspace_status,
     pre_attn_decode,
     pre_attn_prefill,
+    pre_attn_decode_ex,
+    pre_attn_prefill_ex,
 )
 
 load()

@@ -25,6 +25,7 @@ DECODE_MAX_TOKENS = 64
 PA_DECODE_NORM_FUSED = 1
 PA_DECODE_EPILOGUE_FUSED = 2
 PA_ERR_SYNC = -11
+PA_ERR_OPTIONS = -12
 
 EXPORTS = (
     "pa_workspace_bytes",
@@ -37,6 +38,8 @@ EXPORTS = (
     "pa_pack_weight_prefill",
     "pre_attn_decode",
     "pre_attn_prefill",
+    "pre_attn_decode_ex",
+    "pre_attn_prefill_ex",
     "pa_set_kernel_events",
     "pa_set_timeline",
     "pa_strerror",
@@ -53,6 +56,25 @@ class pa_dims(ctypes.Structure):
         ("max_pos", ctypes.c_int32),
         ("eps", ctypes.c_float),
     ]
+
+
+class pa_head_options(ctypes.Structure):
+    _fields_ = [
+        ("static_kv_scale", ctypes.c_int32),
+        ("q_fp8_scale", ctypes.c_float),
+        ("q_fp8_out", ctypes.c_void_p),
+    ]
+
+
+class HeadOptions:
+    """Head-step variants of pre_attn_decode_ex / pre_attn_prefill_ex:
+    static_kv_scale (unit K / V scales) and an optional FP8 q output
+    q_fp8_out (uint8 [tokens, 16 nkv, 128]) with its dequantization scale."""
+
+    def __init__(self, static_kv_scale: bool = False, q_fp8_out=None, q_fp8_scale: float = 1.0):
+        self.static_kv_scale = bool(static_kv_scale)
+        self.q_fp8_out = q_fp8_out
+        self.q_fp8_scale = float(q_fp8_scale)
 
 
 class PaError(RuntimeError):
@@ -100,6 +122,11 @@ def load() -> ctypes.CDLL:
         lib.pre_attn_decode.restype = ctypes.c_int
         lib.pre_attn_prefill.argtypes = [dims_p] + [P] * 21 + [sz, P]
         lib.pre_attn_prefill.restype = ctypes.c_int
+        opts_p = ctypes.POINTER(pa_head_options)
+        lib.pre_attn_decode_ex.argtypes = [dims_p, opts_p] + [P] * 21 + [sz, P]
+        lib.pre_attn_decode_ex.restype = ctypes.c_int
+        lib.pre_attn_prefill_ex.argtypes = [dims_p, opts_p] + [P] * 21 + [sz, P]
+        lib.pre_attn_prefill_ex.restype = ctypes.c_int
         lib.pa_set_timeline.argtypes = [P, sz]
         lib.pa_set_timeline.restype = ctypes.c_int
         lib.pa_set_kernel_events.argtypes = [P, P]
@@ -225,16 +252,25 @@ def pa_pack_weight_prefill(w: torch.Tensor, w_e8m0: torch.Tensor, w_packed: torc
 
 def _run(fn_name: str, mode: int, dims: pa_dims, ar, res, h_out, g_in, w_packed, w_scales,
          g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
-         v_scale, index_cache, q_out, iq_out, workspace, stream):
+         v_scale, index_cache, q_out, iq_out, workspace, stream, opts=None):
     S, K, nkv = dims.tokens, dims.hidden, dims.nkv
     P, L = dims.num_pages, dims.max_pos
     N = (19 * nkv + 1) * HEAD_DIM
     dev = ar.device
     bf, u8, f32, i64 = torch.bfloat16, torch.uint8, torch.float32, torch.int64
+    lead = [ctypes.byref(dims)]
+    if fn_name.endswith("_ex"):
+        c_opts = None
+        if opts is not None:
+            qf = opts.q_fp8_out
+            c_opts = pa_head_options(
+                int(opts.static_kv_scale), opts.q_fp8_scale,
+                None if qf is None else _ptr(qf, "q_fp8_out", u8, S * 16 * nkv * HEAD_DIM, dev))
+        lead.append(None if c_opts is None else ctypes.byref(c_opts))
     ws_need = pa_workspace_bytes(dims, mode)
     if ws_need == 0:
         # let the library name the invalid dimension
-        _check(getattr(load(), fn_name)(ctypes.byref(dims), *([None] * 21), 0, None), fn_name)
+        _check(getattr(load(), fn_name)(*lead, *([None] * 21), 0, None), fn_name)
     if workspace.numel() < ws_need:
         raise ValueError(f"workspace: need {ws_need} bytes, got {workspace.numel()}")
     if mode == PA_MODE_DECODE:
@@ -255,13 +291,13 @@ def _run(fn_name: str, mode: int, dims: pa_dims, ar, res, h_out, g_in, w_packed,
         _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
         _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
         _ptr(index_cache, "index_cache", u8, P * PAGE * HEAD_DIM, dev),
-        _ptr(q_out, "q_out", bf, S * 16 * nkv * HEAD_DIM, dev),
+        None if q_out is None else _ptr(q_out, "q_out", bf, S * 16 * nkv * HEAD_DIM, dev),
         _ptr(iq_out, "iq_out", bf, S * nkv * HEAD_DIM, dev),
         workspace.data_ptr(),
     ]
     if workspace.dtype != u8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    st = getattr(load(), fn_name)(ctypes.byref(dims), *args, workspace.numel(), _stream(stream))
+    st = getattr(load(), fn_name)(*lead, *args, workspace.numel(), _stream(stream))
     _check(st, fn_name)
 
 
@@ -281,3 +317,22 @@ def pre_attn_prefill(dims, ar, res, h_out, g_in, w_packed, s_packed, g_q, g_k, g
     _run("pre_attn_prefill", PA_MODE_PREFILL, dims, ar, res, h_out, g_in, w_packed, s_packed,
          g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
          v_scale, index_cache, q_out, iq_out, workspace, stream)
+
+
+def pre_attn_decode_ex(dims, opts, ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik,
+                       cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                       index_cache, q_out, iq_out, workspace, stream=None) -> None:
+    """Decode prologue with head-step options (a HeadOptions or None); q_out may
+    be None when opts.q_fp8_out is set. As in include/pre_attn.h."""
+    _run("pre_attn_decode_ex", PA_MODE_DECODE, dims, ar, res, h_out, g_in, w_packed, w_scale,
+         g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+         v_scale, index_cache, q_out, iq_out, workspace, stream, opts)
+
+
+def pre_attn_prefill_ex(dims, opts, ar, res, h_out, g_in, w_packed, s_packed, g_q, g_k, g_iq,
+                        g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+                        v_scale, index_cache, q_out, iq_out, workspace, stream=None) -> None:
+    """Prefill prologue with head-step options, as pre_attn_decode_ex."""
+    _run("pre_attn_prefill_ex", PA_MODE_PREFILL, dims, ar, res, h_out, g_in, w_packed, s_packed,
+         g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
+         v_scale, index_cache, q_out, iq_out, workspace, stream, opts)

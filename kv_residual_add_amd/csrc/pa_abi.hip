@@ -78,12 +78,36 @@ struct Ptrs {
   void* ws;
 };
 
-int check_ptrs(const Ptrs& p) {
+// The head-step variants of the _ex entry points (defaults: per-token K / V
+// scales, bf16 q only).
+struct Opts {
+  uint8_t* q_fp8 = nullptr;
+  float q_fp8_inv = 1.0f;
+  int static_kv = 0;
+};
+
+int check_opts(const pa_head_options* o, Opts& out) {
+  if (!o) return PA_OK;
+  out.static_kv = o->static_kv_scale != 0;
+  out.q_fp8 = o->q_fp8_out;
+  if (out.q_fp8) {
+    if (!aligned(out.q_fp8, 16)) return PA_ERR_ALIGN;
+    if (!std::isfinite(o->q_fp8_scale) || !(o->q_fp8_scale > 0.0f)) return PA_ERR_OPTIONS;
+    const volatile float one = 1.0f;  // the correctly rounded float32 reciprocal
+    out.q_fp8_inv = one / o->q_fp8_scale;
+    if (!std::isfinite(out.q_fp8_inv)) return PA_ERR_OPTIONS;
+  }
+  return PA_OK;
+}
+
+// q_out may be NULL only when the FP8 q output is requested.
+int check_ptrs(const Ptrs& p, bool has_q_fp8) {
   const void* all[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.w_scales, p.g_q, p.g_k,
                        p.g_iq, p.g_ik, p.cos_sin, p.positions, p.slot_mapping, p.k_cache,
-                       p.v_cache, p.k_scale, p.v_scale, p.index_cache, p.q_out, p.iq_out, p.ws};
+                       p.v_cache, p.k_scale, p.v_scale, p.index_cache, p.iq_out, p.ws};
   for (const void* q : all)
     if (!q) return PA_ERR_NULL;
+  if (!p.q_out && !has_q_fp8) return PA_ERR_NULL;
   const void* a16[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.q_out, p.iq_out, p.g_q, p.g_k,
                        p.g_iq, p.g_ik, p.cos_sin, p.k_cache, p.v_cache, p.index_cache, p.ws};
   for (const void* q : a16)
@@ -133,15 +157,22 @@ pa::Args make_args(const pa_dims* d, const Ptrs& p, void* stream) {
   return a;
 }
 
-int run(int mode, const pa_dims* dims, const Ptrs& p, size_t ws_bytes, void* stream) {
+int run(int mode, const pa_dims* dims, const Ptrs& p, const pa_head_options* opts, size_t ws_bytes,
+        void* stream) {
   int st = check_dims(dims, mode);
   if (st) return st;
-  st = check_ptrs(p);
+  Opts o;
+  st = check_opts(opts, o);
+  if (st) return st;
+  st = check_ptrs(p, o.q_fp8 != nullptr);
   if (st) return st;
   if (ws_bytes < workspace_for(dims, mode)) return PA_ERR_WORKSPACE;
   st = check_device();
   if (st) return st;
   pa::Args a = make_args(dims, p, stream);
+  a.q_fp8 = o.q_fp8;
+  a.q_fp8_inv = o.q_fp8_inv;
+  a.static_kv = o.static_kv;
   hipError_t e;
   if (mode == PA_MODE_DECODE) {
     a.w_scale = static_cast<const float*>(p.w_scales);
@@ -251,7 +282,21 @@ int pre_attn_decode(const pa_dims* dims, const uint16_t* ar, const uint16_t* res
   const Ptrs p{ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik, cos_sin,
                positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
                q_out, iq_out, workspace};
-  return run(PA_MODE_DECODE, dims, p, workspace_bytes, stream);
+  return run(PA_MODE_DECODE, dims, p, nullptr, workspace_bytes, stream);
+}
+
+int pre_attn_decode_ex(const pa_dims* dims, const pa_head_options* opts, const uint16_t* ar,
+                       const uint16_t* res, uint16_t* h_out, const uint16_t* g_in,
+                       const uint8_t* w_packed, const float* w_scale, const uint16_t* g_q,
+                       const uint16_t* g_k, const uint16_t* g_iq, const uint16_t* g_ik,
+                       const uint16_t* cos_sin, const int64_t* positions,
+                       const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                       float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
+                       uint16_t* iq_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const Ptrs p{ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik, cos_sin,
+               positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
+               q_out, iq_out, workspace};
+  return run(PA_MODE_DECODE, dims, p, opts, workspace_bytes, stream);
 }
 
 int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* res,
@@ -265,7 +310,21 @@ int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* re
   const Ptrs p{ar, res, h_out, g_in, w_packed, s_packed, g_q, g_k, g_iq, g_ik, cos_sin,
                positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
                q_out, iq_out, workspace};
-  return run(PA_MODE_PREFILL, dims, p, workspace_bytes, stream);
+  return run(PA_MODE_PREFILL, dims, p, nullptr, workspace_bytes, stream);
+}
+
+int pre_attn_prefill_ex(const pa_dims* dims, const pa_head_options* opts, const uint16_t* ar,
+                        const uint16_t* res, uint16_t* h_out, const uint16_t* g_in,
+                        const uint8_t* w_packed, const uint8_t* s_packed, const uint16_t* g_q,
+                        const uint16_t* g_k, const uint16_t* g_iq, const uint16_t* g_ik,
+                        const uint16_t* cos_sin, const int64_t* positions,
+                        const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                        float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
+                        uint16_t* iq_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const Ptrs p{ar, res, h_out, g_in, w_packed, s_packed, g_q, g_k, g_iq, g_ik, cos_sin,
+               positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
+               q_out, iq_out, workspace};
+  return run(PA_MODE_PREFILL, dims, p, opts, workspace_bytes, stream);
 }
 
 const char* pa_strerror(int status) {
@@ -282,6 +341,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case PA_ERR_MODE: return "unknown mode";
     case PA_ERR_SYNC: return "a kernel's bounded wait gave up: that call's outputs are not valid";
+    case PA_ERR_OPTIONS: return "q_fp8_scale must be finite and > 0, with a finite float32 reciprocal";
     default: return "unknown status";
   }
 }

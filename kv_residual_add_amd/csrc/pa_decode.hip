@@ -468,9 +468,9 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
 
-  if (h >= v0 && h < iq0) {  // V: the raw projection, per-token scale
+  if (h >= v0 && h < iq0) {  // V: the raw projection, per-token scale (1 when static)
     const int j = h - v0;
-    const double amax = wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
+    const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
@@ -494,12 +494,21 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   const double o1 = nm1;
 
   if (h < k0) {
-    uint16_t* q = a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim;
-    q[d0] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o0)));
-    q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
-  } else if (h < v0) {  // K: per-token scale, shuffled page-16 layout
+    const size_t qrow = (static_cast<size_t>(tok) * k0 + h) * kHeadDim;
+    if (a.q_out != nullptr) {
+      uint16_t* q = a.q_out + qrow;
+      q[d0] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o0)));
+      q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
+    }
+    if (a.q_fp8 != nullptr) {  // E4M3 of the float32 product q * (1 / q_fp8_scale)
+      const float p0 = static_cast<float>(o0) * a.q_fp8_inv, p1 = static_cast<float>(o1) * a.q_fp8_inv;
+      const uint32_t c2 = e4m3x2_scaled(static_cast<double>(p0), static_cast<double>(p1), fp8_scale(0));
+      a.q_fp8[qrow + d0] = static_cast<uint8_t>(c2);
+      a.q_fp8[qrow + d1] = static_cast<uint8_t>(c2 >> 8);
+    }
+  } else if (h < v0) {  // K: per-token scale (1 when static), shuffled page-16 layout
     const int j = h - k0;
-    const double amax = wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
+    const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;

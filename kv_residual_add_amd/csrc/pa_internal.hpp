@@ -24,7 +24,10 @@ struct Args {
   const int64_t *positions, *slot_mapping;
   uint8_t *k_cache, *v_cache, *index_cache;
   float *k_scale, *v_scale;
-  uint16_t *q_out, *iq_out;
+  uint16_t *q_out, *iq_out;      // q_out may be NULL when q_fp8 is set
+  uint8_t* q_fp8;                // optional E4M3 q [S][16 nkv][128]
+  float q_fp8_inv;               // float32(1 / q_fp8_scale)
+  int static_kv;                 // nonzero: unit K / V scales
   uint8_t* ws;
   hipStream_t stream;
   hipEvent_t ev_start, ev_stop;  // optional, around the dominant kernel

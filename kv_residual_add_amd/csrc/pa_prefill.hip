@@ -480,14 +480,16 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
 
-  if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale
+  if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale (1 when static)
     const int j = h - v0;
     float am = 0.f;
+    if (!a.static_kv) {
 #pragma unroll 4
-    for (int i = 0; i < 64; i += 4) {
-      const float4 v = x.chunk(c0 + (i >> 2));
-      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                                               __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+      for (int i = 0; i < 64; i += 4) {
+        const float4 v = x.chunk(c0 + (i >> 2));
+        am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                                                 __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+      }
     }
     double amax = static_cast<double>(am);  // a maximum of magnitudes is exact in f32
     amax = __builtin_fmax(amax, __shfl_xor(amax, 32, 64));
@@ -525,6 +527,8 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
     ssf += __shfl_xor(ssf, 32, 64);
     const float rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
     u32x4 o1[4], o2[4];  // bf16 dims i .. i + 7 and i + 32 .. i + 39 for i = 0, 8, 16, 24
+    uint32_t f8a[8], f8b[8];  // E4M3 q of the lane's dims 0 .. 31 and 32 .. 63 (when requested)
+    const bool fp8_row = h < k0 && live && a.q_fp8 != nullptr;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {  // dims i .. i + 7 and their partners i + 32 .. i + 39
       const float4 p0 = x.chunk(c0 + (i >> 2)), p1 = x.chunk(c0 + (i >> 2) + 1);
@@ -542,11 +546,30 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
         v1[e] = x1 * c - x2 * sn;
         v2[e] = x2 * c + x1 * sn;
       }
+      if (fp8_row) {  // E4M3 of the float32 products q * (1 / q_fp8_scale)
+        const float inv = a.q_fp8_inv;
+        const Fp8Scale unit = fp8_scale(0);
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          f8a[(i >> 2) + (e >> 2)] = e4m3x4_scaled(v1[e] * inv, v1[e + 1] * inv, v1[e + 2] * inv, v1[e + 3] * inv, unit);
+          f8b[(i >> 2) + (e >> 2)] = e4m3x4_scaled(v2[e] * inv, v2[e + 1] * inv, v2[e + 2] * inv, v2[e + 3] * inv, unit);
+        }
+      }
       o1[i >> 3] = u32x4{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
                          pack_bf16x2(v1[6], v1[7])};
       o2[i >> 3] = u32x4{pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]), pack_bf16x2(v2[4], v2[5]),
                          pack_bf16x2(v2[6], v2[7])};
     }
+    if (fp8_row) {  // the lane's 64 contiguous codes of the token's 128-byte q row
+      uint8_t* qf = a.q_fp8 + (static_cast<size_t>(tok) * k0 + h) * kHeadDim + dbase;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        *reinterpret_cast<u32x4*>(qf + 16 * j) = u32x4{f8a[4 * j], f8a[4 * j + 1], f8a[4 * j + 2], f8a[4 * j + 3]};
+        *reinterpret_cast<u32x4*>(qf + 32 + 16 * j) =
+            u32x4{f8b[4 * j], f8b[4 * j + 1], f8b[4 * j + 2], f8b[4 * j + 3]};
+      }
+    }
+    if (h < k0 && a.q_out == nullptr) return;  // FP8 q only
     // The wave's reads of its tile are done (one instruction stream, LDS in
     // order): the token's bf16 row goes into the first 256 bytes of its f32 row,
     // then the wave stores whole rows, 16 lanes (256 contiguous bytes) a row
@@ -595,7 +618,13 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   uint8_t* cbase = nullptr;
   int cstride = 0;  // bytes between 16-dim groups of the code row
   double sd = 1.0, rcp = 1.0;
-  if (h < v0) {
+  if (h < v0 && a.static_kv) {  // K with the unit scale: codes of the values themselves
+    if (!store_cache) return;
+    if (lane < 32) a.k_scale[(page * nkv + (h - k0)) * kPage + t] = 1.0f;
+    mode = kCodes;
+    cbase = a.k_cache + (page * nkv + (h - k0)) * kPageBytes + t * 16 + (dbase >> 4) * 256;
+    cstride = 256;
+  } else if (h < v0) {
     mode = kAmax;
     cbase = a.k_cache + (page * nkv + (h - k0)) * kPageBytes + t * 16 + (dbase >> 4) * 256;
     cstride = 256;
@@ -610,7 +639,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
 #pragma unroll
       for (int e = 0; e < 4; ++e) amax = __builtin_fmax(amax, __builtin_fabs(v[e]));
     } else {
-      // index_k keeps sd = rcp = 1, where div_rn returns v unchanged
+      // index_k and K with the unit scale keep sd = rcp = 1, where div_rn returns v unchanged
       const uint32_t w = e4m3x4_scaled(div_rn(v[0], sd, rcp), div_rn(v[1], sd, rcp), div_rn(v[2], sd, rcp),
                                        div_rn(v[3], sd, rcp), fp8_scale(0));
       *reinterpret_cast<uint32_t*>(cbase + (i >> 4) * cstride + (i & 15)) = w;

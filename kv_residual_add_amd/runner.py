@@ -44,6 +44,19 @@ class Problem:
         t["h_out"] = torch.empty((S, K), dtype=torch.bfloat16, device=dev)
         t["q_out"] = torch.empty((S, 16 * self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
         t["iq_out"] = torch.empty((S, self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        # head-step variants (the _ex entry points): inputs "static_kv_scale",
+        # "q_fp8_scale" (adds the FP8 q output) and "q_bf16" (False: no bf16 q)
+        self.opts = None
+        qs = arrays.get("q_fp8_scale")
+        if arrays.get("static_kv_scale", False) or qs is not None:
+            qf = None
+            if qs is not None:
+                qf = torch.empty((S, 16 * self.nkv, B.HEAD_DIM), dtype=torch.uint8, device=dev)
+                t["q_fp8"] = qf
+            self.opts = B.HeadOptions(bool(arrays.get("static_kv_scale", False)), qf,
+                                      1.0 if qs is None else float(qs))
+        if not arrays.get("q_bf16", True):
+            t["q_out"] = None
         self.t = t
         self.set_weight(arrays)
         nbytes = B.pa_workspace_bytes(self.dims, self.mode)
@@ -75,8 +88,13 @@ class Problem:
                 t["index_cache"], t["q_out"], t["iq_out"], self.workspace if workspace is None else workspace)
 
     def run(self, stream=None, **over) -> None:
-        fn = B.pre_attn_decode if self.mode == B.PA_MODE_DECODE else B.pre_attn_prefill
-        fn(*self.args(**over), stream=stream)
+        if self.opts is None:
+            fn = B.pre_attn_decode if self.mode == B.PA_MODE_DECODE else B.pre_attn_prefill
+            fn(*self.args(**over), stream=stream)
+        else:
+            fn = B.pre_attn_decode_ex if self.mode == B.PA_MODE_DECODE else B.pre_attn_prefill_ex
+            a = self.args(**over)
+            fn(a[0], self.opts, *a[1:], stream=stream)
 
     def outputs(self) -> dict:
         """Outputs and caches as numpy raw bits (synchronizes). Raises if an
@@ -85,7 +103,10 @@ class Problem:
         B.pa_workspace_status(self.workspace)
         out = {}
         for k in ("h_out", "q_out", "iq_out"):
-            out[k] = self.t[k].view(torch.int16).cpu().numpy().view(np.uint16)
+            if self.t[k] is not None:
+                out[k] = self.t[k].view(torch.int16).cpu().numpy().view(np.uint16)
+        if "q_fp8" in self.t:
+            out["q_fp8"] = self.t["q_fp8"].cpu().numpy()
         for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
             out[k] = self.t[k].cpu().numpy()
         return out

@@ -131,6 +131,33 @@ def test_invalid_arguments_rejected(fn):
     assert lib.pa_strerror(-6).decode().startswith("workspace")
 
 
+def _call_ex(fn, opts, ptrs=None, ws_bytes=1 << 30):
+    lib = B.load()
+    if ptrs is None:
+        ptrs = [4096 * (i + 1) for i in range(21)]  # never dereferenced: rejected first
+    return getattr(lib, fn)(ctypes.byref(_dims()), None if opts is None else ctypes.byref(opts),
+                            *ptrs, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["pre_attn_decode_ex", "pre_attn_prefill_ex"])
+def test_head_options_rejected(fn):
+    opts = B.pa_head_options
+    qf = 1 << 20
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-39):  # 1e-39: reciprocal overflows
+        assert _call_ex(fn, opts(0, bad, qf)) == B.PA_ERR_OPTIONS, bad
+    # the scale is ignored without the FP8 q output
+    assert _call_ex(fn, opts(1, 0.0, None), ws_bytes=16) == -6
+    assert _call_ex(fn, opts(0, 0.5, qf + 8)) == -2  # FP8 q not 16-byte aligned
+    ptrs = [4096 * (i + 1) for i in range(21)]
+    ptrs[18] = None  # q_out NULL: allowed only with the FP8 q output
+    assert _call_ex(fn, None, ptrs) == -1
+    assert _call_ex(fn, opts(1, 1.0, None), ptrs) == -1
+    assert _call_ex(fn, opts(0, 0.5, qf), ptrs, ws_bytes=16) == -6
+    ptrs[19] = None  # iq_out is always required
+    assert _call_ex(fn, opts(0, 0.5, qf), ptrs) == -1
+    assert B.load().pa_strerror(B.PA_ERR_OPTIONS).decode().startswith("q_fp8_scale")
+
+
 def test_decode_token_limit():
     assert _call("pre_attn_decode", _dims(tokens=65)) == -5
     # prefill accepts 65 tokens; the tiny workspace stops it before any launch
@@ -147,7 +174,7 @@ def test_pack_rejects_bad_shapes():
 
 def test_strerror_covers_all_codes():
     lib = B.load()
-    for code in range(0, -11, -1):
+    for code in range(0, -13, -1):
         assert lib.pa_strerror(code).decode() != "unknown status"
     assert lib.pa_strerror(-99).decode() == "unknown status"
 
