@@ -19,10 +19,13 @@ separately written scalar reference of the whole pipeline. No function here is
 from .codecs import (  # noqa: F401
     E4M3_MAX,
     bf16_bits_to_f64,
+    e2m1_decode,
+    e2m1_encode,
     e4m3_decode,
     e4m3_decode_table,
     e4m3_encode,
     e8m0_decode,
+    f32_mul_rz,
     f32_to_bf16_bits,
 )
 from .prologue import (  # noqa: F401
@@ -30,6 +33,8 @@ from .prologue import (  # noqa: F401
     head_norm_rope,
     input_norm,
     mxfp8_quantize,
+    nvfp4_quantize,
+    nvfp4_scale_offset,
     prefill,
     project_decode,
     project_mxfp8,

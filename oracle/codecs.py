@@ -9,6 +9,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   The prologue rounds to nearest even and saturates at +-448 (the pre_attn page's
   module docstring and ``norm_quant``: FP8 with scale amax / FP8_MAX).
 * E8M0 (OCP MX scale): code c means 2^(c - 127); c = 255 is NaN.
+* E2M1 (OCP MX FP4, the element type of NVFP4): 1 sign bit (0x8), 2 exponent
+  bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no
+  NaN or infinity. Rounded to nearest even and saturated at +-6 (the epilogue
+  page's NVFP4 quantizer converts with satfinite).
 """
 
 from __future__ import annotations
@@ -92,3 +96,55 @@ def e8m0_decode(codes) -> np.ndarray:
     c = np.asarray(codes, dtype=np.int64)
     out = np.ldexp(1.0, (c - 127).astype(np.int32))
     return np.where(c == 255, np.nan, out)
+
+
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit E2M1 code (float64)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.ldexp(1.0, (e - 1).astype(np.int32)))
+    return np.where(c & 0x8, -mag, mag)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Round float64 values to E2M1 codes: saturate to 6, nearest, ties to even.
+
+    Below 1 (exponent field 0) the grid is the subnormal step 0.5; the binade
+    [2^E, 2^(E+1)) for E = 0, 1, 2 holds 2 codes spaced 2^(E-1). As for E4M3,
+    np.rint on the magnitude scaled to its grid step is the exact
+    nearest-even rounding. The sign is kept (-0 -> 0x8).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("NaN has no saturating E2M1 encoding")
+    neg = np.signbit(v)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    code = np.empty(a.shape, dtype=np.int64)
+    sub = a < 1.0
+    code[sub] = np.rint(a[sub] / 0.5).astype(np.int64)  # 0, 1 or 2 (2 = 1.0)
+    an = a[~sub]
+    _, ex = np.frexp(an)
+    e = ex.astype(np.int64) - 1  # floor(log2(an)) in [0, 2]
+    m = np.rint(np.ldexp(an, (1 - e).astype(np.int32))).astype(np.int64)  # in [2, 4]
+    code[~sub] = e * 2 + m
+    return (code | (neg.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def f32_mul_rz(a, b) -> np.ndarray:
+    """float32 product a * b rounded toward zero (a, b float32).
+
+    The product of two float32 values is exact in float64 (48 significant bits
+    at most); its round-to-nearest float32 image is one of the two float32
+    neighbours, and stepping it one ulp toward zero where it landed farther
+    from zero than the exact value gives the truncated one."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    p = a.astype(np.float64) * b.astype(np.float64)
+    r = p.astype(np.float32)
+    over = np.abs(r.astype(np.float64)) > np.abs(p)
+    r = np.where(over, np.nextafter(r, np.float32(0.0)), r)
+    return r.astype(np.float32)

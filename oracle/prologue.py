@@ -46,6 +46,20 @@ Two variants of the head step, both optional inputs:
       epilogue page's q_fp8_out / q_fp8_scale, q branch: x * qfp8_inv cast to
       e4m3).
 
+NVFP4 caches (the epilogue page's cache format; optional, inp["kv_format"] ==
+"nvfp4"): K (normed + roped), V (raw) and index_k are quantized per 16-value
+group instead of per token, as float32 values (``_nvfp4_quant32``):
+  scale code  sf = E4M3(max(f32(f32(amax * f32(1/6)) * gs), 2^-9)), saturating
+  elements    E2M1(RZ(v * f32(f32(1 / dec(sf)) * gs))), satfinite, and a code
+              of magnitude zero loses its sign
+with gs = f32(1 / global_scale) for K and V (k_scale / v_scale of the page's
+argument list) and no gs for index_k. Layout (``_nvfp4_cache_views``): a page of
+kv_cache holds 2 nkv slots (K of KV head j in slot 2j, V in 2j + 1), each of 16
+tokens x 64 data bytes followed by 16 x 8 scale bytes; the index cache page holds
+one such slot. Data byte b of a token holds elements 2b (low nibble) and 2b + 1
+(high nibble). K and index_k scale bytes are linear (token t, group g at 8t + g
+of the scale area); V scale bytes take the swizzled layout of that view.
+
 Readings where the pages leave a point open (each also listed in the design
 notes): the activation norm and the FP8 decisions that follow it are taken in
 float64; eps is the float32 value the library receives; K and index_k are
@@ -62,9 +76,11 @@ from .codecs import (
     E4M3_MAX,
     bf16_bits_to_f32,
     bf16_bits_to_f64,
+    e2m1_encode,
     e4m3_decode,
     e4m3_encode,
     e8m0_decode,
+    f32_mul_rz,
     f32_to_bf16_bits,
 )
 
@@ -72,6 +88,9 @@ HEAD_DIM = 128
 ROTARY_DIM = 64
 PAGE = 16
 MX_BLOCK = 32
+NV_GROUP = 16
+NV_SLOT_BYTES = PAGE * (HEAD_DIM // 2 + HEAD_DIM // NV_GROUP)  # 1152
+NV_SF_OFF = PAGE * HEAD_DIM // 2  # scale area of a slot: 1024
 
 
 def input_norm(ar, res, g_in, eps):
@@ -171,6 +190,81 @@ def q_fp8_codes(o_q, q_fp8_scale):
     return e4m3_encode(x.astype(np.float64))
 
 
+def nvfp4_quantize(v, gs=None):
+    """NVFP4 of head rows v [T, 128] (float32 values): per 16-value group an
+    E4M3 scale byte and 16 E2M1 codes, following the epilogue page's
+    ``_nvfp4_quant32``. gs is float32(1 / global scale), or None (unit scale).
+
+    Returns (data uint8 [T, 64], element 2b in the low nibble of byte b, and
+    scale codes uint8 [T, 8]).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    T = v.shape[0]
+    grp = v.reshape(T, HEAD_DIM // NV_GROUP, NV_GROUP)
+    gmax = np.abs(grp).max(axis=2)  # exact
+    a = gmax * np.float32(1.0 / 6.0)  # float32 product with the float32 constant
+    if gs is not None:
+        a = (a * np.float32(gs)).astype(np.float32)
+    a = np.maximum(a, np.float32(2.0 ** -9))
+    sf = e4m3_encode(a.astype(np.float64))  # nearest even, saturating at 448
+    sfv = e4m3_decode(sf).astype(np.float32)  # exact
+    r = (np.float32(1.0) / sfv).astype(np.float32)  # correctly rounded reciprocal
+    if gs is not None:
+        r = (r * np.float32(gs)).astype(np.float32)
+    q = f32_mul_rz(grp, r[:, :, None])
+    codes = e2m1_encode(q.astype(np.float64)).reshape(T, HEAD_DIM)
+    codes = np.where((codes & 0x7) == 0, 0, codes).astype(np.uint8)  # no -0
+    data = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return data, sf
+
+
+def nvfp4_scale_offset(t, g, swizzled):
+    """Byte offset, inside a slot's scale area, of token t's group-g scale.
+
+    Linear: [8 groups, 16 tokens] with strides (1, 8). V-swizzled: the view of
+    shape ((2, 4), (4, 4)) with strides ((4, 8), (1, 32)) over (group, token),
+    i.e. group g = g0 + 2 g1 and token t = t0 + 4 t1 sit at
+    4 g0 + 8 g1 + t0 + 32 t1 (the epilogue page's ``_nvfp4_cache_views``).
+    """
+    if not swizzled:
+        return 8 * t + g
+    g0, g1 = g % 2, g // 2
+    t0, t1 = t % 4, t // 4
+    return 4 * g0 + 8 * g1 + 1 * t0 + 32 * t1
+
+
+def _nvfp4_insert(out, inp, o_k, y_v, o_ik):
+    """Steps a7-a9 with the NVFP4 caches (kv_cache [P, 2 nkv, 1152] and
+    index_cache [P, 1152])."""
+    S, nkv = o_k.shape[0], o_k.shape[1]
+    gk = np.float32(np.float32(1.0) / np.float32(inp.get("k_global_scale", 1.0)))
+    gv = np.float32(np.float32(1.0) / np.float32(inp.get("v_global_scale", 1.0)))
+    kd, ks = nvfp4_quantize(o_k.reshape(S * nkv, HEAD_DIM).astype(np.float32), gk)
+    vd, vs = nvfp4_quantize(y_v.reshape(S * nkv, HEAD_DIM).astype(np.float32), gv)
+    idd, ids = nvfp4_quantize(o_ik.astype(np.float32), None)
+    kd, ks = kd.reshape(S, nkv, -1), ks.reshape(S, nkv, -1)
+    vd, vs = vd.reshape(S, nkv, -1), vs.reshape(S, nkv, -1)
+    kv = inp["kv_cache"].copy()
+    ic = inp["index_cache"].copy()
+    slots = np.asarray(inp["slot_mapping"], np.int64)
+    P = kv.shape[0]
+    for s in range(S):
+        slot = int(slots[s])
+        if slot < 0 or slot >= P * PAGE:
+            continue
+        page, t = slot // PAGE, slot % PAGE
+        for j in range(nkv):
+            for sl, data, sc, swz in ((2 * j, kd[s, j], ks[s, j], False), (2 * j + 1, vd[s, j], vs[s, j], True)):
+                kv[page, sl, t * 64:(t + 1) * 64] = data
+                for g in range(8):
+                    kv[page, sl, NV_SF_OFF + nvfp4_scale_offset(t, g, swz)] = sc[g]
+        ic[page, t * 64:(t + 1) * 64] = idd[s]
+        for g in range(8):
+            ic[page, NV_SF_OFF + nvfp4_scale_offset(t, g, False)] = ids[s, g]
+    out.update(kv_cache=kv, index_cache=ic, k_nv=(kd, ks), v_nv=(vd, vs), ik_nv=(idd, ids))
+    return out
+
+
 def _epilogue(y, inp):
     """Steps a5-a10 on the float64 projection y [S, N]."""
     nkv = int(inp["nkv"])
@@ -203,6 +297,8 @@ def _epilogue(y, inp):
     }
     if inp.get("q_fp8_scale") is not None:
         out["q_fp8"] = q_fp8_codes(o_q, inp["q_fp8_scale"])
+    if inp.get("kv_format", "fp8") == "nvfp4":
+        return _nvfp4_insert(out, inp, o_k, y_v, o_ik)
     static = bool(inp.get("static_kv_scale", False))
     k_codes, k_s = _scaled_codes(o_k.reshape(S * nkv, HEAD_DIM), static)
     v_codes, v_s = _scaled_codes(y_v.reshape(S * nkv, HEAD_DIM), static)

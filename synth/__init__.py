@@ -14,4 +14,5 @@ from .inputs import (  # noqa: F401
     Workload,
     make_workload,
     named_config,
+    with_nvfp4_caches,
 )

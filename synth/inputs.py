@@ -220,3 +220,22 @@ def make_workload(wl: Workload, seed: int = 0, weights: bool = True) -> dict:
     out["nkv"] = wl.nkv
     out["mode"] = wl.mode
     return out
+
+
+NV_SLOT_BYTES = PAGE * (HEAD_DIM // 2 + HEAD_DIM // 16)  # 16 tokens x (64 data + 8 scale bytes)
+
+
+def with_nvfp4_caches(inp: dict, k_global_scale: float = 1.0, v_global_scale: float = 1.0) -> dict:
+    """The same call with NVFP4 caches instead of the FP8 ones: kv_cache
+    [pages, 2 nkv, 1152] and index_cache [pages, 1152], sentinel-filled, plus
+    the K / V global (dequantization) scales."""
+    out = {k: v for k, v in inp.items() if k not in ("k_cache", "v_cache", "k_scale", "v_scale",
+                                                     "index_cache")}
+    P = inp["k_cache"].shape[0]
+    nkv = int(inp["nkv"])
+    out["kv_format"] = "nvfp4"
+    out["kv_cache"] = np.full((P, 2 * nkv, NV_SLOT_BYTES), SENTINEL_CACHE_BYTE, np.uint8)
+    out["index_cache"] = np.full((P, NV_SLOT_BYTES), SENTINEL_CACHE_BYTE, np.uint8)
+    out["k_global_scale"] = np.float32(k_global_scale)
+    out["v_global_scale"] = np.float32(v_global_scale)
+    return out

@@ -81,6 +81,90 @@ def e4m3_round(x: float) -> int:
     return best | (0x80 if negative else 0)
 
 
+def _f32_neighbours(x: float):
+    """x (a float32 value) and the float32 values just below and above it."""
+    b = struct.unpack("<I", struct.pack("<f", x))[0]
+    out = [x]
+    for step in (-1, 1):
+        if x == 0.0:
+            out.append(struct.unpack("<f", struct.pack("<I", 1))[0] * (1 if step > 0 else -1))
+            continue
+        nb = b + step if x > 0 else b - step  # toward +inf / -inf
+        out.append(struct.unpack("<f", struct.pack("<I", nb & 0xFFFFFFFF))[0])
+    return out
+
+
+def f32_nearest(q: Fraction) -> float:
+    """The float32 nearest the rational q, ties to an even last bit."""
+    best, best_d = None, None
+    for c in _f32_neighbours(f32(float(q))):
+        d = abs(Fraction(c) - q)
+        even = struct.unpack("<I", struct.pack("<f", c))[0] % 2 == 0
+        if best is None or d < best_d or (d == best_d and even):
+            best, best_d = c, d
+    return best
+
+
+def f32_toward_zero(q: Fraction) -> float:
+    """The float32 of largest magnitude not above |q|, with q's sign."""
+    cands = [c for c in _f32_neighbours(f32(float(q))) if abs(Fraction(c)) <= abs(q)
+             and (c == 0.0 or (c > 0) == (q > 0))]
+    return max(cands, key=lambda c: abs(Fraction(c)))
+
+
+def _e2m1_values():
+    vals = {}
+    for c in range(8):
+        e, m = c >> 1, c & 1
+        vals[c] = Fraction(m, 2) if e == 0 else (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+    return vals
+
+
+E2M1 = _e2m1_values()
+
+
+def e2m1_round(x: float) -> int:
+    """Saturating nearest-even E2M1 code by search; a zero magnitude is +0."""
+    mag = min(abs(Fraction(x)), Fraction(6))
+    best, best_d = None, None
+    for c in range(8):
+        d = abs(E2M1[c] - mag)
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return best | (0x8 if x < 0 and best != 0 else 0)
+
+
+def nvfp4_row(vals, gs):
+    """NVFP4 of 128 float32 values: 128 E2M1 codes and 8 E4M3 group scale
+    codes, per the epilogue page's _nvfp4_quant32 (gs: float32 reciprocal of
+    the global scale, or None)."""
+    codes, scales = [], []
+    sixth = f32(1.0 / 6.0)
+    for g in range(8):
+        grp = vals[16 * g:16 * g + 16]
+        a = f32_nearest(Fraction(max(abs(v) for v in grp)) * Fraction(sixth))
+        if gs is not None:
+            a = f32_nearest(Fraction(a) * Fraction(gs))
+        a = max(a, 2.0 ** -9)
+        sf = e4m3_round(a)
+        r = f32_nearest(1 / E4M3[sf])
+        if gs is not None:
+            r = f32_nearest(Fraction(r) * Fraction(gs))
+        scales.append(sf)
+        codes += [e2m1_round(f32_toward_zero(Fraction(v) * Fraction(r))) for v in grp]
+    return codes, scales
+
+
+def _nv_place(writes, name, base, t, codes, scales, swizzled):
+    """Bytes of one token's NVFP4 row in a 1152-byte slot at `base`."""
+    for b in range(64):
+        writes[(name, base + t * 64 + b)] = codes[2 * b] | (codes[2 * b + 1] << 4)
+    for g in range(8):
+        # the epilogue page's formula for the V-swizzled scale byte h of token t
+        off = (t // 4 * 4 + g // 2) * 8 + g % 2 * 4 + t % 4 if swizzled else 8 * t + g
+        writes[(name, base + 1024 + off)] = scales[g]
+
+
 def _norm_row(vals, gam, eps):
     """Gemma RMSNorm of a row (float64, fsum)."""
     ms = math.fsum(v * v for v in vals) / len(vals)
@@ -103,6 +187,10 @@ def run(inp, mode: str):
     product of q and the float32 reciprocal of the scale, the epilogue page's
     q_fp8_out)."""
     static = bool(inp.get("static_kv_scale", False))
+    nvfp4 = inp.get("kv_format", "fp8") == "nvfp4"
+    if nvfp4:
+        gk = f32(1.0 / f32(float(inp["k_global_scale"])))
+        gv = f32(1.0 / f32(float(inp["v_global_scale"])))
     qs = inp.get("q_fp8_scale")
     q_inv = None if qs is None else f32(1.0 / f32(float(qs)))
     q_fp8 = []
@@ -178,6 +266,17 @@ def run(inp, mode: str):
         if slot < 0:
             continue
         page, t = slot // 16, slot % 16
+        if nvfp4:
+            for j in range(nkv):
+                ok = head(16 * nkv + j, "g_k")
+                yv = y[(17 * nkv + j) * HEAD_DIM:(17 * nkv + j + 1) * HEAD_DIM]
+                kc, ksc = nvfp4_row([f32(v) for v in ok], gk)
+                vc, vsc = nvfp4_row([f32(v) for v in yv], gv)
+                _nv_place(writes, "kv_cache", (page * 2 * nkv + 2 * j) * 1152, t, kc, ksc, False)
+                _nv_place(writes, "kv_cache", (page * 2 * nkv + 2 * j + 1) * 1152, t, vc, vsc, True)
+            ic, isc = nvfp4_row([f32(v) for v in head(19 * nkv, "g_ik")], None)
+            _nv_place(writes, "index_cache", page * 1152, t, ic, isc, False)
+            continue
         for j in range(nkv):
             ok = head(16 * nkv + j, "g_k")
             yv = y[(17 * nkv + j) * HEAD_DIM:(17 * nkv + j + 1) * HEAD_DIM]
