@@ -91,8 +91,9 @@ typedef enum pa_status {
   PA_ERR_DEVICE = -9,    /* the current device is not a gfx950 GPU */
   PA_ERR_MODE = -10,     /* unknown mode argument */
   PA_ERR_SYNC = -11,     /* a kernel's bounded wait for another CTA gave up */
-  PA_ERR_OPTIONS = -12   /* pa_head_options: q_fp8_scale not finite and > 0, or its
-                            float32 reciprocal not finite */
+  PA_ERR_OPTIONS = -12   /* pa_head_options: a scale not finite and > 0 (or its float32
+                            reciprocal not finite), an unknown kv_cache_format, or
+                            static_kv_scale together with NVFP4 */
 } pa_status;
 
 /* Problem size of one call. */
@@ -203,10 +204,37 @@ int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* re
  * q_fp8_scale      the dequantization scale of q_fp8_out; with q_fp8_out set it
  *     must be finite and > 0 with a finite float32 reciprocal (else
  *     PA_ERR_OPTIONS). Ignored when q_fp8_out is NULL. */
+/* kv_cache_format  PA_KV_FP8 (0): the caches of the plain calls.
+ *     PA_KV_NVFP4 (1): the epilogue page's NVFP4 caches (its _nvfp4_quant32
+ *     quantizer and _nvfp4_cache_views layout, the k / v / index_k branches of
+ *     the per-role epilogue). Per 16-value group of a row (as float32):
+ *       sf = E4M3(max(amax * f32(1/6) * gs, 2^-9)), saturating;
+ *       element codes E2M1(RZ(v * f32(f32(1 / sf) * gs))), nearest even,
+ *       saturating at +-6; a zero magnitude is stored as +0;
+ *     gs = f32(1 / k_global_scale) for K (normed + roped), f32(1 / v_global_scale)
+ *     for V (raw), none for index_k (normed + roped).
+ *     Layouts (uint8, 16-byte aligned, caller-owned):
+ *       k_cache      the K/V cache [num_pages][2 nkv][1152]: slot 2j holds
+ *                    K of KV head j, slot 2j + 1 its V;
+ *       index_cache  [num_pages][1152], one slot per page;
+ *     a 1152-byte slot holds the 16 tokens' data, 64 bytes each (byte b of
+ *     token t at 64 t + b: element 2b in the low nibble, 2b + 1 in the high),
+ *     then their scale bytes from offset 1024: K and index_k linear (token t,
+ *     group g at 1024 + 8 t + g); V swizzled, at 1024 + (t / 4 * 4 + g / 2) * 8
+ *     + (g % 2) * 4 + t % 4. v_cache, k_scale and v_scale are unused (NULL is
+ *     allowed). static_kv_scale must be 0.
+ * k_global_scale, v_global_scale  NVFP4 only: the dequantization (global)
+ *     scales of the K and V entries, finite and > 0 with finite float32
+ *     reciprocals. */
+#define PA_KV_FP8 0
+#define PA_KV_NVFP4 1
 typedef struct pa_head_options {
   int32_t static_kv_scale;
   float q_fp8_scale;
   uint8_t* q_fp8_out;
+  int32_t kv_cache_format;
+  float k_global_scale;
+  float v_global_scale;
 } pa_head_options;
 
 /* pre_attn_decode with head-step options. Same arguments and results, except:

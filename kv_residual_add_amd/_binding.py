@@ -26,6 +26,9 @@ PA_DECODE_NORM_FUSED = 1
 PA_DECODE_EPILOGUE_FUSED = 2
 PA_ERR_SYNC = -11
 PA_ERR_OPTIONS = -12
+PA_KV_FP8 = 0
+PA_KV_NVFP4 = 1
+NV_SLOT_BYTES = 1152
 
 EXPORTS = (
     "pa_workspace_bytes",
@@ -63,18 +66,28 @@ class pa_head_options(ctypes.Structure):
         ("static_kv_scale", ctypes.c_int32),
         ("q_fp8_scale", ctypes.c_float),
         ("q_fp8_out", ctypes.c_void_p),
+        ("kv_cache_format", ctypes.c_int32),
+        ("k_global_scale", ctypes.c_float),
+        ("v_global_scale", ctypes.c_float),
     ]
 
 
 class HeadOptions:
     """Head-step variants of pre_attn_decode_ex / pre_attn_prefill_ex:
-    static_kv_scale (unit K / V scales) and an optional FP8 q output
-    q_fp8_out (uint8 [tokens, 16 nkv, 128]) with its dequantization scale."""
+    static_kv_scale (unit K / V scales), an optional FP8 q output q_fp8_out
+    (uint8 [tokens, 16 nkv, 128]) with its dequantization scale, and the NVFP4
+    cache format (nvfp4=True: k_cache is the K/V cache uint8
+    [pages, 2 nkv, 1152], index_cache uint8 [pages, 1152]; v_cache, k_scale and
+    v_scale may be None) with the K / V global scales."""
 
-    def __init__(self, static_kv_scale: bool = False, q_fp8_out=None, q_fp8_scale: float = 1.0):
+    def __init__(self, static_kv_scale: bool = False, q_fp8_out=None, q_fp8_scale: float = 1.0,
+                 nvfp4: bool = False, k_global_scale: float = 1.0, v_global_scale: float = 1.0):
         self.static_kv_scale = bool(static_kv_scale)
         self.q_fp8_out = q_fp8_out
         self.q_fp8_scale = float(q_fp8_scale)
+        self.nvfp4 = bool(nvfp4)
+        self.k_global_scale = float(k_global_scale)
+        self.v_global_scale = float(v_global_scale)
 
 
 class PaError(RuntimeError):
@@ -259,13 +272,15 @@ def _run(fn_name: str, mode: int, dims: pa_dims, ar, res, h_out, g_in, w_packed,
     dev = ar.device
     bf, u8, f32, i64 = torch.bfloat16, torch.uint8, torch.float32, torch.int64
     lead = [ctypes.byref(dims)]
+    nvfp4 = opts is not None and opts.nvfp4
     if fn_name.endswith("_ex"):
         c_opts = None
         if opts is not None:
             qf = opts.q_fp8_out
             c_opts = pa_head_options(
                 int(opts.static_kv_scale), opts.q_fp8_scale,
-                None if qf is None else _ptr(qf, "q_fp8_out", u8, S * 16 * nkv * HEAD_DIM, dev))
+                None if qf is None else _ptr(qf, "q_fp8_out", u8, S * 16 * nkv * HEAD_DIM, dev),
+                PA_KV_NVFP4 if nvfp4 else PA_KV_FP8, opts.k_global_scale, opts.v_global_scale)
         lead.append(None if c_opts is None else ctypes.byref(c_opts))
     ws_need = pa_workspace_bytes(dims, mode)
     if ws_need == 0:
@@ -286,11 +301,16 @@ def _run(fn_name: str, mode: int, dims: pa_dims, ar, res, h_out, g_in, w_packed,
         _ptr(g_iq, "g_iq", bf, HEAD_DIM, dev), _ptr(g_ik, "g_ik", bf, HEAD_DIM, dev),
         _ptr(cos_sin, "cos_sin", bf, L * 64, dev),
         _ptr(positions, "positions", i64, S, dev), _ptr(slot_mapping, "slot_mapping", i64, S, dev),
-        _ptr(k_cache, "k_cache", u8, P * nkv * PAGE_BYTES, dev),
-        _ptr(v_cache, "v_cache", u8, P * nkv * PAGE_BYTES, dev),
-        _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
-        _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
-        _ptr(index_cache, "index_cache", u8, P * PAGE * HEAD_DIM, dev),
+        *([_ptr(k_cache, "kv_cache (NVFP4)", u8, P * 2 * nkv * NV_SLOT_BYTES, dev),
+           None if v_cache is None else _ptr(v_cache, "v_cache", u8, P * nkv * PAGE_BYTES, dev),
+           None if k_scale is None else _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
+           None if v_scale is None else _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
+           _ptr(index_cache, "index_cache (NVFP4)", u8, P * NV_SLOT_BYTES, dev)] if nvfp4 else
+          [_ptr(k_cache, "k_cache", u8, P * nkv * PAGE_BYTES, dev),
+           _ptr(v_cache, "v_cache", u8, P * nkv * PAGE_BYTES, dev),
+           _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
+           _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
+           _ptr(index_cache, "index_cache", u8, P * PAGE * HEAD_DIM, dev)]),
         None if q_out is None else _ptr(q_out, "q_out", bf, S * 16 * nkv * HEAD_DIM, dev),
         _ptr(iq_out, "iq_out", bf, S * nkv * HEAD_DIM, dev),
         workspace.data_ptr(),

@@ -84,30 +84,46 @@ struct Opts {
   uint8_t* q_fp8 = nullptr;
   float q_fp8_inv = 1.0f;
   int static_kv = 0;
+  int nvfp4 = 0;
+  float k_gs = 1.0f, v_gs = 1.0f;
 };
+
+// float32(1 / s), correctly rounded, for a finite s > 0 whose reciprocal is finite
+bool reciprocal(float s, float& out) {
+  if (!std::isfinite(s) || !(s > 0.0f)) return false;
+  const volatile float one = 1.0f;
+  out = one / s;
+  return std::isfinite(out);
+}
 
 int check_opts(const pa_head_options* o, Opts& out) {
   if (!o) return PA_OK;
   out.static_kv = o->static_kv_scale != 0;
+  if (o->kv_cache_format != PA_KV_FP8 && o->kv_cache_format != PA_KV_NVFP4) return PA_ERR_OPTIONS;
+  if (o->kv_cache_format == PA_KV_NVFP4) {
+    if (out.static_kv) return PA_ERR_OPTIONS;  // per-group scales have no static form
+    out.nvfp4 = 1;
+    if (!reciprocal(o->k_global_scale, out.k_gs) || !reciprocal(o->v_global_scale, out.v_gs))
+      return PA_ERR_OPTIONS;
+  }
   out.q_fp8 = o->q_fp8_out;
   if (out.q_fp8) {
     if (!aligned(out.q_fp8, 16)) return PA_ERR_ALIGN;
-    if (!std::isfinite(o->q_fp8_scale) || !(o->q_fp8_scale > 0.0f)) return PA_ERR_OPTIONS;
-    const volatile float one = 1.0f;  // the correctly rounded float32 reciprocal
-    out.q_fp8_inv = one / o->q_fp8_scale;
-    if (!std::isfinite(out.q_fp8_inv)) return PA_ERR_OPTIONS;
+    if (!reciprocal(o->q_fp8_scale, out.q_fp8_inv)) return PA_ERR_OPTIONS;
   }
   return PA_OK;
 }
 
-// q_out may be NULL only when the FP8 q output is requested.
-int check_ptrs(const Ptrs& p, bool has_q_fp8) {
+// q_out may be NULL only when the FP8 q output is requested; v_cache, k_scale
+// and v_scale are not used (and may be NULL) with the NVFP4 caches.
+int check_ptrs(const Ptrs& p, bool has_q_fp8, bool nvfp4) {
   const void* all[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.w_scales, p.g_q, p.g_k,
                        p.g_iq, p.g_ik, p.cos_sin, p.positions, p.slot_mapping, p.k_cache,
-                       p.v_cache, p.k_scale, p.v_scale, p.index_cache, p.iq_out, p.ws};
+                       p.index_cache, p.iq_out, p.ws};
   for (const void* q : all)
     if (!q) return PA_ERR_NULL;
   if (!p.q_out && !has_q_fp8) return PA_ERR_NULL;
+  if (!nvfp4 && (!p.v_cache || !p.k_scale || !p.v_scale)) return PA_ERR_NULL;
   const void* a16[] = {p.ar, p.res, p.h_out, p.g_in, p.w_packed, p.q_out, p.iq_out, p.g_q, p.g_k,
                        p.g_iq, p.g_ik, p.cos_sin, p.k_cache, p.v_cache, p.index_cache, p.ws};
   for (const void* q : a16)
@@ -164,7 +180,7 @@ int run(int mode, const pa_dims* dims, const Ptrs& p, const pa_head_options* opt
   Opts o;
   st = check_opts(opts, o);
   if (st) return st;
-  st = check_ptrs(p, o.q_fp8 != nullptr);
+  st = check_ptrs(p, o.q_fp8 != nullptr, o.nvfp4 != 0);
   if (st) return st;
   if (ws_bytes < workspace_for(dims, mode)) return PA_ERR_WORKSPACE;
   st = check_device();
@@ -173,6 +189,9 @@ int run(int mode, const pa_dims* dims, const Ptrs& p, const pa_head_options* opt
   a.q_fp8 = o.q_fp8;
   a.q_fp8_inv = o.q_fp8_inv;
   a.static_kv = o.static_kv;
+  a.kv_nvfp4 = o.nvfp4;
+  a.k_gs = o.k_gs;
+  a.v_gs = o.v_gs;
   hipError_t e;
   if (mode == PA_MODE_DECODE) {
     a.w_scale = static_cast<const float*>(p.w_scales);
@@ -341,7 +360,9 @@ const char* pa_strerror(int status) {
     case PA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case PA_ERR_MODE: return "unknown mode";
     case PA_ERR_SYNC: return "a kernel's bounded wait gave up: that call's outputs are not valid";
-    case PA_ERR_OPTIONS: return "q_fp8_scale must be finite and > 0, with a finite float32 reciprocal";
+    case PA_ERR_OPTIONS:
+      return "bad pa_head_options: a scale not finite and > 0 (or with an infinite float32 reciprocal), "
+             "an unknown kv_cache_format, or static_kv_scale with NVFP4";
     default: return "unknown status";
   }
 }

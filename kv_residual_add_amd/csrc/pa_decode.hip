@@ -408,6 +408,27 @@ __device__ __forceinline__ float load_partial(const float* p) {
     return *p;
 }
 
+// NVFP4 row of one token into a 1152-byte cache slot (the wave holds dims lane
+// and lane + 64 as float32): 16-lane group maxima, then each even lane stores
+// the byte of its dim pair in both halves, and lanes 0, 16, 32, 48 the scale
+// bytes of their two groups. Every lane of the wave must call it.
+__device__ __forceinline__ void nvfp4_row_wave(float x0, float x1, float gs, bool has_gs, uint8_t* slot, int t,
+                                               bool swizzled, int lane) {
+#pragma nounroll
+  for (int hh = 0; hh < 2; ++hh) {  // one half at a time keeps the extra registers few
+    const float x = hh ? x1 : x0;
+    float m = __builtin_fabsf(x);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+    const NvScale ns = nv_scale(m, gs, has_gs);
+    const uint32_t c = e2m1_code(mul_rz(x, ns.r));
+    const uint32_t n = __shfl_down(c, 1, 64);
+    if ((lane & 1) == 0) slot[t * 64 + 32 * hh + (lane >> 1)] = static_cast<uint8_t>(c | (n << 4));
+    if ((lane & 15) == 0)
+      slot[kNvScaleOff + nv_scale_offset(t, 4 * hh + (lane >> 4), swizzled)] = static_cast<uint8_t>(ns.sf);
+  }
+}
+
 template <bool COHERENT>
 __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, const float* __restrict__ part,
                                               const float* __restrict__ sx, int ksplit, int tlb) {
@@ -468,6 +489,12 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
 
+  if (h >= v0 && h < iq0 && a.kv_nvfp4) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
+    if (store_cache)
+      nvfp4_row_wave(static_cast<float>(y0), static_cast<float>(y1), a.v_gs, true,
+                     a.k_cache + (page * 2 * nkv + 2 * (h - v0) + 1) * kNvSlotBytes, t, true, lane);
+    return;
+  }
   if (h >= v0 && h < iq0) {  // V: the raw projection, per-token scale (1 when static)
     const int j = h - v0;
     const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
@@ -506,6 +533,10 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
       a.q_fp8[qrow + d0] = static_cast<uint8_t>(c2);
       a.q_fp8[qrow + d1] = static_cast<uint8_t>(c2 >> 8);
     }
+  } else if (h < v0 && a.kv_nvfp4) {  // K, NVFP4: slot 2j, linear scale bytes
+    if (store_cache)
+      nvfp4_row_wave(static_cast<float>(o0), static_cast<float>(o1), a.k_gs, true,
+                     a.k_cache + (page * 2 * nkv + 2 * (h - k0)) * kNvSlotBytes, t, false, lane);
   } else if (h < v0) {  // K: per-token scale (1 when static), shuffled page-16 layout
     const int j = h - k0;
     const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
@@ -523,6 +554,9 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
     uint16_t* q = a.iq_out + (static_cast<size_t>(tok) * nkv + j) * kHeadDim;
     q[d0] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o0)));
     q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
+  } else if (store_cache && a.kv_nvfp4) {  // index_k, NVFP4: the page's one slot, no global scale
+    nvfp4_row_wave(static_cast<float>(o0), static_cast<float>(o1), 1.0f, false,
+                   a.index_cache + page * kNvSlotBytes, t, false, lane);
   } else if (store_cache) {  // index_k: unit-scale E4M3 into the slot's row
     uint8_t* ic = a.index_cache + slot * kHeadDim;
     const uint32_t c2 = e4m3x2_scaled(o0, o1, fp8_scale(0));

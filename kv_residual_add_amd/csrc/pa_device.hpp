@@ -139,6 +139,68 @@ __device__ __forceinline__ uint32_t e4m3x4_scaled(double v0, double v1, double v
   return static_cast<uint32_t>(w);
 }
 
+// NVFP4 (the epilogue page's K / V / index_k cache format): per 16-value group
+// an E4M3 scale byte and 16 E2M1 codes, element 2b in the low nibble of byte b.
+constexpr int kNvSlotBytes = kPage * (kHeadDim / 2 + kHeadDim / 16);  // 1152
+constexpr int kNvScaleOff = kPage * kHeadDim / 2;                     // 1024
+
+// Value of a non-negative E4M3 code (exact): (1 + m/8) 2^(e-7), or m 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
+}
+
+// A group's scale code sf and element multiplier r, from the group's largest
+// magnitude (float32): sf = E4M3(max(amax * f32(1/6) [* gs], 2^-9)), saturating;
+// r = RN32(1 / dec(sf)) [* gs]. The reciprocal is taken in float64 and rounded
+// once more to float32: 1 / dec(sf) is m^-1 2^k with m an odd integer below 16,
+// whose binary expansion repeats with a period of at most 12 bits, so the
+// float64 value is never a float32 midpoint and the second rounding gives the
+// correctly rounded float32 reciprocal.
+struct NvScale {
+  uint32_t sf;
+  float r;
+};
+
+__device__ __forceinline__ NvScale nv_scale(float amax, float gs, bool has_gs) {
+#pragma clang fp contract(off)
+  float a = amax * (1.0f / 6.0f);
+  if (has_gs) a = a * gs;
+  a = __builtin_fmaxf(a, 0x1p-9f);
+  NvScale s;
+  s.sf = e4m3x2_scaled(static_cast<double>(a), 0.0, fp8_scale(0)) & 0xFFu;
+  s.r = static_cast<float>(1.0 / static_cast<double>(e4m3_to_f32(s.sf)));
+  if (has_gs) s.r = s.r * gs;
+  return s;
+}
+
+// float32 product rounded toward zero: exact in float64, rounded to nearest
+// float32, then one ulp back toward zero where that landed past the exact value.
+__device__ __forceinline__ float mul_rz(float x, float y) {
+  const double p = static_cast<double>(x) * static_cast<double>(y);
+  const float f = static_cast<float>(p);
+  return __builtin_fabs(static_cast<double>(f)) > __builtin_fabs(p) ? __uint_as_float(__float_as_uint(f) - 1u) : f;
+}
+
+// E2M1 code of q: nearest, ties to the even code, saturating at +-6 (the
+// comparisons below are the rounding boundaries of the grid 0, .5, 1, 1.5, 2,
+// 3, 4, 6, strict where the tie goes down to the even code); a zero magnitude
+// keeps no sign.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = __builtin_fabsf(q);
+  const uint32_t m = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.0f);
+  return m | (q < 0.0f && m != 0u ? 8u : 0u);
+}
+
+// Offset of token t's group-g scale byte in a slot's scale area: linear
+// (K, index_k) or the swizzled V view, (t/4*4 + g/2)*8 + (g%2)*4 + t%4.
+__device__ __forceinline__ int nv_scale_offset(int t, int g, bool swizzled) {
+  return swizzled ? ((t >> 2) * 4 + (g >> 1)) * 8 + (g & 1) * 4 + (t & 3) : 8 * t + g;
+}
+
 // Wave64 reductions of float64 with DPP row operations (no LDS traffic):
 // xor-1 and xor-2 inside quads, the half-row and row mirrors, then the row
 // broadcasts of lanes 15 and 31 carry the partial results up to lane 63, which

@@ -28,6 +28,8 @@ struct Args {
   uint8_t* q_fp8;                // optional E4M3 q [S][16 nkv][128]
   float q_fp8_inv;               // float32(1 / q_fp8_scale)
   int static_kv;                 // nonzero: unit K / V scales
+  int kv_nvfp4;                  // nonzero: NVFP4 caches (k_cache = K/V cache, index_cache NVFP4)
+  float k_gs, v_gs;              // NVFP4: float32(1 / global scale) of K and V
   uint8_t* ws;
   hipStream_t stream;
   hipEvent_t ev_start, ev_stop;  // optional, around the dominant kernel

@@ -465,6 +465,95 @@ __device__ __forceinline__ const uint16_t* head_gamma(const Args& a, int h) {
 }
 
 
+// A lane's half row of NVFP4 (64 dims = 4 groups, dims dbase + 16 gl ..): the
+// 32 data bytes as 8 words and the 4 scale bytes, stored into a 1152-byte
+// cache slot at token row t.
+__device__ __forceinline__ void nv_store_half(uint8_t* slot, int t, int half, const uint32_t (&w)[8],
+                                              const uint32_t (&sf)[4], bool swizzled) {
+  uint8_t* d = slot + t * 64 + 32 * half;
+  *reinterpret_cast<u32x4*>(d) = u32x4{w[0], w[1], w[2], w[3]};
+  *reinterpret_cast<u32x4*>(d + 16) = u32x4{w[4], w[5], w[6], w[7]};
+  if (!swizzled) {
+    *reinterpret_cast<uint32_t*>(slot + kNvScaleOff + 8 * t + 4 * half) =
+        sf[0] | (sf[1] << 8) | (sf[2] << 16) | (sf[3] << 24);
+  } else {
+#pragma unroll
+    for (int gl = 0; gl < 4; ++gl) slot[kNvScaleOff + nv_scale_offset(t, 4 * half + gl, true)] = static_cast<uint8_t>(sf[gl]);
+  }
+}
+
+// K / index_k values of the lane's half row in float64: Gemma norm with rr and
+// the gamma row, NeoX rotation with the token's cos / sin (identity for the
+// upper half), for the dim pair (i + e, i + 32 + e), rounded to float32 (the
+// values the NVFP4 quantizer takes).
+__device__ __forceinline__ void k_pair_f32(const TileRow& x, const uint16_t* gam, const u32x4 (&c)[4],
+                                           const u32x4 (&sn)[4], double rr, int c0, int dbase, int i, float (&f1)[4],
+                                           float (&f2)[4]) {
+#pragma clang fp contract(off)
+  const float4 a1 = x.chunk(c0 + (i >> 2));
+  const float4 a2 = x.chunk(c0 + (i >> 2) + 8);
+  const float x1s[4] = {a1.x, a1.y, a1.z, a1.w}, x2s[4] = {a2.x, a2.y, a2.z, a2.w};
+  const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + (i & ~7));
+  const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + (i & ~7));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int d = i + e;
+    const double x1 = (static_cast<double>(x1s[e]) * rr) * (1.0 + bf16_at(ga, d & 7));
+    const double x2 = (static_cast<double>(x2s[e]) * rr) * (1.0 + bf16_at(gb, d & 7));
+    const double cd = bf16_at(c[d >> 3], d & 7), sd2 = bf16_at(sn[d >> 3], d & 7);
+    f1[e] = static_cast<float>(x1 * cd - x2 * sd2);
+    f2[e] = static_cast<float>(x2 * cd + x1 * sd2);
+  }
+}
+
+// NVFP4 of the lane's half row: 64 float32 values read from the wave's LDS
+// tile row (dims dbase + 16 gl .. for groups gl = 0..3, chunks c0 + 4 gl ..),
+// into a 1152-byte cache slot at token row t.
+__device__ __forceinline__ void nv_half_from_tile(const TileRow& x, int c0, float gs, bool has_gs, uint8_t* slot,
+                                                  int t, int half, bool swizzled) {
+  uint32_t w[8], sf[4];
+#pragma unroll
+  for (int gl = 0; gl < 4; ++gl) {
+    float am = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v = x.chunk(c0 + 4 * gl + c);
+      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                                               __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+    }
+    const NvScale ns = nv_scale(am, gs, has_gs);
+    sf[gl] = ns.sf;
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      const float4 p = x.chunk(c0 + 4 * gl + c), q = x.chunk(c0 + 4 * gl + c + 1);
+      const float f[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= e2m1_code(mul_rz(f[e], ns.r)) << (4 * e);
+      w[2 * gl + (c >> 1)] = word;
+    }
+  }
+  nv_store_half(slot, t, half, w, sf, swizzled);
+}
+
+// NVFP4 of the lane's half row of K (global scale gs) or index_k (none). The
+// float32 images of the normed and roped values replace the lane's own 64
+// accumulators in its LDS tile row (a rotation pair (i, i + 32) lies inside
+// one lane's half, and no other lane reads them), and the quantizer reads
+// them back: the 64 values are never live in registers at once.
+__device__ __forceinline__ void nv_k_half(const TileRow& x, const uint16_t* gam, const EpiIn& in, double rr, int c0,
+                                          int dbase, bool has_gs, float gs, uint8_t* slot, int t, int half) {
+  float* rowp = const_cast<float*>(x.row);
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    float f1[4], f2[4];
+    k_pair_f32(x, gam, in.c, in.sn, rr, c0, dbase, i, f1, f2);
+    *reinterpret_cast<float4*>(rowp + 4 * ((c0 + (i >> 2)) ^ x.r)) = float4{f1[0], f1[1], f1[2], f1[3]};
+    *reinterpret_cast<float4*>(rowp + 4 * ((c0 + (i >> 2) + 8) ^ x.r)) = float4{f2[0], f2[1], f2[2], f2[3]};
+  }
+  nv_half_from_tile(x, c0, gs, has_gs, slot, t, half, false);
+}
+
 __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, const uint16_t* gam, int h, int tok,
                                               int64_t slot, const EpiIn& in) {
 #pragma clang fp contract(off)
@@ -479,6 +568,13 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
+
+  if (h >= v0 && h < iq0 && a.kv_nvfp4) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
+    if (store_cache)
+      nv_half_from_tile(x, c0, a.v_gs, true, a.k_cache + (page * 2 * nkv + 2 * (h - v0) + 1) * kNvSlotBytes, t, half,
+                        true);
+    return;
+  }
 
   if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale (1 when static)
     const int j = h - v0;
@@ -613,6 +709,14 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   // K and index_k share one copy of the f64 group code: pass kAmax finds the K
   // row's scale, pass kCodes writes E4M3 codes (K with its scale into the
   // shuffled page layout, index_k with unit scale into its row).
+  if (a.kv_nvfp4) {  // K into slot 2j, index_k into the page's slot, linear scale bytes
+    if (!store_cache) return;
+    uint8_t* slot_base =
+        h < v0 ? a.k_cache + (page * 2 * nkv + 2 * (h - k0)) * kNvSlotBytes : a.index_cache + page * kNvSlotBytes;
+    nv_k_half(x, gam, in, rr, c0, dbase, h < v0, a.k_gs, slot_base, t, half);
+    return;
+  }
+
   enum { kAmax, kCodes };
   int mode;
   uint8_t* cbase = nullptr;
@@ -776,7 +880,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __
   const TileRow tr{tile + row * kHeadDim, row};
   // one token tile at a time (written out per tile: a loop over n would index
   // the accumulators at run time)
-  auto epilogue = [&](const f32x16 (&accn)[4], int n, int64_t slot, int64_t pos) {
+  auto epilogue = [&](const f32x16 (&accn)[4], int n, int64_t slot, int64_t pos) __attribute__((always_inline)) {
     const EpiIn in = epilogue_loads(a, pos);
     // Each wave hands its tile over through its own ring slot (every wave is
     // past its last read of the ring), reading it back in the same instruction

@@ -29,7 +29,8 @@ class Problem:
         S, K = arrays["ar"].shape
         self.nkv = int(arrays["nkv"])
         self.N = (19 * self.nkv + 1) * B.HEAD_DIM
-        self.dims = B.make_dims(S, K, self.nkv, arrays["k_cache"].shape[0],
+        pages = (arrays["kv_cache"] if arrays.get("kv_format", "fp8") == "nvfp4" else arrays["k_cache"]).shape[0]
+        self.dims = B.make_dims(S, K, self.nkv, pages,
                                 arrays["cos_sin"].shape[0], float(arrays["eps"]))
         dev = self.device
         t = {}
@@ -37,10 +38,16 @@ class Problem:
             t[k] = _to_dev(arrays[k].view(np.int16), dev, torch.bfloat16)
         for k in ("positions", "slot_mapping"):
             t[k] = _to_dev(arrays[k].astype(np.int64), dev)
-        for k in ("k_cache", "v_cache", "index_cache"):
-            t[k] = _to_dev(arrays[k], dev)
-        for k in ("k_scale", "v_scale"):
-            t[k] = _to_dev(arrays[k], dev)
+        self.nvfp4 = arrays.get("kv_format", "fp8") == "nvfp4"
+        if self.nvfp4:  # the K/V cache goes in the k_cache argument
+            t["k_cache"] = _to_dev(arrays["kv_cache"], dev)
+            t["index_cache"] = _to_dev(arrays["index_cache"], dev)
+            t["v_cache"] = t["k_scale"] = t["v_scale"] = None
+        else:
+            for k in ("k_cache", "v_cache", "index_cache"):
+                t[k] = _to_dev(arrays[k], dev)
+            for k in ("k_scale", "v_scale"):
+                t[k] = _to_dev(arrays[k], dev)
         t["h_out"] = torch.empty((S, K), dtype=torch.bfloat16, device=dev)
         t["q_out"] = torch.empty((S, 16 * self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
         t["iq_out"] = torch.empty((S, self.nkv, B.HEAD_DIM), dtype=torch.bfloat16, device=dev)
@@ -48,13 +55,15 @@ class Problem:
         # "q_fp8_scale" (adds the FP8 q output) and "q_bf16" (False: no bf16 q)
         self.opts = None
         qs = arrays.get("q_fp8_scale")
-        if arrays.get("static_kv_scale", False) or qs is not None:
+        if arrays.get("static_kv_scale", False) or qs is not None or self.nvfp4:
             qf = None
             if qs is not None:
                 qf = torch.empty((S, 16 * self.nkv, B.HEAD_DIM), dtype=torch.uint8, device=dev)
                 t["q_fp8"] = qf
             self.opts = B.HeadOptions(bool(arrays.get("static_kv_scale", False)), qf,
-                                      1.0 if qs is None else float(qs))
+                                      1.0 if qs is None else float(qs), self.nvfp4,
+                                      float(arrays.get("k_global_scale", 1.0)),
+                                      float(arrays.get("v_global_scale", 1.0)))
         if not arrays.get("q_bf16", True):
             t["q_out"] = None
         self.t = t
@@ -107,6 +116,10 @@ class Problem:
                 out[k] = self.t[k].view(torch.int16).cpu().numpy().view(np.uint16)
         if "q_fp8" in self.t:
             out["q_fp8"] = self.t["q_fp8"].cpu().numpy()
+        if self.nvfp4:
+            out["kv_cache"] = self.t["k_cache"].cpu().numpy()
+            out["index_cache"] = self.t["index_cache"].cpu().numpy()
+            return out
         for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
             out[k] = self.t[k].cpu().numpy()
         return out

@@ -6,6 +6,9 @@ prologue's contract states:
   which cache bytes / scales    bit-exact set (caches start as sentinels)
   FP8 cache codes               code distance <= 1, in at most 0.1% of codes
   K / V scales                  relative difference <= 1e-6
+  NVFP4 caches (when requested) E2M1 element codes and E4M3 group scale codes:
+                                distance <= 1, in at most 0.1% of each; the
+                                written bytes exactly the slots' bytes
   FP8 q (when requested)        decoded values (times the scale) within the q bar
                                 plus one E4M3 step at the oracle's value; codes
                                 differ in at most 1% of elements
@@ -98,6 +101,13 @@ def compare(inp: dict, ref: dict, got: dict, rows=None, strict: bool = True) -> 
 
     slots = np.asarray(inp["slot_mapping"])[rows]
     nkv = int(inp["nkv"])
+    if inp.get("kv_format", "fp8") == "nvfp4":
+        _compare_nvfp4(got, ref, slots, nkv, stats, fails)
+        stats["live_slots"] = int((slots >= 0).sum())
+        if strict:
+            assert not fails, "; ".join(fails) + f" | {stats}"
+        stats["failures"] = fails
+        return stats
     for cache, idx in (("k_cache", None), ("v_cache", None), ("index_cache", None)):
         gs, rs = [], []
         for slot in slots:
@@ -145,6 +155,80 @@ def compare(inp: dict, ref: dict, got: dict, rows=None, strict: bool = True) -> 
         assert not fails, "; ".join(fails) + f" | {stats}"
     stats["failures"] = fails
     return stats
+
+
+def e2m1_ord(c):
+    c = np.asarray(c, np.int64)
+    return np.where(c & 0x8, -(c & 0x7), c & 0x7)
+
+
+NV_SLOT = 1152
+
+
+def _nv_rows(cache_page_slot: np.ndarray, t: int):
+    """A token's 128 E2M1 codes and its slot's whole scale area."""
+    data = cache_page_slot[t * 64:(t + 1) * 64]
+    codes = np.stack([data & 0xF, data >> 4], axis=-1).reshape(128)
+    return codes, cache_page_slot[1024:]
+
+
+def _compare_nvfp4(got, ref, slots, nkv, stats, fails):
+    gc, rc, gs, rs = [], [], [], []
+    for slot in slots:
+        if slot < 0:
+            continue
+        page, t = slot // 16, slot % 16
+        pairs = [(got["kv_cache"][page, s], ref["kv_cache"][page, s]) for s in range(2 * nkv)]
+        pairs.append((got["index_cache"][page], ref["index_cache"][page]))
+        for g, r in pairs:
+            a, sa = _nv_rows(g, t)
+            b, sb = _nv_rows(r, t)
+            gc.append(a)
+            rc.append(b)
+            wr = sb != SENTINEL  # the scale bytes the oracle wrote in this slot so far
+            gs.append(sa[wr])
+            rs.append(sb[wr])
+    if not gc:
+        return
+    for name, g, r, ordf in (("nv_code", np.concatenate(gc), np.concatenate(rc), e2m1_ord),
+                             ("nv_scale", np.concatenate(gs), np.concatenate(rs), code_ord)):
+        d = np.abs(ordf(g) - ordf(r))
+        stats[f"{name}_max_dist"] = int(d.max(initial=0))
+        stats[f"{name}_frac_diff"] = float((d > 0).mean()) if d.size else 0.0
+        if d.max(initial=0) > 1:
+            fails.append(f"{name}: distance {d.max()} > 1")
+        if d.size and (d > 0).mean() > CODE_FRAC:
+            fails.append(f"{name}: {(d > 0).mean():.2e} differ (> {CODE_FRAC})")
+
+
+SENTINEL = 0x7F
+
+
+def check_written_sets_nvfp4(inp: dict, got: dict) -> None:
+    """Outside the slots' data and scale bytes, the NVFP4 caches keep their
+    sentinels; every scale byte of a live slot was written (E4M3 scale codes
+    are never 0x7F, the sentinel)."""
+    nkv = int(inp["nkv"])
+    kv = np.zeros(inp["kv_cache"].shape, bool)
+    ic = np.zeros(inp["index_cache"].shape, bool)
+    for slot in np.asarray(inp["slot_mapping"]):
+        if slot < 0:
+            continue
+        page, t = slot // 16, slot % 16
+        for m in (kv[page], ic[page][None, :]):
+            m[:, t * 64:(t + 1) * 64] = True
+        for s in range(2 * nkv):
+            v = s % 2 == 1
+            for g in range(8):
+                off = (t // 4 * 4 + g // 2) * 8 + g % 2 * 4 + t % 4 if v else 8 * t + g
+                kv[page, s, 1024 + off] = True
+        ic[page, 1024 + 8 * t: 1024 + 8 * t + 8] = True
+    for name, mask in (("kv_cache", kv), ("index_cache", ic)):
+        assert np.array_equal(got[name][~mask], inp[name][~mask]), f"{name}: a byte outside the slots changed"
+        scale_area = np.zeros(mask.shape, bool)
+        scale_area[..., 1024:] = True
+        written_scales = got[name][mask & scale_area]
+        assert np.all(written_scales != SENTINEL), f"{name}: a live slot's scale byte was not written"
 
 
 def expected_written_masks(inp: dict) -> dict:

@@ -155,7 +155,19 @@ def test_head_options_rejected(fn):
     assert _call_ex(fn, opts(0, 0.5, qf), ptrs, ws_bytes=16) == -6
     ptrs[19] = None  # iq_out is always required
     assert _call_ex(fn, opts(0, 0.5, qf), ptrs) == -1
-    assert B.load().pa_strerror(B.PA_ERR_OPTIONS).decode().startswith("q_fp8_scale")
+    assert B.load().pa_strerror(B.PA_ERR_OPTIONS).decode().startswith("bad pa_head_options")
+    # NVFP4: an unknown format, static scales with NVFP4, bad global scales
+    assert _call_ex(fn, opts(0, 1.0, None, 2, 1.0, 1.0)) == B.PA_ERR_OPTIONS
+    assert _call_ex(fn, opts(1, 1.0, None, B.PA_KV_NVFP4, 1.0, 1.0)) == B.PA_ERR_OPTIONS
+    for bad in (0.0, -2.0, float("inf"), float("nan"), 1e-39):
+        assert _call_ex(fn, opts(0, 1.0, None, B.PA_KV_NVFP4, bad, 1.0)) == B.PA_ERR_OPTIONS, bad
+        assert _call_ex(fn, opts(0, 1.0, None, B.PA_KV_NVFP4, 1.0, bad)) == B.PA_ERR_OPTIONS, bad
+    ptrs = [4096 * (i + 1) for i in range(21)]
+    ptrs[14] = ptrs[15] = ptrs[16] = None  # v_cache, k_scale, v_scale: unused with NVFP4
+    assert _call_ex(fn, opts(0, 1.0, None, B.PA_KV_NVFP4, 0.5, 2.0), ptrs, ws_bytes=16) == -6
+    assert _call_ex(fn, opts(0, 1.0, None, B.PA_KV_FP8, 1.0, 1.0), ptrs) == -1
+    ptrs[13] = 4096 + 8  # the NVFP4 K/V cache takes 16-byte pieces
+    assert _call_ex(fn, opts(0, 1.0, None, B.PA_KV_NVFP4, 0.5, 2.0), ptrs) == -2
 
 
 def test_decode_token_limit():

@@ -135,3 +135,58 @@ def test_plain_and_ex_calls_agree():
     b = p2.outputs()
     for k in a:
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+# ---------------------------------------------------------------- NVFP4 caches
+NV_SCALES = [(1.0, 1.0), (0.37, 1.9)]  # (K, V) global scales; non-powers of two round the reciprocals
+
+
+def _nvfp4_check(inp, ref, got, rows=None):
+    stats = parity.compare(inp, ref, got, rows=rows)
+    parity.check_written_sets_nvfp4(inp, got)
+    return stats
+
+
+@pytest.mark.parametrize("scales", NV_SCALES, ids=lambda v: f"gk{v[0]}_gv{v[1]}")
+@pytest.mark.parametrize("S,K,nkv,kw", DECODE_CASES, ids=lambda v: str(v))
+def test_decode_nvfp4(S, K, nkv, kw, scales):
+    wl = synth.Workload(name=f"decode_s{S}_k{K}_nkv{nkv}", mode="decode", tokens=S, hidden=K, nkv=nkv,
+                        max_pos=4096, num_pages=max(1, -(-S // 16) + 2), layout="random", **kw)
+    _say(f"decode nvfp4 {wl.name} {kw} {scales}")
+    inp = synth.with_nvfp4_caches(synth.make_workload(wl, seed=S * 17 + K), *scales)
+    ref = oracle.decode(inp)
+    _, got = _run_gpu(inp)
+    _say(f"  {_nvfp4_check(inp, ref, got)}")
+
+
+@pytest.mark.parametrize("scales", NV_SCALES, ids=lambda v: f"gk{v[0]}_gv{v[1]}")
+@pytest.mark.parametrize("S,K,nkv,kw", PREFILL_CASES, ids=lambda v: str(v))
+def test_prefill_nvfp4(S, K, nkv, kw, scales):
+    wl = synth.Workload(name=f"prefill_s{S}_k{K}_nkv{nkv}", mode="prefill", tokens=S, hidden=K, nkv=nkv,
+                        max_pos=4096, num_pages=max(1, -(-S // 16) + 2), layout="random", **kw)
+    _say(f"prefill nvfp4 {wl.name} {kw} {scales}")
+    inp = synth.with_nvfp4_caches(synth.make_workload(wl, seed=S * 19 + K), *scales)
+    ref = oracle.prefill(inp)
+    _, got = _run_gpu(inp)
+    _say(f"  {_nvfp4_check(inp, ref, got)}")
+
+
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
+def test_nvfp4_full_workload(key):
+    """NVFP4 caches with the FP8 q output on a full workload (prefill: sampled
+    tokens for the values, every slot for the written-byte set)."""
+    wl = synth.named_config(key)
+    _say(f"nvfp4 full {wl.name}")
+    inp = synth.with_nvfp4_caches(synth.make_workload(wl, seed=0), 0.37, 1.9)
+    inp["q_fp8_scale"] = 0.008
+    inp["q_bf16"] = True
+    p, got = _run_gpu(inp)
+    rows = None
+    if wl.mode == "decode":
+        ref = oracle.decode(inp)
+    else:
+        rng = np.random.default_rng(3)
+        rows = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 40, replace=False)]))
+        ref = oracle.prefill(parity.subset(inp, rows))
+    _say(f"  {_nvfp4_check(inp, ref, got, rows=rows)}")
+    del p
