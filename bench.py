@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--pool-mb", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--head-options", default="none", choices=["none", "static", "fp8q", "nvfp4"],
+                    help="time the pre_attn_*_ex head-step options: unit K/V scales, the FP8 q "
+                         "output (scale 0.008) besides bf16 q, or NVFP4 caches (global scales "
+                         "0.37 / 1.9)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (the known-size "
@@ -61,7 +65,7 @@ def calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 10}))
 
 
-def algorithmic(wl, structure=0):
+def algorithmic(wl, structure=0, head_options="none"):
     """(bytes per call, bytes of the dominant kernel per launch, flops per call,
     the dominant kernel's name).
 
@@ -74,9 +78,14 @@ def algorithmic(wl, structure=0):
     S, K, nkv = wl.tokens, wl.hidden, wl.nkv
     N = (19 * nkv + 1) * 128
     norm_bytes = 4 * S * K + 2 * S * K + 2 * K  # ar + res in, h_out out, g_in
+    # cache writes: FP8 K and V codes + scales per KV head and the index row, or
+    # NVFP4 slots of 64 data + 8 scale bytes for K, V and index_k
+    cache_bytes = S * (2 * nkv + 1) * 72 if head_options == "nvfp4" else S * nkv * (256 + 8) + 128 * S
     call_bytes = (N * K + 4 * N + norm_bytes + 4 * 256
-                  + S * 16 * nkv * 256 + S * nkv * 256 + S * nkv * (256 + 8) + 128 * S
+                  + S * 16 * nkv * 256 + S * nkv * 256 + cache_bytes
                   + 128 * S + 16 * S)
+    if head_options == "fp8q":
+        call_bytes += S * 16 * nkv * 128
     flops = 2 * S * N * K
     if wl.mode == "prefill":
         call_bytes += N * K // 32 - 4 * N  # E8M0 block scales instead of row scales
@@ -168,12 +177,18 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.named_config(args.config)
     inp = synth.make_workload(wl, seed=0)
+    if args.head_options == "static":
+        inp["static_kv_scale"] = True
+    elif args.head_options == "fp8q":
+        inp["q_fp8_scale"] = 0.008
+    elif args.head_options == "nvfp4":
+        inp = synth.with_nvfp4_caches(inp, 0.37, 1.9)
     prob = Problem(inp)
     dev = prob.device
     S, K = wl.tokens, wl.hidden
     N = prob.N
     structure = B.pa_decode_structure(prob.dims) if prob.mode == B.PA_MODE_DECODE else 0
-    call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, structure)
+    call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, structure, args.head_options)
 
     # rotating pool of distinct weight + activation sets
     set_bytes = prob.w_packed.numel() + prob.w_scales.numel() * prob.w_scales.element_size() \
@@ -256,7 +271,7 @@ def main():
     B.pa_workspace_status(prob.workspace)  # raises if an in-kernel wait gave up
 
     key = args.config
-    traffic = measured_traffic(key, wl.mode)
+    traffic = measured_traffic(key, wl.mode) if args.head_options == "none" else None
     if wl.mode == "decode":
         metric, unit = "decode tokens/s", "tokens/s"
         value = S * args.steps / elapsed
@@ -287,7 +302,8 @@ def main():
         "dtype": "fp8_e4m3" if wl.mode == "decode" else "mxfp8_e4m3",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": S, "hidden": K, "nkv": wl.nkv, "n_rows": N,
-                   "pool_sets": n_sets, "timing": "hip graph replay" if graph else "eager"},
+                   "pool_sets": n_sets, "timing": "hip graph replay" if graph else "eager",
+                   **({} if args.head_options == "none" else {"head_options": args.head_options})},
         "roofline": roof,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 5),
         **extra,

@@ -190,3 +190,29 @@ def test_nvfp4_full_workload(key):
         ref = oracle.prefill(parity.subset(inp, rows))
     _say(f"  {_nvfp4_check(inp, ref, got, rows=rows)}")
     del p
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_nvfp4_and_fp8q_degenerate_rows(mode):
+    """An all-zero row (ar = -res: every group below the scale floor, zero codes,
+    signed-zero q codes), position 0 (identity RoPE), the last table row and a slot of -1,
+    with NVFP4 caches and the FP8 q output only."""
+    wl = synth.Workload(name=f"{mode}_degenerate", mode=mode, tokens=6, hidden=256, nkv=1, max_pos=64,
+                        num_pages=3, layout="random")
+    inp = synth.make_workload(wl, seed=3)
+    inp["res"][0] = inp["ar"][0] ^ 0x8000  # bf16 negation: acc row 0 == 0
+    inp["positions"][1] = 0
+    inp["positions"][2] = 63
+    inp["slot_mapping"][3] = -1
+    inp = synth.with_nvfp4_caches(inp, 0.37, 1.9)
+    inp["q_fp8_scale"] = 0.02
+    inp["q_bf16"] = False
+    ref = oracle.decode(inp) if mode == "decode" else oracle.prefill(inp)
+    _, got = _run_gpu(inp)
+    assert "q_out" not in got
+    _say(f"  {_nvfp4_check(inp, ref, got)}")
+    assert np.all((got["q_fp8"][0] & 0x7F) == 0)  # the zero row's q codes are signed zeros
+    page, t = inp["slot_mapping"][0] // 16, inp["slot_mapping"][0] % 16
+    for sl in range(2):  # K and V of the zero row: zero codes, floor scales (E4M3 2^-9 = 0x01)
+        assert np.all(got["kv_cache"][page, sl, t * 64:(t + 1) * 64] == 0)
+    assert np.all(got["kv_cache"][page, 0, 1024 + 8 * t:1024 + 8 * t + 8] == 0x01)
