@@ -188,8 +188,7 @@ int run(int mode, const pa_dims* dims, const Ptrs& p, const pa_head_options* opt
   pa::Args a = make_args(dims, p, stream);
   a.q_fp8 = o.q_fp8;
   a.q_fp8_inv = o.q_fp8_inv;
-  a.static_kv = o.static_kv;
-  a.kv_nvfp4 = o.nvfp4;
+  a.opts = (o.static_kv ? pa::kOptStaticKv : 0u) | (o.nvfp4 ? pa::kOptNvfp4 : 0u);
   a.k_gs = o.k_gs;
   a.v_gs = o.v_gs;
   hipError_t e;

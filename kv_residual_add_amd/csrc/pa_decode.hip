@@ -25,6 +25,12 @@
 // measured slower than kernel boundaries under graph replay; one inside an
 // XCD's L2 did not.
 //
+// Head-step options (pre_attn_decode_ex, runtime flags read by the epilogue):
+// unit K / V scales (the K1 mono_pre page's STATIC_KV_SCALE), an FP8 q output
+// (the epilogue page's q_fp8_out), and the epilogue page's NVFP4 K / V /
+// index_k caches (E2M1 codes with an E4M3 scale per 16 values, 16-lane group
+// maxima by shuffles).
+//
 // Numerics: the input norm, its FP8 decision and the head epilogue run in
 // float64 with contraction off, so a code is decided from the same value the
 // float64 statement of the method gives; the projection's products are exact
@@ -99,7 +105,7 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
 // which take the row's rstd and scale from *rstd_out and *s_out (every thread
 // receives them).
 template <int NV, bool CODES = true>
-__device__ __forceinline__ void norm_token(const Args& a, int row, uint8_t* __restrict__ x8,
+__device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __restrict__ x8,
                                            float* __restrict__ sx, double* red, int tl, bool write_h = true,
                                            double* rstd_out = nullptr, float* s_out = nullptr) {
 #pragma clang fp contract(off)
@@ -271,7 +277,7 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_
 // once the XCD's norm CTAs have published each token's rstd and scale, the CTA
 // forms its slice's FP8 codes itself (codes8) straight into LDS.
 template <int CPC, int NT, bool FUSED>
-__device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
+__device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
                                           const Publish& pub) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -388,7 +394,7 @@ __device__ __forceinline__ void gemv_tile(const Args& a, int h, int ks, const ui
 }
 
 template <int CPC, int NT>
-__global__ __launch_bounds__(256) void decode_gemv(Args a, size_t off_x8, size_t off_part) {
+__global__ __launch_bounds__(256) void decode_gemv(KArgs a, size_t off_x8, size_t off_part) {
   const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
                      Publish{nullptr, nullptr, nullptr});
@@ -429,8 +435,11 @@ __device__ __forceinline__ void nvfp4_row_wave(float x0, float x1, float gs, boo
   }
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, const float* __restrict__ part,
+// OPT: the head-step options (unit K / V scales, FP8 q, NVFP4 caches) are read
+// from the arguments; without it the plain path is compiled alone, since these
+// short kernels fetch their code cold and every extra instruction costs.
+template <bool COHERENT, bool OPT>
+__device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, const float* __restrict__ part,
                                               const float* __restrict__ sx, int ksplit, int tlb) {
 #pragma clang fp contract(off)
   const int N = a.N();
@@ -489,7 +498,7 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
 
-  if (h >= v0 && h < iq0 && a.kv_nvfp4) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
+  if (OPT && h >= v0 && h < iq0 && a.kv_nvfp4()) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
     if (store_cache)
       nvfp4_row_wave(static_cast<float>(y0), static_cast<float>(y1), a.v_gs, true,
                      a.k_cache + (page * 2 * nkv + 2 * (h - v0) + 1) * kNvSlotBytes, t, true, lane);
@@ -497,7 +506,7 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   }
   if (h >= v0 && h < iq0) {  // V: the raw projection, per-token scale (1 when static)
     const int j = h - v0;
-    const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
+    const double amax = OPT && a.static_kv() ? 0.0 : wave_max_f64(fmax(__builtin_fabs(y0), __builtin_fabs(y1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
@@ -522,24 +531,24 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
 
   if (h < k0) {
     const size_t qrow = (static_cast<size_t>(tok) * k0 + h) * kHeadDim;
-    if (a.q_out != nullptr) {
+    if (!OPT || a.q_out != nullptr) {
       uint16_t* q = a.q_out + qrow;
       q[d0] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o0)));
       q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
     }
-    if (a.q_fp8 != nullptr) {  // E4M3 of the float32 product q * (1 / q_fp8_scale)
+    if (OPT && a.q_fp8 != nullptr) {  // E4M3 of the float32 product q * (1 / q_fp8_scale)
       const float p0 = static_cast<float>(o0) * a.q_fp8_inv, p1 = static_cast<float>(o1) * a.q_fp8_inv;
       const uint32_t c2 = e4m3x2_scaled(static_cast<double>(p0), static_cast<double>(p1), fp8_scale(0));
       a.q_fp8[qrow + d0] = static_cast<uint8_t>(c2);
       a.q_fp8[qrow + d1] = static_cast<uint8_t>(c2 >> 8);
     }
-  } else if (h < v0 && a.kv_nvfp4) {  // K, NVFP4: slot 2j, linear scale bytes
+  } else if (OPT && h < v0 && a.kv_nvfp4()) {  // K, NVFP4: slot 2j, linear scale bytes
     if (store_cache)
       nvfp4_row_wave(static_cast<float>(o0), static_cast<float>(o1), a.k_gs, true,
                      a.k_cache + (page * 2 * nkv + 2 * (h - k0)) * kNvSlotBytes, t, false, lane);
   } else if (h < v0) {  // K: per-token scale (1 when static), shuffled page-16 layout
     const int j = h - k0;
-    const double amax = a.static_kv ? 0.0 : wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
+    const double amax = OPT && a.static_kv() ? 0.0 : wave_max_f64(fmax(__builtin_fabs(o0), __builtin_fabs(o1)));
     const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
     if (store_cache) {
       const double sd = static_cast<double>(s), rcp = 1.0 / sd;
@@ -554,7 +563,7 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
     uint16_t* q = a.iq_out + (static_cast<size_t>(tok) * nkv + j) * kHeadDim;
     q[d0] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o0)));
     q[d1] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o1)));
-  } else if (store_cache && a.kv_nvfp4) {  // index_k, NVFP4: the page's one slot, no global scale
+  } else if (OPT && store_cache && a.kv_nvfp4()) {  // index_k, NVFP4: the page's one slot, no global scale
     nvfp4_row_wave(static_cast<float>(o0), static_cast<float>(o1), 1.0f, false,
                    a.index_cache + page * kNvSlotBytes, t, false, lane);
   } else if (store_cache) {  // index_k: unit-scale E4M3 into the slot's row
@@ -565,15 +574,16 @@ __device__ __forceinline__ void head_epilogue(const Args& a, int h, int tok, con
   }
 }
 
-__global__ __launch_bounds__(64) void decode_epilogue(Args a, size_t off_part, size_t off_sx, int ksplit) {
+template <bool OPT>
+__global__ __launch_bounds__(64) void decode_epilogue(KArgs a, size_t off_part, size_t off_sx, int ksplit) {
   const int H = a.heads();
-  head_epilogue<false>(a, blockIdx.x % H, blockIdx.x / H, reinterpret_cast<const float*>(a.ws + off_part),
+  head_epilogue<false, OPT>(a, blockIdx.x % H, blockIdx.x / H, reinterpret_cast<const float*>(a.ws + off_part),
                        reinterpret_cast<const float*>(a.ws + off_sx), ksplit, a.S + H * ksplit + blockIdx.x);
 }
 
 // A GEMV CTA of XCD x is done with the XCD's published values: the last of the
 // XCD's gx GEMV CTAs (counted with a device-scope atomic) clears them.
-__device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int x, int gx, uint64_t* pub_r,
+__device__ __forceinline__ void xcd_done(const KArgs& a, const DecodePlan& p, int x, int gx, uint64_t* pub_r,
                                          uint64_t* pub_s) {
   uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
   if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(gx - 1)) {
@@ -602,8 +612,8 @@ __device__ __forceinline__ void xcd_done(const Args& a, const DecodePlan& p, int
 // waits for them, and the only wait is bounded. The last GEMV CTA of an XCD
 // clears the XCD's published values, a head's epilogue CTA the slice flags, for the
 // next call.
-template <int CPC, int NV, bool EPI>
-__global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
+template <int CPC, int NV, bool EPI, bool OPT>
+__global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
   __shared__ double red[16];
   const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
@@ -650,7 +660,7 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
     __syncthreads();
     const int wave = threadIdx.x >> 6;
     for (int tok = wave; tok < S; tok += 4)
-      head_epilogue<true>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
+      head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
     if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
   }
   if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, pub_r, pub_s);
@@ -665,8 +675,8 @@ __global__ __launch_bounds__(256) void decode_fused(Args a, DecodePlan p) {
 // slice past the wait (a per-head counter) clears the flags for the next call.
 // A head's slices are dispatched together (a contiguous run of its XCD's
 // blocks, at most one per CU of the XCD), and every wait is bounded.
-template <int CPC, int NT>
-__global__ __launch_bounds__(256) void decode_gemv_epi(Args a, DecodePlan p) {
+template <int CPC, int NT, bool OPT>
+__global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   const int b = blockIdx.x, x = b & 7, j = b >> 3, H = a.heads(), ksplit = p.ksplit;
   const int h = x + 8 * (j / ksplit), ks = j % ksplit;
   if (h >= H) return;  // XCDs with fewer heads have idle blocks
@@ -688,13 +698,13 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(Args a, DecodePlan p) {
   }
   const int wave = threadIdx.x >> 6;
   for (int tok = ks + ksplit * wave; tok < a.S; tok += 4 * ksplit)
-    head_epilogue<true>(a, h, tok, part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+    head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, a.S + H * ksplit + tok * H + h);
 }
 
 // ---------------------------------------------------------------------------
 // norm kernel: blockDim.x threads (a multiple of 64, at most 1024)
 template <int NV>
-__global__ __launch_bounds__(1024) void decode_norm(Args a, size_t off_x8, size_t off_sx) {
+__global__ __launch_bounds__(1024) void decode_norm(KArgs a, size_t off_x8, size_t off_sx) {
   __shared__ double red[16];
   norm_token<NV>(a, blockIdx.x, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_sx), red,
                  blockIdx.x);
@@ -734,11 +744,19 @@ hipError_t launch_gemv(const Args& a, const DecodePlan& p) {
   return hipGetLastError();
 }
 
+// whether a call uses any head-step option (the OPT kernel instantiations)
+bool has_options(const Args& a) {
+  return a.q_fp8 != nullptr || a.static_kv() || a.kv_nvfp4() || a.q_out == nullptr;
+}
+
 template <int CPC, int NT>
 hipError_t launch_gemv_epi(const Args& a, const DecodePlan& p) {
   const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
   const dim3 grid(8 * ((a.heads() + 7) / 8) * p.ksplit);
-  hipLaunchKernelGGL((decode_gemv_epi<CPC, NT>), grid, dim3(256), lds, a.stream, a, p);
+  if (has_options(a))
+    hipLaunchKernelGGL((decode_gemv_epi<CPC, NT, true>), grid, dim3(256), lds, a.stream, a, p);
+  else
+    hipLaunchKernelGGL((decode_gemv_epi<CPC, NT, false>), grid, dim3(256), lds, a.stream, a, p);
   return hipGetLastError();
 }
 
@@ -748,25 +766,37 @@ hipError_t launch_gemv_nt(const Args& a, const DecodePlan& p) {
   return a.S <= 32 ? launch_gemv<CPC, 1>(a, p) : launch_gemv<CPC, 2>(a, p);
 }
 
-template <int CPC, bool EPI>
+template <int CPC, bool EPI, bool OPT>
 hipError_t launch_fused_e(const Args& a, const DecodePlan& p) {
   const int nv = (a.K / 8 + 255) / 256;  // 8-element vectors a norm thread holds
   const int gemv = EPI ? 8 * ((a.heads() + 7) / 8) * p.ksplit : a.heads() * p.ksplit;
   const dim3 grid(8 * a.S + gemv);
   const size_t lds = static_cast<size_t>(a.S) * (CPC * 128 + kLdsPad);
   switch (nv) {
-    case 1: hipLaunchKernelGGL((decode_fused<CPC, 1, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
-    case 2: hipLaunchKernelGGL((decode_fused<CPC, 2, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
-    case 3: hipLaunchKernelGGL((decode_fused<CPC, 3, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
-    case 4: hipLaunchKernelGGL((decode_fused<CPC, 4, EPI>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 1: hipLaunchKernelGGL((decode_fused<CPC, 1, EPI, OPT>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 2: hipLaunchKernelGGL((decode_fused<CPC, 2, EPI, OPT>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 3: hipLaunchKernelGGL((decode_fused<CPC, 3, EPI, OPT>), grid, dim3(256), lds, a.stream, a, p); break;
+    case 4: hipLaunchKernelGGL((decode_fused<CPC, 4, EPI, OPT>), grid, dim3(256), lds, a.stream, a, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_epilogue(const Args& a, const DecodePlan& p) {
+  if (has_options(a))
+    hipLaunchKernelGGL(decode_epilogue<true>, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part, p.off_sx,
+                       p.ksplit);
+  else
+    hipLaunchKernelGGL(decode_epilogue<false>, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part, p.off_sx,
+                       p.ksplit);
+  return hipGetLastError();
+}
+
 template <int CPC>
 hipError_t launch_fused(const Args& a, const DecodePlan& p) {
-  return p.fused_epilogue ? launch_fused_e<CPC, true>(a, p) : launch_fused_e<CPC, false>(a, p);
+  // without the epilogue in it the launch never reads the options
+  if (!p.fused_epilogue) return launch_fused_e<CPC, false, false>(a, p);
+  return has_options(a) ? launch_fused_e<CPC, true, true>(a, p) : launch_fused_e<CPC, true, false>(a, p);
 }
 
 }  // namespace
@@ -835,9 +865,7 @@ hipError_t launch_decode(const Args& a, const DecodePlan& p) {
     if (e != hipSuccess) return e;
     if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
     if (p.fused_epilogue) return hipSuccess;
-    hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part,
-                       p.off_sx, p.ksplit);
-    return hipGetLastError();
+    return launch_epilogue(a, p);
   }
   // norm: one thread per 8-element vector up to 1024 threads, then loop
   const int vecs = a.K / 8;
@@ -862,9 +890,7 @@ hipError_t launch_decode(const Args& a, const DecodePlan& p) {
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
   if (p.gemv_epilogue) return hipSuccess;
-  hipLaunchKernelGGL(decode_epilogue, dim3(a.S * a.heads()), dim3(64), 0, a.stream, a, p.off_part,
-                     p.off_sx, p.ksplit);
-  return hipGetLastError();
+  return launch_epilogue(a, p);
 }
 
 hipError_t launch_pack_decode(const uint8_t* w, uint8_t* wp, int N, int K, hipStream_t s) {

@@ -11,8 +11,13 @@ namespace pa {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Everything a prologue launch reads or writes (device pointers).
-struct Args {
+// Everything a prologue kernel reads or writes (device pointers), passed by
+// value as the kernels' argument block: host-only state stays in Args below,
+// so the block does not grow with it.
+constexpr uint32_t kOptStaticKv = 1u;  // unit K / V scales
+constexpr uint32_t kOptNvfp4 = 2u;     // NVFP4 caches (k_cache = K/V cache, index_cache NVFP4)
+
+struct KArgs {
   int S, K, nkv, num_pages, max_pos;
   float eps;
   const uint16_t *ar, *res, *g_in;
@@ -27,16 +32,21 @@ struct Args {
   uint16_t *q_out, *iq_out;      // q_out may be NULL when q_fp8 is set
   uint8_t* q_fp8;                // optional E4M3 q [S][16 nkv][128]
   float q_fp8_inv;               // float32(1 / q_fp8_scale)
-  int static_kv;                 // nonzero: unit K / V scales
-  int kv_nvfp4;                  // nonzero: NVFP4 caches (k_cache = K/V cache, index_cache NVFP4)
+  uint32_t opts;                 // kOpt* flags
   float k_gs, v_gs;              // NVFP4: float32(1 / global scale) of K and V
   uint8_t* ws;
-  hipStream_t stream;
-  hipEvent_t ev_start, ev_stop;  // optional, around the dominant kernel
   uint64_t* timeline;            // optional per-CTA phase stamps (s_memrealtime)
   uint32_t timeline_slots;       // stamps available in `timeline`
   __host__ __device__ int N() const { return (19 * nkv + 1) * 128; }
   __host__ __device__ int heads() const { return 19 * nkv + 1; }
+  __host__ __device__ bool static_kv() const { return (opts & kOptStaticKv) != 0; }
+  __host__ __device__ bool kv_nvfp4() const { return (opts & kOptNvfp4) != 0; }
+};
+
+// A call: the kernels' arguments plus the host-side launch state.
+struct Args : KArgs {
+  hipStream_t stream;
+  hipEvent_t ev_start, ev_stop;  // optional, around the dominant kernel
 };
 
 // The words kernels synchronize through (flags, counters, published

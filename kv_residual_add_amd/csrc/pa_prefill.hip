@@ -25,6 +25,10 @@
 //                       K1 mono_pre head tasks) runs on the f32 accumulator;
 //                       the projection is never written to memory.
 //
+// Head-step options (pre_attn_prefill_ex) as in decode: unit K / V scales,
+// an FP8 q output, NVFP4 K / V / index_k caches (lane-local 16-value groups;
+// K and index_k stage their float32 values in the lane's own LDS row half).
+//
 // Numerics: as in decode, the norm / MX decision and the head epilogue run in
 // float64 with contraction off.
 #include <hip/hip_runtime.h>
@@ -249,7 +253,7 @@ struct Panels {
 };
 
 template <int NTW>
-__device__ __forceinline__ Panels make_panels(const Args& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
+__device__ __forceinline__ Panels make_panels(const KArgs& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
   const size_t nks = a.K / kKStep;
   Panels p;
   p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
@@ -382,7 +386,7 @@ __device__ __forceinline__ void pipeline_step(Stage<PRECISE, NTW, SUB> (&st)[kSl
 }
 
 template <bool PRECISE, int NTW, int SUB>
-__device__ __forceinline__ void mainloop(const Args& a, int h, int tt0, const uint8_t* __restrict__ xq,
+__device__ __forceinline__ void mainloop(const KArgs& a, int h, int tt0, const uint8_t* __restrict__ xq,
                                          const uint8_t* __restrict__ xs, uint8_t* const (&ring)[kSlots], int wave,
                                          f32x16 (&acc)[NTW][4]) {
   const int nks = a.K / kKStep;
@@ -443,7 +447,7 @@ struct EpiIn {
   u32x4 sn[4];  // sin of rotary index 8j .. + 7
 };
 
-__device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int64_t pos) {
+__device__ __forceinline__ EpiIn epilogue_loads(const KArgs& a, int64_t pos) {
   const int half = (threadIdx.x & 63) >> 5;
   EpiIn in;
   if (half == 0) {
@@ -459,7 +463,7 @@ __device__ __forceinline__ EpiIn epilogue_loads(const Args& a, int64_t pos) {
 }
 
 // the gamma row of head h's role
-__device__ __forceinline__ const uint16_t* head_gamma(const Args& a, int h) {
+__device__ __forceinline__ const uint16_t* head_gamma(const KArgs& a, int h) {
   const int nkv = a.nkv;
   return h < 16 * nkv ? a.g_q : (h < 17 * nkv ? a.g_k : (h < 19 * nkv ? a.g_iq : a.g_ik));
 }
@@ -554,7 +558,7 @@ __device__ __forceinline__ void nv_k_half(const TileRow& x, const uint16_t* gam,
   nv_half_from_tile(x, c0, gs, has_gs, slot, t, half, false);
 }
 
-__device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, const uint16_t* gam, int h, int tok,
+__device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, const uint16_t* gam, int h, int tok,
                                               int64_t slot, const EpiIn& in) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
@@ -569,7 +573,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   const int64_t page = slot_page(slot);
   const int t = slot_row(slot);
 
-  if (h >= v0 && h < iq0 && a.kv_nvfp4) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
+  if (h >= v0 && h < iq0 && a.kv_nvfp4()) {  // V, NVFP4: slot 2j + 1, swizzled scale bytes
     if (store_cache)
       nv_half_from_tile(x, c0, a.v_gs, true, a.k_cache + (page * 2 * nkv + 2 * (h - v0) + 1) * kNvSlotBytes, t, half,
                         true);
@@ -579,7 +583,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   if (h >= v0 && h < iq0) {  // V: raw projection, per-token scale (1 when static)
     const int j = h - v0;
     float am = 0.f;
-    if (!a.static_kv) {
+    if (!a.static_kv()) {
 #pragma unroll 4
       for (int i = 0; i < 64; i += 4) {
         const float4 v = x.chunk(c0 + (i >> 2));
@@ -709,7 +713,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   // K and index_k share one copy of the f64 group code: pass kAmax finds the K
   // row's scale, pass kCodes writes E4M3 codes (K with its scale into the
   // shuffled page layout, index_k with unit scale into its row).
-  if (a.kv_nvfp4) {  // K into slot 2j, index_k into the page's slot, linear scale bytes
+  if (a.kv_nvfp4()) {  // K into slot 2j, index_k into the page's slot, linear scale bytes
     if (!store_cache) return;
     uint8_t* slot_base =
         h < v0 ? a.k_cache + (page * 2 * nkv + 2 * (h - k0)) * kNvSlotBytes : a.index_cache + page * kNvSlotBytes;
@@ -722,7 +726,7 @@ __device__ __forceinline__ void tile_epilogue(const Args& a, const TileRow& x, c
   uint8_t* cbase = nullptr;
   int cstride = 0;  // bytes between 16-dim groups of the code row
   double sd = 1.0, rcp = 1.0;
-  if (h < v0 && a.static_kv) {  // K with the unit scale: codes of the values themselves
+  if (h < v0 && a.static_kv()) {  // K with the unit scale: codes of the values themselves
     if (!store_cache) return;
     if (lane < 32) a.k_scale[(page * nkv + (h - k0)) * kPage + t] = 1.0f;
     mode = kCodes;
@@ -813,7 +817,7 @@ struct HeadMap {
 // fastest, so CTAs dispatched together share token tiles. The mapping is a
 // bijection onto the tiles whatever the hardware's placement.
 template <int NTW>
-__global__ __launch_bounds__(256, 2) void prefill_gemm(Args a, const uint8_t* __restrict__ xq,
+__global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int mtiles, HeadMap map) {
   // the weight ring; afterwards slot w holds wave w's output tile
   __shared__ __align__(16) uint8_t ring0[kSlotBytes];
