@@ -96,18 +96,75 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
   return r;
 }
 
+// One block reduction of (sum, top two of per-thread maxima) over up to 16
+// waves: the sum in the same fixed order as block_sum_f64; m1 the largest
+// contribution and m2 the second largest, counting each thread once (the DPP
+// steps and the LDS tree combine disjoint sets of threads, as for the sum).
+// Values are >= 0. red holds 48 doubles.
+__device__ __forceinline__ void top2_merge(double& m1, double& m2, double b1, double b2) {
+  const double lo = __builtin_fmin(m1, b1);
+  m1 = __builtin_fmax(m1, b1);
+  m2 = __builtin_fmax(lo, __builtin_fmax(m2, b2));
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void dpp_sum_top2(double& v, double& m1, double& m2) {
+  const double bv = dpp_f64<kCtrl, kRowMask>(v, 0.0);
+  const double b1 = dpp_f64<kCtrl, kRowMask>(m1, 0.0);
+  const double b2 = dpp_f64<kCtrl, kRowMask>(m2, 0.0);
+  v += bv;
+  top2_merge(m1, m2, b1, b2);
+}
+
+__device__ __forceinline__ void block_sum_top2_f64(double& v, double& m1, double& m2, double* red) {
+  dpp_sum_top2<0xB1, 0xf>(v, m1, m2);   // quad_perm [1,0,3,2]
+  dpp_sum_top2<0x4E, 0xf>(v, m1, m2);   // quad_perm [2,3,0,1]
+  dpp_sum_top2<0x141, 0xf>(v, m1, m2);  // row_half_mirror
+  dpp_sum_top2<0x140, 0xf>(v, m1, m2);  // row_mirror
+  dpp_sum_top2<0x142, 0xa>(v, m1, m2);  // row_bcast:15 into rows 1, 3
+  dpp_sum_top2<0x143, 0xc>(v, m1, m2);  // row_bcast:31 into rows 2, 3
+  v = lane63_f64(v);
+  m1 = lane63_f64(m1);
+  m2 = lane63_f64(m2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = static_cast<int>(blockDim.x >> 6);
+  if (lane == 0) red[wave] = v, red[16 + wave] = m1, red[32 + wave] = m2;
+  if (threadIdx.x < 16 && threadIdx.x >= nw) red[threadIdx.x] = 0.0, red[16 + threadIdx.x] = 0.0, red[32 + threadIdx.x] = 0.0;
+  __syncthreads();
+  double t[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) t[w] = red[w] + red[w + 8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) t[w] += t[w + 4];
+  v = (t[0] + t[2]) + (t[1] + t[3]);
+  double a1 = red[16], a2 = red[32];
+  for (int w = 1; w < 16; ++w) top2_merge(a1, a2, red[16 + w], red[32 + w]);
+  m1 = a1;
+  m2 = a2;
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // norm: residual add + Gemma RMSNorm + per-token FP8 for token `row`; thread
 // t owns the 8-element vectors t, t + blockDim.x, ... (NV of them). The element
 // loops stay rolled: each wave runs this code once, so its size, not its
 // instruction count, sets the time.
 // With CODES false the row's FP8 codes are left to the GEMV CTAs (codes8),
-// which take the row's rstd and scale from *rstd_out and *s_out (every thread
-// receives them).
+// which take the row's rstd and scale from *rstd_out and *s_out (rstd in every
+// thread, the scale in the row's owner thread, see below).
+// Without CODES the row's scale comes from one block reduction instead of two:
+// the exact products y = |acc| (1 + g) (a float32 times a 9-bit value, exact in
+// float64) order the normalized values |xn| = RN(RN(|acc| rstd) (1 + g)) except
+// within 2^-50 relative of each other. When the largest per-thread y is clear
+// of the second by more than that, the one thread holding it computes the
+// row's max |xn| from its own values and is the row's owner (*owner_out): it
+// alone holds the scale. Otherwise (near-ties, or an all-zero row) the second
+// reduction runs as with CODES and thread 0 is the owner.
 template <int NV, bool CODES = true>
 __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __restrict__ x8,
                                            float* __restrict__ sx, double* red, int tl, bool write_h = true,
-                                           double* rstd_out = nullptr, float* s_out = nullptr) {
+                                           double* rstd_out = nullptr, float* s_out = nullptr,
+                                           bool* owner_out = nullptr) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -129,10 +186,12 @@ __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __r
   float acc[NV][8];
   double ssp[4] = {0.0, 0.0, 0.0, 0.0};  // four chains, combined pairwise
   uint32_t hw[NV][4];  // the bf16 residual, stored with the codes at the end
+  double ymine = 0.0, y1 = 0.0, y2 = 0.0;  // this thread's largest y; the row's two largest
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const uint32_t aw[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
     const uint32_t bw[4] = {bv[i].x, bv[i].y, bv[i].z, bv[i].w};
+    const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[i][2 * q] = bf16_to_f32(aw[q] & 0xffffu) + bf16_to_f32(bw[q] & 0xffffu);
@@ -141,10 +200,23 @@ __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __r
       // a float32 square is exact in float64: the fma rounds only the sum
       ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q]), static_cast<double>(acc[i][2 * q]), ssp[q]);
       ssp[q] = __builtin_fma(static_cast<double>(acc[i][2 * q + 1]), static_cast<double>(acc[i][2 * q + 1]), ssp[q]);
+      if constexpr (!CODES) {
+        ymine = __builtin_fmax(ymine, __builtin_fabs(static_cast<double>(acc[i][2 * q]) *
+                                                     (1.0 + static_cast<double>(bf16_to_f32(gw[q] & 0xffffu)))));
+        ymine = __builtin_fmax(ymine, __builtin_fabs(static_cast<double>(acc[i][2 * q + 1]) *
+                                                     (1.0 + static_cast<double>(bf16_to_f32(gw[q] >> 16)))));
+      }
     }
   }
   stamp(a.timeline, a.timeline_slots, tl, 1);
-  const double ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
+  double ss;
+  if constexpr (CODES) {
+    ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
+  } else {
+    ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
+    y1 = ymine;
+    block_sum_top2_f64(ss, y1, y2, red);
+  }
   stamp(a.timeline, a.timeline_slots, tl, 2);
   const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(a.eps));
   double xn[NV][8];
@@ -164,7 +236,14 @@ __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __r
     amax = __builtin_fmax(amax, mm);
   }
   stamp(a.timeline, a.timeline_slots, tl, 3);
-  amax = block_max_f64(amax, red);
+  bool owner = threadIdx.x == 0;
+  // one clear maximum (uniform: every thread holds the same y1, y2): its thread's
+  // own max |xn| is the row's; else the second reduction
+  const bool clear = !CODES && y2 < y1 * (1.0 - 0x1p-50);
+  if (clear)
+    owner = ymine == y1;
+  else
+    amax = block_max_f64(amax, red);
   stamp(a.timeline, a.timeline_slots, tl, 4);
   const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
   const double sd = static_cast<double>(s);
@@ -182,9 +261,10 @@ __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __r
     if (v < nvec && write_h)
       *reinterpret_cast<uint4*>(a.h_out + base + 8 * v) = make_uint4(hw[i][0], hw[i][1], hw[i][2], hw[i][3]);
   }
-  if (tid == 0) sx[row] = s;
+  if (owner) sx[row] = s;
   if (rstd_out != nullptr) *rstd_out = rstd;
   if (s_out != nullptr) *s_out = s;
+  if (owner_out != nullptr) *owner_out = owner;
   stamp(a.timeline, a.timeline_slots, tl, 5);
 }
 
@@ -614,7 +694,7 @@ __device__ __forceinline__ void xcd_done(const KArgs& a, const DecodePlan& p, in
 // next call.
 template <int CPC, int NV, bool EPI, bool OPT>
 __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
-  __shared__ double red[16];
+  __shared__ double red[48];
   const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
   uint64_t* pub_r = reinterpret_cast<uint64_t*>(a.ws + p.off_rstd) + x * 2 * kSxStride;
@@ -623,8 +703,9 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
     const int tok = b >> 3;
     double rstd;
     float sc;
-    norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, &rstd, &sc);
-    if (threadIdx.x == 0) {
+    bool owner;
+    norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, &rstd, &sc, &owner);
+    if (owner) {  // the thread that holds the row's scale
       __builtin_amdgcn_s_waitcnt(0);  // sx (read by the epilogue) is in the L2 before the values are
       pub_r[tok] = static_cast<uint64_t>(__double_as_longlong(rstd));
       pub_s[tok] = (uint64_t{1} << 32) | __float_as_uint(sc);

@@ -289,3 +289,43 @@ def test_positions_out_of_range_are_clamped():
     _, got = _gpu(inp)
     parity.compare(inp, ref, got)
 
+
+
+def _bf16_of(x):
+    import struct
+    return struct.unpack("<I", struct.pack("<f", float(x)))[0] >> 16  # exact for the values used
+
+
+@pytest.mark.parametrize("K", [1024, 6144])
+def test_fused_norm_scale_with_exact_ties(K):
+    # The one-launch decode norm takes the row's FP8 scale from the thread that
+    # holds the largest |acc| (1 + g) when it is unique, and from a second block
+    # reduction on an exact tie (distinct products are never within 2^-50 of
+    # each other). Rows 0 and 1 tie across threads 0 and 1 (elements 0 and 8),
+    # with the same and with different factors; rows 2 and 3 have a unique
+    # maximum. Every XCD's copy of the per-token scale must equal the oracle's.
+    from kv_residual_add_amd import _binding as B
+    from kv_residual_add_amd.runner import Problem
+
+    wl = _wl("decode", 4, K, 1, max_pos=64)
+    inp = synth.make_workload(wl, seed=9)
+    g = inp["g_in"].copy()
+    g[0], g[8] = _bf16_of(0.25), 0
+    inp["g_in"] = g
+    for r, (a0, a8) in enumerate(((40.0, 50.0), (48.0, 60.0))):  # 40 * 1.25 = 50, 48 * 1.25 = 60
+        inp["ar"][r, 0], inp["ar"][r, 8] = _bf16_of(a0), _bf16_of(a8)
+        inp["res"][r, 0], inp["res"][r, 8] = 0, 0
+    inp["ar"][2, 16] = _bf16_of(70.0)
+    inp["res"][2, 16] = 0
+    ref = oracle.decode(inp)
+    p = Problem(inp)
+    assert B.pa_decode_structure(p.dims) & B.PA_DECODE_NORM_FUSED
+    p.run()
+    got = p.outputs()
+    parity.compare(inp, ref, got)
+    parity.check_written_sets(inp, got)
+    ws = p.workspace.cpu().numpy()
+    sx_base = parity.SYNC_BYTES  # the fused launch keeps no activation codes in the workspace
+    for x in range(8):
+        sx = ws[sx_base + 4 * 64 * x: sx_base + 4 * (64 * x + 4)].view(np.float32)
+        assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (x, sx, ref["s_x"])
