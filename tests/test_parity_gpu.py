@@ -296,18 +296,21 @@ def _bf16_of(x):
     return struct.unpack("<I", struct.pack("<f", float(x)))[0] >> 16  # exact for the values used
 
 
-@pytest.mark.parametrize("K", [1024, 6144])
-def test_fused_norm_scale_with_exact_ties(K):
-    # The one-launch decode norm takes the row's FP8 scale from the thread that
-    # holds the largest |acc| (1 + g) when it is unique, and from a second block
-    # reduction on an exact tie (distinct products are never within 2^-50 of
-    # each other). Rows 0 and 1 tie across threads 0 and 1 (elements 0 and 8),
-    # with the same and with different factors; rows 2 and 3 have a unique
-    # maximum. Every XCD's copy of the per-token scale must equal the oracle's.
+@pytest.mark.parametrize("S,K", [(4, 1024), (4, 6144), (20, 1024), (20, 6144)])
+def test_norm_scale_with_exact_ties(S, K):
+    # The decode norm takes the row's FP8 scale from the thread that holds the
+    # largest |acc| (1 + g) when it is unique, and from a second block reduction
+    # on an exact tie (distinct products are never within 2^-50 of each other).
+    # Rows 0 and 1 tie across threads 0 and 1 (elements 0 and 8), with the same
+    # and with different factors; the other rows have a unique maximum. With 4
+    # tokens the norm shares the projection's launch and every XCD keeps a copy
+    # of the per-token scales; with 20 it is a launch of its own that leaves the
+    # scales and the activation codes in the workspace. All must equal the
+    # oracle's bit for bit.
     from kv_residual_add_amd import _binding as B
     from kv_residual_add_amd.runner import Problem
 
-    wl = _wl("decode", 4, K, 1, max_pos=64)
+    wl = _wl("decode", S, K, 1, max_pos=64)
     inp = synth.make_workload(wl, seed=9)
     g = inp["g_in"].copy()
     g[0], g[8] = _bf16_of(0.25), 0
@@ -319,13 +322,20 @@ def test_fused_norm_scale_with_exact_ties(K):
     inp["res"][2, 16] = 0
     ref = oracle.decode(inp)
     p = Problem(inp)
-    assert B.pa_decode_structure(p.dims) & B.PA_DECODE_NORM_FUSED
+    fused = bool(B.pa_decode_structure(p.dims) & B.PA_DECODE_NORM_FUSED)
+    assert fused == (S <= 16)
     p.run()
     got = p.outputs()
     parity.compare(inp, ref, got)
     parity.check_written_sets(inp, got)
     ws = p.workspace.cpu().numpy()
-    sx_base = parity.SYNC_BYTES  # the fused launch keeps no activation codes in the workspace
-    for x in range(8):
-        sx = ws[sx_base + 4 * 64 * x: sx_base + 4 * (64 * x + 4)].view(np.float32)
-        assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (x, sx, ref["s_x"])
+    base = parity.SYNC_BYTES
+    if fused:  # no activation codes in the workspace; 8 copies of the scales, 64 apart
+        for x in range(8):
+            sx = ws[base + 4 * 64 * x: base + 4 * (64 * x + S)].view(np.float32)
+            assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (x, sx, ref["s_x"])
+    else:  # codes [S][K], then the scales from the next 256-byte boundary
+        assert np.array_equal(ws[base: base + S * K].reshape(S, K), ref["x8"])
+        off = base + -(-(S * K) // 256) * 256
+        sx = ws[off: off + 4 * S].view(np.float32)
+        assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (sx, ref["s_x"])
