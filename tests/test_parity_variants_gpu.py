@@ -66,6 +66,7 @@ DECODE_CASES = [
     (8, 6144, 1, {}),                     # norm + GEMV, then the epilogue
     (40, 2048, 2, {"outlier_frac": 0.01}),  # norm, then GEMV + epilogue
     (20, 4736, 1, {"skip_frac": 0.1}),    # 37 k slices: three launches
+    (16, 1024, 4, {"skip_frac": 0.25}),   # nkv = 4: 77 heads, 8 K/V slots a page
 ]
 
 
@@ -85,6 +86,7 @@ PREFILL_CASES = [
     (5, 256, 2, {"skip_frac": 0.4}),
     (300, 1024, 4, {"skip_frac": 0.1}),   # 128-token CTAs, ragged tail
     (2560, 256, 4, {}),                   # 256-token CTAs
+    (130, 512, 1, {"outlier_frac": 0.01}),  # nkv = 1, a ragged 128-token tile
 ]
 
 
