@@ -100,7 +100,7 @@ __device__ __forceinline__ double block_max_f64(double v, double* red) {
 // waves: the sum in the same fixed order as block_sum_f64; m1 the largest
 // contribution and m2 the second largest, counting each thread once (the DPP
 // steps and the LDS tree combine disjoint sets of threads, as for the sum).
-// Values are >= 0. red holds 48 doubles.
+// Values are >= 0. red holds 48 doubles; the reduction leaves them in use.
 __device__ __forceinline__ void top2_merge(double& m1, double& m2, double b1, double b2) {
   const double lo = __builtin_fmin(m1, b1);
   m1 = __builtin_fmax(m1, b1);
@@ -141,7 +141,8 @@ __device__ __forceinline__ void block_sum_top2_f64(double& v, double& m1, double
   for (int w = 1; w < 16; ++w) top2_merge(a1, a2, red[16 + w], red[32 + w]);
   m1 = a1;
   m2 = a2;
-  __syncthreads();
+  // no trailing barrier: its one caller runs it once per CTA and gives the
+  // fallback reduction a region of its own (red + 48)
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +244,7 @@ __device__ __forceinline__ void norm_token(const KArgs& a, int row, uint8_t* __r
   if (clear)
     owner = ymine == y1;
   else
-    amax = block_max_f64(amax, red);
+    amax = block_max_f64(amax, !CODES ? red + 48 : red);
   stamp(a.timeline, a.timeline_slots, tl, 4);
   const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
   const double sd = static_cast<double>(s);
@@ -694,7 +695,7 @@ __device__ __forceinline__ void xcd_done(const KArgs& a, const DecodePlan& p, in
 // next call.
 template <int CPC, int NV, bool EPI, bool OPT>
 __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
-  __shared__ double red[48];
+  __shared__ double red[64];
   const int b = blockIdx.x, x = b & 7, S = a.S, H = a.heads(), ksplit = p.ksplit;
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
   uint64_t* pub_r = reinterpret_cast<uint64_t*>(a.ws + p.off_rstd) + x * 2 * kSxStride;
