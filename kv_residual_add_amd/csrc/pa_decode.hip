@@ -408,6 +408,18 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
+  // with a publisher, the weights are widened while the norm statistics are
+  // still on their way (off the critical path)
+  bf16x8 aw[FUSED ? CPC : 1][FUSED ? 8 : 1];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int c = 0; c < CPC; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const i32x4& w = wv[c][j >> 1];
+        aw[c][j] = fp8x8_to_bf16(w[2 * (j & 1)], w[2 * (j & 1) + 1], 1.0f);
+      }
+  }
   if constexpr (FUSED) {
     double rstd_l;
     float sc_l;
@@ -447,8 +459,13 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
   for (int c = 0; c < CPC; ++c) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const i32x4& w = wv[c][j >> 1];
-      const bf16x8 A = fp8x8_to_bf16(w[2 * (j & 1)], w[2 * (j & 1) + 1], 1.0f);
+      bf16x8 A;
+      if constexpr (FUSED) {
+        A = aw[c][j];
+      } else {
+        const i32x4& w = wv[c][j >> 1];
+        A = fp8x8_to_bf16(w[2 * (j & 1)], w[2 * (j & 1) + 1], 1.0f);
+      }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         const uint2 bv = *reinterpret_cast<const uint2*>(brow[tt] + c * 128 + 16 * j);
