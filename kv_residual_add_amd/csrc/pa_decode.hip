@@ -381,9 +381,23 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
       xv[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
     }
   };
-  // without a publisher the activation slice goes first (small, L2): the LDS
-  // stores below then wait only for it
-  if constexpr (!FUSED) load_rows();
+  // without a publisher the activation slice goes to LDS before any weight
+  // load is issued: behind the grid's weight requests it would arrive only once
+  // they all had, and the MFMAs below could not start on the first chunks
+  // while the later ones stream
+  if constexpr (!FUSED) {
+    load_rows();
+#pragma unroll
+    for (int r = 0; r < kMaxPieces; ++r) {
+      const int i = tid + r * 256;
+      if (i < S * per_row) {
+        const int s = i / per_row, j = i - s * per_row;
+        *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = xv[r];
+      }
+    }
+    __syncthreads();
+    stamp(a.timeline, a.timeline_slots, tlb, 2);
+  }
   // with one, the raw slice: 8-element groups i = tid + 256 r, token i / (16 CPC)
   constexpr int kGroups = CPC;  // per thread: at most 16 tokens x 16 CPC groups over 256 threads
   u32x4 ga[FUSED ? kGroups : 1], gb[FUSED ? kGroups : 1], gg[FUSED ? kGroups : 1];
@@ -434,17 +448,8 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
       if (i < S * 16 * CPC)
         *reinterpret_cast<uint2*>(lds + s * ldw + j * 8) = codes8(ga[r], gb[r], gg[r], rstd, sd, 1.0 / sd);
     }
-  } else {
-#pragma unroll
-    for (int r = 0; r < kMaxPieces; ++r) {
-      const int i = tid + r * 256;
-      if (i < S * per_row) {
-        const int s = i / per_row, j = i - s * per_row;
-        *reinterpret_cast<i32x4*>(lds + s * ldw + j * 16) = xv[r];
-      }
-    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const int hh = lane >> 5;
   const uint8_t* brow[NT];
@@ -790,6 +795,7 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   if (threadIdx.x == 0) hflags[ks] = 1u;
   if (threadIdx.x < 64) wait_flags(hflags, ksplit, err);
   __syncthreads();
+  stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 4);
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit - 1)) {
     for (int f = 0; f < ksplit; ++f) hflags[f] = 0u;  // every slice is past its wait
@@ -798,6 +804,7 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   const int wave = threadIdx.x >> 6;
   for (int tok = ks + ksplit * wave; tok < a.S; tok += 4 * ksplit)
     head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+  stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 5);
 }
 
 // ---------------------------------------------------------------------------
