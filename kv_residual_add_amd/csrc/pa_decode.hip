@@ -304,6 +304,7 @@ struct Publish {
   const uint64_t* rstd;  // this XCD's per-token rstd bits (0: not yet; a real rstd is > 0)
   const uint64_t* srec;  // this XCD's per-token scale bits, tagged 1 in the upper half (0: not yet)
   uint32_t* err;         // set if a wait gave up
+  uint32_t* done;        // this XCD's count of GEMV CTAs done with the values
 };
 
 // Waits until the XCD's S tokens are published and returns this lane's token's
@@ -358,8 +359,9 @@ __device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_
 // once the XCD's norm CTAs have published each token's rstd and scale, the CTA
 // forms its slice's FP8 codes itself (codes8) straight into LDS.
 template <int CPC, int NT, bool FUSED>
-__device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
-                                          const Publish& pub) {
+__device__ __forceinline__ uint32_t gemv_tile(const KArgs& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
+                                              const Publish& pub) {
+  uint32_t done_before = 0;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, K = a.K, N = a.N();
@@ -449,6 +451,10 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
         *reinterpret_cast<uint2*>(lds + s * ldw + j * 8) = codes8(ga[r], gb[r], gg[r], rstd, sd, 1.0 / sd);
     }
     __syncthreads();
+    // the CTA is done with the published values: counted now, so that the
+    // counter's round trip overlaps the MFMAs (its value is looked at last)
+    if (threadIdx.x == 0)
+      done_before = __hip_atomic_fetch_add(pub.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   const int hh = lane >> 5;
@@ -494,13 +500,14 @@ __device__ __forceinline__ void gemv_tile(const KArgs& a, int h, int ks, const u
     }
   }
   stamp(a.timeline, a.timeline_slots, tlb, 1);
+  return done_before;
 }
 
 template <int CPC, int NT>
 __global__ __launch_bounds__(256) void decode_gemv(KArgs a, size_t off_x8, size_t off_part) {
   const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
-                     Publish{nullptr, nullptr, nullptr});
+                     Publish{nullptr, nullptr, nullptr, nullptr});
 }
 
 // ---------------------------------------------------------------------------
@@ -684,12 +691,12 @@ __global__ __launch_bounds__(64) void decode_epilogue(KArgs a, size_t off_part, 
                        reinterpret_cast<const float*>(a.ws + off_sx), ksplit, a.S + H * ksplit + blockIdx.x);
 }
 
-// A GEMV CTA of XCD x is done with the XCD's published values: the last of the
-// XCD's gx GEMV CTAs (counted with a device-scope atomic) clears them.
-__device__ __forceinline__ void xcd_done(const KArgs& a, const DecodePlan& p, int x, int gx, uint64_t* pub_r,
-                                         uint64_t* pub_s) {
-  uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
-  if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(gx - 1)) {
+// The GEMV CTAs of XCD x count themselves once done with the XCD's published
+// values (gemv_tile); the one that counted last of the XCD's gx clears them
+// and the counter for the next call.
+__device__ __forceinline__ void xcd_clear(const KArgs& a, uint32_t done_before, int gx, uint32_t* done,
+                                          uint64_t* pub_r, uint64_t* pub_s) {
+  if (done_before == static_cast<uint32_t>(gx - 1)) {
     for (int t = 0; t < a.S; ++t) pub_r[t] = 0u, pub_s[t] = 0u;
     __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -712,9 +719,9 @@ __device__ __forceinline__ void xcd_done(const KArgs& a, const DecodePlan& p, in
 //    the next launch.
 // No cache write-back or invalidate is needed and nothing crosses XCDs. The
 // norm CTAs come first in block order, so they are placed before any CTA that
-// waits for them, and the only wait is bounded. The last GEMV CTA of an XCD
-// clears the XCD's published values, a head's epilogue CTA the slice flags, for the
-// next call.
+// waits for them, and the only wait is bounded. The GEMV CTA of an XCD that is
+// the last to be done with the XCD's published values clears them, a head's
+// epilogue CTA the slice flags, for the next call.
 template <int CPC, int NV, bool EPI, bool OPT>
 __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
   __shared__ double red[64];
@@ -747,10 +754,12 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
     ks = g / H;
   }
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
-  gemv_tile<CPC, 1, true>(a, h, ks, nullptr, part, S + ks * H + h,
-                          Publish{pub_r, pub_s, reinterpret_cast<uint32_t*>(a.ws + p.off_err)});
+  uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
+  const uint32_t done_before =
+      gemv_tile<CPC, 1, true>(a, h, ks, nullptr, part, S + ks * H + h,
+                              Publish{pub_r, pub_s, reinterpret_cast<uint32_t*>(a.ws + p.off_err), done});
   if constexpr (!EPI) {
-    if (threadIdx.x == 0) xcd_done(a, p, x, (H * ksplit - x + 7) / 8, pub_r, pub_s);
+    if (threadIdx.x == 0) xcd_clear(a, done_before, (H * ksplit - x + 7) / 8, done, pub_r, pub_s);
     return;
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
@@ -767,7 +776,7 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
       head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
     if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
   }
-  if (threadIdx.x == 0) xcd_done(a, p, x, (H - x + 7) / 8 * ksplit, pub_r, pub_s);
+  if (threadIdx.x == 0) xcd_clear(a, done_before, (H - x + 7) / 8 * ksplit, done, pub_r, pub_s);
 }
 
 // The GEMV with the head epilogue in the same launch, after a norm launch (more
@@ -787,7 +796,7 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   const float* sx = reinterpret_cast<const float*>(a.ws + p.off_sx);
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + p.off_err);
-  gemv_tile<CPC, NT, false>(a, h, ks, a.ws + p.off_x8, part, a.S + ks * H + h, Publish{nullptr, nullptr, nullptr});
+  gemv_tile<CPC, NT, false>(a, h, ks, a.ws + p.off_x8, part, a.S + ks * H + h, Publish{nullptr, nullptr, nullptr, nullptr});
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
   __syncthreads();
   uint32_t* hflags = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;
@@ -796,7 +805,9 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   if (threadIdx.x < 64) wait_flags(hflags, ksplit, err);
   __syncthreads();
   stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 4);
-  if (threadIdx.x == 0 &&
+  // the counter's round trip is made by the last wave, which holds the fewest
+  // epilogue tokens (wave 0 holds the most)
+  if (threadIdx.x == 192 &&
       __hip_atomic_fetch_add(hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit - 1)) {
     for (int f = 0; f < ksplit; ++f) hflags[f] = 0u;  // every slice is past its wait
     __hip_atomic_store(hcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
