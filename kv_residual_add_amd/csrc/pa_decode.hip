@@ -549,8 +549,9 @@ __device__ __forceinline__ void nvfp4_row_wave(float x0, float x1, float gs, boo
 // from the arguments; without it the plain path is compiled alone, since these
 // short kernels fetch their code cold and every extra instruction costs.
 template <bool COHERENT, bool OPT>
-__device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, const float* __restrict__ part,
-                                              const float* __restrict__ sx, int ksplit, int tlb) {
+__device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, int64_t pos,
+                                              const float* __restrict__ part, const float* __restrict__ sx,
+                                              int ksplit, int tlb) {
 #pragma clang fp contract(off)
   const int N = a.N();
   const int lane = threadIdx.x & 63;
@@ -561,10 +562,9 @@ __device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, co
   stamp(a.timeline, a.timeline_slots, tlb, 0);
 
   // Everything the epilogue reads goes out before anything waits: the token's
-  // position first (cos / sin depend on it), then the slice partials (sixteen
-  // slices in flight at a time, summed in slice order), the scales, the slot
-  // and the gamma pair.
-  int64_t pos = a.positions[tok];
+  // position (pos, a load the caller issues first, since cos / sin depend on
+  // it), the slice partials (sixteen slices in flight at a time, summed in
+  // slice order), the scales, the slot and the gamma pair.
   double y0 = 0.0, y1 = 0.0;
   const size_t stride = static_cast<size_t>(S) * N;
   const float* p = part + static_cast<size_t>(tok) * N;
@@ -687,7 +687,8 @@ __device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, co
 template <bool OPT>
 __global__ __launch_bounds__(64) void decode_epilogue(KArgs a, size_t off_part, size_t off_sx, int ksplit) {
   const int H = a.heads();
-  head_epilogue<false, OPT>(a, blockIdx.x % H, blockIdx.x / H, reinterpret_cast<const float*>(a.ws + off_part),
+  head_epilogue<false, OPT>(a, blockIdx.x % H, blockIdx.x / H, a.positions[blockIdx.x / H],
+                            reinterpret_cast<const float*>(a.ws + off_part),
                        reinterpret_cast<const float*>(a.ws + off_sx), ksplit, a.S + H * ksplit + blockIdx.x);
 }
 
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
     __syncthreads();
     const int wave = threadIdx.x >> 6;
     for (int tok = wave; tok < S; tok += 4)
-      head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, S + H * ksplit + tok * H + h);
+      head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, S + H * ksplit + tok * H + h);
     if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
   }
   if (threadIdx.x == 0) xcd_clear(a, done_before, (H - x + 7) / 8 * ksplit, done, pub_r, pub_s);
@@ -814,7 +815,7 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   }
   const int wave = threadIdx.x >> 6;
   for (int tok = ks + ksplit * wave; tok < a.S; tok += 4 * ksplit)
-    head_epilogue<true, OPT>(a, h, tok, part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+    head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, a.S + H * ksplit + tok * H + h);
   stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 5);
 }
 
