@@ -269,10 +269,17 @@ int pre_attn_prefill_ex(const pa_dims* dims, const pa_head_options* opts, const 
 int pa_set_kernel_events(void* start, void* stop);
 
 /* Instrumentation: from now on, calls on this host thread have thread 0 of
- * every CTA of the dominant kernel store the 100 MHz s_memrealtime counter at
- * its phase boundaries into `buffer` (device memory, 8 uint64 slots per CTA,
- * CTA-major; slot 0 = start, 1 = end for the decode GEMV; the prefill GEMM adds
- * its own phases). Stamps beyond `bytes` are dropped. NULL turns it off. */
+ * each CTA store the 100 MHz s_memrealtime counter at its phase boundaries
+ * into `buffer` (device memory, a record of 8 uint64 slots each). Decode records: token t's input norm at record t (slots 0 = loads
+ * issued ... 5 = done; in the one-launch structure, one XCD's copy); the
+ * GEMV CTA of head h and k slice ks at S + ks * heads + h (0 = start,
+ * 1 = partial sums stored; without the norm in its launch 2 = activation
+ * slice in LDS; in the GEMV + epilogue launch 4 = the head's slices all
+ * stored, 5 = its epilogue tokens done); the epilogue of token t and head h
+ * at S + heads * ksplit + t * heads + h (0 = start, 1 = inputs loaded; only
+ * the tokens a CTA's first wave runs).
+ * Prefill: the GEMM CTAs' own phases. Stamps beyond `bytes` are dropped and
+ * the outputs do not depend on the stamps. NULL turns it off. */
 int pa_set_timeline(void* buffer, size_t bytes);
 
 /* Static text for a pa_status value. */

@@ -339,3 +339,72 @@ def test_norm_scale_with_exact_ties(S, K):
         off = base + -(-(S * K) // 256) * 256
         sx = ws[off: off + 4 * S].view(np.float32)
         assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (sx, ref["s_x"])
+
+
+@pytest.mark.parametrize("S, K, nkv", [(4, 1024, 1), (33, 1536, 2), (20, 4736, 1)])
+def test_decode_timeline_stamps(S, K, nkv):
+    """Phase stamps (pa_set_timeline) leave every output bit unchanged, are in
+    program order within each CTA, cover every GEMV CTA, and stay inside the
+    buffer they are given."""
+    from kv_residual_add_amd import _binding as B
+    from kv_residual_add_amd.runner import Problem
+
+    _say(f"timeline decode S={S} K={K} nkv={nkv}")
+    wl = _wl("decode", S, K, nkv)
+    ref = _gpu(synth.make_workload(wl, seed=11))[1]
+    p = Problem(synth.make_workload(wl, seed=11))
+    H = 19 * nkv + 1
+    records = S + H * (K // 128) + S * H  # an upper bound for every structure
+    sentinel = -7
+    buf = torch.full((records * 8 + 64,), sentinel, dtype=torch.int64, device="cuda:0")
+    buf[: records * 8].zero_()
+    B.pa_set_timeline(buf[: records * 8])
+    try:
+        p.run()
+        out = p.outputs()
+    finally:
+        B.pa_set_timeline(None)
+    for k, v in ref.items():
+        assert np.array_equal(v.view(np.uint8), out[k].view(np.uint8)), f"{k} changed with the timeline on"
+    t = buf.cpu().numpy()
+    assert (t[records * 8:] == sentinel).all(), "a stamp landed past the buffer"
+    t = t[: records * 8].reshape(records, 8)
+    flags = B.pa_decode_structure(p.dims)
+    assert (t[:S, 0] > 0).all() and (t[:S, 5] >= t[:S, 0]).all()  # the norm of each token
+    # then head h, k slice ks at S + ks H + h (the first H records at least:
+    # k slice 0), and the epilogues after those; every stamped record is in
+    # program order
+    rest = t[S:]
+    assert (rest[:H, 0] > 0).all()
+    on = rest[:, 0] > 0
+    assert (rest[on, 1] >= rest[on, 0]).all()
+    if flags & B.PA_DECODE_NORM_FUSED:
+        assert not rest[:, 2].any()
+    else:
+        # the GEMV records carry the activation-in-LDS stamp, between start and
+        # end: a contiguous block of H ksplit records
+        g2 = np.flatnonzero(rest[:, 2])
+        ksplit = len(g2) // H
+        assert len(g2) == H * ksplit and ksplit >= 1 and (K // 128) % ksplit == 0
+        assert np.array_equal(g2, np.arange(H * ksplit))
+        g = rest[: H * ksplit]
+        assert ((g[:, 2] >= g[:, 0]) & (g[:, 2] <= g[:, 1])).all()
+        if flags == B.PA_DECODE_EPILOGUE_FUSED:
+            # GEMV + epilogue launch: the head's slices all stored, then the
+            # slice's epilogue tokens
+            assert ((g[:, 4] >= g[:, 1]) & (g[:, 5] >= g[:, 4])).all()
+    # a buffer too small for the call: the stamps past it are dropped
+    small = S + 3
+    buf.fill_(sentinel)
+    buf[: small * 8].zero_()
+    B.pa_set_timeline(buf[: small * 8])
+    try:
+        p.run()
+        out = p.outputs()
+    finally:
+        B.pa_set_timeline(None)
+    for k, v in ref.items():
+        assert np.array_equal(v.view(np.uint8), out[k].view(np.uint8)), f"{k} changed with a short timeline"
+    t = buf.cpu().numpy()
+    assert (t[small * 8:] == sentinel).all(), "a stamp landed past a short buffer"
+    assert (t[: S * 8].reshape(S, 8)[:, 0] > 0).all()
