@@ -926,9 +926,12 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   const int heads = N / kHeadDim;
   // The largest chunk count that still gives every CU a CTA, among those whose
   // whole grid is resident at once (a grid in two rounds streams its second
-  // half only after the first has finished). CTAs per CU allowed by the
-  // kernel's register allocation at 256 threads, for 1..4 chunks (the compiler
-  // reports 70, 94, 114 and 150 registers a lane with two token tiles).
+  // half only after the first has finished). CTAs per CU for 1..4 chunks,
+  // from register counts the compiler once reported for the GEMV with two
+  // token tiles (70, 94, 114, 150). The kernels have changed since (now 68-84
+  // for the GEMV alone, 124 with the epilogue in its launch), and only the
+  // choice of split depends on the table: a head's slices in the GEMV +
+  // epilogue launch need one CTA a CU, whatever the table says.
   // When no grid is resident at once (many heads and a long k), the largest
   // chunk count, i.e. the fewest CTAs, is taken.
   // In the one-launch structure the 8 S norm CTAs also occupy CUs: counted
