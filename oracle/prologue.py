@@ -32,7 +32,9 @@ Per token (decode):
   a9  index_k: E4M3 with unit scale into the index cache row of the slot.
   a10 slot -> (page = slot // 16, row = slot % 16); slot < 0 writes nothing
       (``page16_of`` at its default stride; slot -1 = skip in the epilogue page's
-      argument list).
+      argument list). A slot at or past the cache's end (num_pages * 16) is
+      outside the caller's precondition; it is read like slot -1 and writes
+      nothing, so no byte outside the caches is ever addressed.
 
 Prefill replaces a3/a4 by MXFP8: per (row, 32-wide k block) an E8M0 scale
 2^(floor(log2 amax) - 8) and E4M3 elements, and the block-scaled dot product.
@@ -318,9 +320,10 @@ def _epilogue(y, inp):
     d = np.arange(HEAD_DIM)
     k_off = (d // 16) * (PAGE * 16) + d % 16  # + row * 16
     v_off = d * PAGE  # + row
+    P = k_cache.shape[0]
     for s in range(S):
         slot = int(slots[s])
-        if slot < 0:
+        if slot < 0 or slot >= P * PAGE:  # a slot outside the cache writes nothing, as slot -1
             continue
         page, row = slot // PAGE, slot % PAGE
         for j in range(nkv):

@@ -61,6 +61,9 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_mult: float = 50.0
     skip_frac: float = 0.0  # fraction of tokens whose slot is -1
+    # fraction of tokens whose slot lies at or past the cache's end (outside the
+    # caller's precondition; such a token writes no cache byte)
+    oob_frac: float = 0.0
     eps: float = 1e-6
 
     @property
@@ -206,6 +209,13 @@ def make_workload(wl: Workload, seed: int = 0, weights: bool = True) -> dict:
     if wl.skip_frac > 0:
         n_skip = int(round(wl.skip_frac * S))
         slots[rng.choice(S, size=n_skip, replace=False)] = -1
+    if wl.oob_frac > 0:
+        n_slots = wl.num_pages * PAGE
+        live = np.flatnonzero(slots >= 0)
+        n_oob = max(1, int(round(wl.oob_frac * S)))
+        pick = rng.choice(live, size=min(n_oob, len(live)), replace=False)
+        past = np.array([n_slots, n_slots + PAGE - 1, n_slots + 16 * PAGE + 3, 1 << 40], np.int64)
+        slots[pick] = past[np.arange(len(pick)) % len(past)]
     out["positions"] = pos
     out["slot_mapping"] = slots
     out["cos_sin"] = _rope_table(wl.max_pos)

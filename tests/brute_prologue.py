@@ -263,7 +263,8 @@ def run(inp, mode: str):
         iq_out.append([[bf16_round_bits(f32(v)) for v in head(18 * nkv + j, "g_iq")]
                        for j in range(nkv)])
         slot = int(inp["slot_mapping"][s])
-        if slot < 0:
+        pages = (inp["kv_cache"] if nvfp4 else inp["k_cache"]).shape[0]
+        if slot < 0 or slot >= 16 * pages:  # outside the cache: no write, like -1
             continue
         page, t = slot // 16, slot % 16
         if nvfp4:

@@ -48,6 +48,17 @@ def subset(inp: dict, rows) -> dict:
     return out
 
 
+def cache_pages(inp: dict) -> int:
+    """Pages of the call's cache (FP8 or NVFP4 layout)."""
+    return int((inp["kv_cache"] if inp.get("kv_format", "fp8") == "nvfp4" else inp["k_cache"]).shape[0])
+
+
+def writes_cache(slot, pages: int) -> bool:
+    """Whether a token with this slot writes the cache: 0 <= slot < pages * 16
+    (a negative slot, or one at or past the cache's end, writes nothing)."""
+    return 0 <= int(slot) < 16 * pages
+
+
 def code_ord(c):
     c = np.asarray(c, np.int64)
     return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
@@ -100,6 +111,8 @@ def compare(inp: dict, ref: dict, got: dict, rows=None, strict: bool = True) -> 
                 fails.append(f"q_fp8: {(d > 0).mean():.2e} of codes differ (> {Q_FP8_FRAC})")
 
     slots = np.asarray(inp["slot_mapping"])[rows]
+    pages = cache_pages(inp)
+    slots = np.where((slots >= 0) & (slots < 16 * pages), slots, -1)  # the ones that write
     nkv = int(inp["nkv"])
     if inp.get("kv_format", "fp8") == "nvfp4":
         _compare_nvfp4(got, ref, slots, nkv, stats, fails)
@@ -212,7 +225,7 @@ def check_written_sets_nvfp4(inp: dict, got: dict) -> None:
     kv = np.zeros(inp["kv_cache"].shape, bool)
     ic = np.zeros(inp["index_cache"].shape, bool)
     for slot in np.asarray(inp["slot_mapping"]):
-        if slot < 0:
+        if not writes_cache(slot, kv.shape[0]):
             continue
         page, t = slot // 16, slot % 16
         for m in (kv[page], ic[page][None, :]):
@@ -241,7 +254,7 @@ def expected_written_masks(inp: dict) -> dict:
     ic = np.zeros(inp["index_cache"].shape, bool)
     d = np.arange(128)
     for slot in np.asarray(inp["slot_mapping"]):
-        if slot < 0:
+        if not writes_cache(slot, P):
             continue
         page, t = slot // 16, slot % 16
         k[page, :, (d // 16) * 256 + t * 16 + d % 16] = True

@@ -239,6 +239,38 @@ def test_all_negative_slots_write_nothing():
         assert np.array_equal(out[k].view(np.uint32), inp[k].view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_slots_past_the_cache_write_nothing(mode, fmt):
+    # Slots at or past num_pages * 16 are outside the caller's precondition and
+    # are read like slot -1: the written bytes are exactly those of the same
+    # call with those slots set to -1, the count per remaining slot is the
+    # layout's, and the separately written scalar statement agrees.
+    wl = _small(mode=mode, tokens=8, hidden=64 if mode == "prefill" else 128, nkv=1, num_pages=2,
+                oob_frac=0.5, skip_frac=0.1)
+    inp = synth.make_workload(wl, seed=31)
+    if fmt == "nvfp4":
+        inp = synth.with_nvfp4_caches(inp, 0.37, 1.9)
+    slots = inp["slot_mapping"]
+    past = slots >= 32
+    assert past.sum() >= 4 and (slots >= 1 << 40).any() and (slots == 32).any()
+    run = oracle.decode if mode == "decode" else oracle.prefill
+    out = run(inp)
+    minus = dict(inp, slot_mapping=np.where(past, -1, slots))
+    ref = run(minus)
+    keys = ("kv_cache", "index_cache") if fmt == "nvfp4" else ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale")
+    for k in keys:
+        assert np.array_equal(out[k].view(np.uint8), ref[k].view(np.uint8)), k
+    live = int(((slots >= 0) & ~past).sum())
+    if fmt == "fp8":
+        changed = sum(int((out[k] != inp[k]).sum()) for k in ("k_cache", "v_cache", "index_cache"))
+        assert changed == live * (wl.nkv * 256 + 128)
+        _check_against_brute(inp, out, mode)
+    else:
+        from tests.test_oracle_nvfp4 import _check_against_brute as check_nv
+        check_nv(inp, out, mode)
+
+
 def test_full_cache_written_exactly_once_by_prefill_layout():
     wl = synth.Workload("fill", "prefill", 64, 64, 1, 64, 4, "prefill", requests=2)
     inp = synth.make_workload(wl)
