@@ -1,19 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the MiniMax-M3 pre-attention prologue on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config all|c1..c5]
 
 A step is one whole prologue call (pre_attn_decode or pre_attn_prefill through
-the C ABI) over one batch of synthetic input. Inputs rotate over a pool of
-distinct weight / activation sets of at least 512 MB (twice the 256 MB
-Infinity Cache), so every step streams its weight from HBM. The K timed steps
-are captured into one HIP graph (as a serving engine replays decode steps) and
+the C ABI) over one batch of synthetic input. The default run measures all five
+workloads and prints one JSON line headlined by the largest one (c5, the
+prefill of 8192 tokens: FP8 TFLOP/s and its fraction of the MFMA peak), with a
+record per workload under "configs" (decode: tokens/s and HBM GB/s; prefill:
+TFLOP/s), each with its roofline and its CPU baseline.
+
+Per workload: inputs rotate over a pool of distinct weight / activation sets of
+at least 512 MB (twice the 256 MB Infinity Cache) and at least one set per timed
+step, and a 512 MB copy runs between the graph's upload replay and the timed
+replay, so every timed step reads its weight from HBM. The K timed steps are
+captured into one HIP graph (as a serving engine replays decode steps) and
 replayed between device synchronizations; a second, eager pass over the same
 pool records HIP events around every launch of the dominant kernel to get its
-average duration for the roofline. Prints one JSON line.
+average duration for the roofline.
 
-Workloads (``--config``): c1 tiny decode, c2 decode batch (default: the
-decode-throughput headline shape), c3 speculative decode, c4 / c5 prefill.
+Workloads: c1 tiny decode, c2 decode batch, c3 speculative decode, c4 / c5
+prefill.
 """
 
 from __future__ import annotations
@@ -29,6 +36,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+KEYS = ["c1", "c2", "c3", "c4", "c5"]
+HEADLINE = "c5"  # the largest configuration
+METRIC = "decode tokens/s + HBM GB/s (% of peak); prefill FP8 TFLOP/s (% MFMA peak)"
 
 
 def parse():
@@ -36,10 +46,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="all", choices=["all"] + KEYS,
+                    help="one workload, or all five (headlined by c5)")
     ap.add_argument("--pool-mb", type=int, default=512)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="approximate CPU time of each oracle baseline measurement (0 = skip)")
     ap.add_argument("--head-options", default="none", choices=["none", "static", "fp8q", "nvfp4"],
                     help="time the pre_attn_*_ex head-step options: unit K/V scales, the FP8 q "
                          "output (scale 0.008) besides bf16 q, or NVFP4 caches (global scales "
@@ -107,45 +118,53 @@ def source_sha(mode: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(key: str, mode: str):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter runs, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(fname: str, key: str, mode: str):
+    """A committed rocprofv3 figure for workload `key`, if it was taken on the
+    current kernel source."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", fname)) as f:
             rec = json.load(f).get(key)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_sha") != source_sha(mode):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
-def cpu_baseline(wl, inp, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(wl, inp, budget_s: float, one_core: bool = False):
+    """The oracle, as it stands, on a bounded sample of the same workload: every
+    token for decode, 64 tokens for prefill. With one_core, BLAS runs on one
+    thread; otherwise on all of them."""
+    import contextlib
+
     import numpy as np
 
     import oracle
     from tests import parity
 
     try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = max((i["num_threads"] for i in blas), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = 1
+        threadpool_info, threadpool_limits = None, None
+    ctx = threadpool_limits(limits=1, user_api="blas") if (one_core and threadpool_limits) \
+        else contextlib.nullcontext()
     S = wl.tokens
     rows = np.arange(S) if wl.mode == "decode" else np.arange(min(S, 64))
     sub = inp if len(rows) == S else parity.subset(inp, rows)
     fn = oracle.decode if wl.mode == "decode" else oracle.prefill
     times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        fn(sub)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 1000:
-            break
+    with ctx:
+        cores = 1
+        if threadpool_info is not None:
+            blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+            cores = max((i["num_threads"] for i in blas), default=1)
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            fn(sub)
+            times.append(time.perf_counter() - t0)
+            if (time.perf_counter() - t_start > budget_s and len(times) >= 3) or len(times) >= 1000:
+                break
     t = float(np.median(times))
     N = (19 * wl.nkv + 1) * 128
     if wl.mode == "decode":
@@ -157,16 +176,8 @@ def cpu_baseline(wl, inp, budget_s: float):
                       f"({sum(times):.1f} s), float64 NumPy"}
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the prologue shards by heads with no exchange, so per-GPU throughput is the "
-              "figure that matters", file=sys.stderr)
-        sys.exit(2)
+def run_config(key, args):
+    """Measures one workload; returns its record."""
     import numpy as np
     import torch
 
@@ -174,8 +185,7 @@ def main():
     from kv_residual_add_amd import _binding as B
     from kv_residual_add_amd.runner import Problem
 
-    torch.cuda.set_device(0)
-    wl = synth.named_config(args.config)
+    wl = synth.named_config(key)
     inp = synth.make_workload(wl, seed=0)
     if args.head_options == "static":
         inp["static_kv_scale"] = True
@@ -190,10 +200,13 @@ def main():
     structure = B.pa_decode_structure(prob.dims) if prob.mode == B.PA_MODE_DECODE else 0
     call_bytes, kernel_bytes, flops, kernel_name = algorithmic(wl, structure, args.head_options)
 
-    # rotating pool of distinct weight + activation sets
+    # rotating pool of distinct weight + activation sets: >= pool_mb, and one
+    # set per timed step when that is more
     set_bytes = prob.w_packed.numel() + prob.w_scales.numel() * prob.w_scales.element_size() \
         + 4 * S * K
     n_sets = max(2, math.ceil(args.pool_mb * 2**20 / set_bytes))
+    if set_bytes < 256 << 20:  # a set smaller than the Infinity Cache: one per timed step
+        n_sets = max(n_sets, min(args.steps, 64))
     w_dev = torch.from_numpy(inp["w"]).to(dev)
     sets = []
     for i in range(n_sets):
@@ -211,6 +224,8 @@ def main():
         res = torch.roll(prob.t["res"], sh, dims=1).contiguous()
         sets.append((wp, ws, ar, res))
     del w_dev
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
     torch.cuda.synchronize()
 
     def step(i):
@@ -234,6 +249,7 @@ def main():
         torch.cuda.synchronize()
         graph.replay()  # first replay uploads the graph; not timed
         torch.cuda.synchronize()
+    flush_dst.copy_(flush_src)  # the Infinity Cache holds none of the timed steps' sets
     t_ev0 = torch.cuda.Event(enable_timing=True)
     t_ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -249,6 +265,7 @@ def main():
     wall_s = time.perf_counter() - t0
     gpu_s = t_ev0.elapsed_time(t_ev1) / 1e3
     elapsed = max(wall_s, gpu_s)
+    del graph
 
     # eager pass with HIP events around every launch of the dominant kernel
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -258,6 +275,7 @@ def main():
         b.record()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    flush_dst.copy_(flush_src)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
@@ -270,48 +288,94 @@ def main():
     eager_s = e0.elapsed_time(e1) / 1e3
     B.pa_workspace_status(prob.workspace)  # raises if an in-kernel wait gave up
 
-    key = args.config
-    traffic = measured_traffic(key, wl.mode) if args.head_options == "none" else None
+    traffic_rec = _profile_record("traffic.json", key, wl.mode) if args.head_options == "none" else None
+    prof_rec = _profile_record("kernel_times.json", key, wl.mode) if args.head_options == "none" else None
+    prof_ms = prof_rec["avg_ns"] / 1e6 if prof_rec else None
     if wl.mode == "decode":
         metric, unit = "decode tokens/s", "tokens/s"
         value = S * args.steps / elapsed
-        achieved = kernel_bytes / (kern_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kernel_name, "kernel_ms": round(kern_ms, 5),
-                "algorithmic_bytes_per_launch": kernel_bytes}
+        work, peak, bound, runit = kernel_bytes / 1e9, HBM_PEAK_GBS, "hbm", "GB/s"
         extra = {"step_hbm_gbs": round(call_bytes * args.steps / elapsed / 1e9, 1),
                  "step_hbm_frac": round(call_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 4),
                  "algorithmic_bytes_per_step": call_bytes}
+        per_launch = {"algorithmic_bytes_per_launch": kernel_bytes}
     else:
         metric, unit = "prefill FP8 TFLOP/s", "TFLOP/s"
         value = flops * args.steps / elapsed / 1e12
-        achieved = flops / (kern_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": kernel_name, "kernel_ms": round(kern_ms, 5),
-                "algorithmic_flops_per_launch": flops}
+        work, peak, bound, runit = flops / 1e12, FP8_PEAK_TFLOPS, "mfma", "TFLOP/s"
         extra = {"step_tflops_frac": round(value / FP8_PEAK_TFLOPS, 4),
                  "tokens_per_s": round(S * args.steps / elapsed, 1)}
-
-    line = {
-        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
+        per_launch = {"algorithmic_flops_per_launch": flops}
+    achieved = work / (kern_ms / 1e3)
+    roof = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": runit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_rec.get("bytes_per_launch") if traffic_rec else None,
+            "kernel": kernel_name, "kernel_ms": round(kern_ms, 5), "kernel_ms_from": "hip events, eager pass",
+            **per_launch}
+    if prof_ms:
+        roof["kernel_ms_rocprof"] = round(prof_ms, 5)
+        roof["frac_rocprof"] = round(work / (prof_ms / 1e3) / peak, 4)
+    rec = {
+        "workload": wl.name, "metric": metric, "value": round(value, 3), "unit": unit,
         "ms_per_step": round(elapsed / args.steps * 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3" if wl.mode == "decode" else "mxfp8_e4m3",
-        "data": "synthetic",
         "config": {"workload": wl.name, "tokens": S, "hidden": K, "nkv": wl.nkv, "n_rows": N,
-                   "pool_sets": n_sets, "timing": "hip graph replay" if graph else "eager",
+                   "pool_sets": n_sets, "pool_mb": round(n_sets * set_bytes / 2**20),
+                   "distinct_sets_timed": min(args.steps, n_sets), "cache_flush_mb": 512,
+                   "timing": "hip graph replay" if not args.no_graph else "eager",
                    **({} if args.head_options == "none" else {"head_options": args.head_options})},
         "roofline": roof,
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 5),
         **extra,
     }
+    del sets, prob, flush_src, flush_dst
+    torch.cuda.empty_cache()
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        if wl.mode == "decode":
+            rec["cpu_baseline_1core"] = cpu_baseline(wl, inp, args.cpu_seconds, one_core=True)
     else:
-        line["cpu_baseline"] = None
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the prologue shards by heads with no exchange, so per-GPU throughput is the "
+              "figure that matters", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    keys = KEYS if args.config == "all" else [args.config]
+    head = HEADLINE if args.config == "all" else args.config
+    recs = {}
+    for key in keys:
+        print(f"bench: {key} ...", file=sys.stderr, flush=True)
+        recs[key] = run_config(key, args)
+        r = recs[key]
+        print(f"bench: {key} {r['value']:.1f} {r['unit']}, {r['ms_per_step'] * 1e3:.2f} us a step, "
+              f"roofline frac {r['roofline']['frac']}", file=sys.stderr, flush=True)
+    h = recs[head]
+    line = {
+        "metric": METRIC, "value": h["value"], "unit": h["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": h["dtype"], "data": "synthetic",
+        "config": dict(h["config"], headline=f"{head} ({h['metric']})"),
+        "roofline": h["roofline"],
+        "cpu_baseline": h.get("cpu_baseline"),
+    }
+    if len(keys) > 1:
+        line["configs"] = recs
+    else:
+        line.update({k: v for k, v in h.items() if k not in line and k not in ("workload", "metric", "value",
+                                                                                  "unit", "config")})
     print(json.dumps(line), flush=True)
 
 

@@ -91,9 +91,11 @@ typedef enum pa_status {
   PA_ERR_DEVICE = -9,    /* the current device is not a gfx950 GPU */
   PA_ERR_MODE = -10,     /* unknown mode argument */
   PA_ERR_SYNC = -11,     /* a kernel's bounded wait for another CTA gave up */
-  PA_ERR_OPTIONS = -12   /* pa_head_options: a scale not finite and > 0 (or its float32
+  PA_ERR_OPTIONS = -12,  /* pa_head_options: a scale not finite and > 0 (or its float32
                             reciprocal not finite), an unknown kv_cache_format, or
                             static_kv_scale together with NVFP4 */
+  PA_ERR_WEIGHT_RANGE = -13 /* pa_pack_weight_prefill: an E8M0 code of a k, v or index_k
+                               row outside [10, 246] */
 } pa_status;
 
 /* Problem size of one call. */
@@ -158,7 +160,19 @@ int pa_pack_weight_decode(const uint8_t* w, uint8_t* w_packed, int32_t n_rows,
  *   w         E4M3 codes [n_rows][hidden]
  *   w_e8m0    E8M0 codes [n_rows][hidden / 32]
  *   w_packed  output, pa_packed_weight_bytes(PA_MODE_PREFILL, ...) bytes
- *   s_packed  output, pa_packed_scale_bytes(PA_MODE_PREFILL, ...) bytes */
+ *   s_packed  output, pa_packed_scale_bytes(PA_MODE_PREFILL, ...) bytes
+ * The k, v and index_k heads (whose per-token FP8 scales and codes must follow
+ * the exact projection to 1e-6) are computed on bf16 MFMAs from the MXFP8
+ * values widened exactly to bf16, which holds while every weight value
+ * code * 2^(e - 127) is a normal bf16 number: each E8M0 code e of those rows
+ * must lie in [10, 246]. This call checks that and returns PA_ERR_WEIGHT_RANGE
+ * otherwise (the packed buffers are written either way). Unlike the other
+ * packing and prologue calls it synchronizes `stream` (a load-time call).
+ * Precision notes for pre_attn_prefill: the projection accumulates in
+ * float32, so its partial sums must stay below 2^127 in magnitude; an
+ * activation 32-block whose largest normalized magnitude is below 2^-109
+ * (but not zero) widens to bf16 subnormals, where the k, v and index_k
+ * products are no longer exact. */
 int pa_pack_weight_prefill(const uint8_t* w, const uint8_t* w_e8m0, uint8_t* w_packed,
                            uint8_t* s_packed, int32_t n_rows, int32_t hidden,
                            void* stream);

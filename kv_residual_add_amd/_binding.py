@@ -24,8 +24,20 @@ PAGE_BYTES = 2048
 DECODE_MAX_TOKENS = 64
 PA_DECODE_NORM_FUSED = 1
 PA_DECODE_EPILOGUE_FUSED = 2
+PA_OK = 0
+PA_ERR_NULL = -1
+PA_ERR_ALIGN = -2
+PA_ERR_NKV = -3
+PA_ERR_HIDDEN = -4
+PA_ERR_TOKENS = -5
+PA_ERR_WORKSPACE = -6
+PA_ERR_DIMS = -7
+PA_ERR_HIP = -8
+PA_ERR_DEVICE = -9
+PA_ERR_MODE = -10
 PA_ERR_SYNC = -11
 PA_ERR_OPTIONS = -12
+PA_ERR_WEIGHT_RANGE = -13
 PA_KV_FP8 = 0
 PA_KV_NVFP4 = 1
 NV_SLOT_BYTES = 1152
@@ -356,3 +368,4 @@ def pre_attn_prefill_ex(dims, opts, ar, res, h_out, g_in, w_packed, s_packed, g_
     _run("pre_attn_prefill_ex", PA_MODE_PREFILL, dims, ar, res, h_out, g_in, w_packed, s_packed,
          g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
          v_scale, index_cache, q_out, iq_out, workspace, stream, opts)
+

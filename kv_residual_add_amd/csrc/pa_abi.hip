@@ -1,6 +1,7 @@
 // extern "C" entry points of libpre_attn.so: argument validation, workspace
 // carve-up and kernel launches on the caller's stream. Nothing here allocates
-// device memory or synchronizes the host.
+// device memory or synchronizes the host (except the status queries and the
+// prefill weight check, which say so).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -285,9 +286,13 @@ int pa_pack_weight_prefill(const uint8_t* w, const uint8_t* w_e8m0, uint8_t* w_p
   if (st) return st;
   st = check_device();
   if (st) return st;
-  hipError_t e = pa::launch_pack_prefill(w, w_e8m0, w_packed, s_packed, n_rows, hidden,
-                                         static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_pack_weight_prefill");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pa::launch_pack_prefill(w, w_e8m0, w_packed, s_packed, n_rows, hidden, s);
+  if (e != hipSuccess) return hip_fail(e, "pa_pack_weight_prefill");
+  bool ok = false;
+  if ((e = pa::prefill_weight_range_ok(w_e8m0, n_rows, hidden, s, ok)) != hipSuccess)
+    return hip_fail(e, "pa_pack_weight_prefill");
+  return ok ? PA_OK : PA_ERR_WEIGHT_RANGE;
 }
 
 int pre_attn_decode(const pa_dims* dims, const uint16_t* ar, const uint16_t* res, uint16_t* h_out,
@@ -359,6 +364,8 @@ const char* pa_strerror(int status) {
     case PA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case PA_ERR_MODE: return "unknown mode";
     case PA_ERR_SYNC: return "a kernel's bounded wait gave up: that call's outputs are not valid";
+    case PA_ERR_WEIGHT_RANGE:
+      return "an E8M0 code of a k, v or index_k weight row is outside [10, 246]";
     case PA_ERR_OPTIONS:
       return "bad pa_head_options: a scale not finite and > 0 (or with an infinite float32 reciprocal), "
              "an unknown kv_cache_format, or static_kv_scale with NVFP4";

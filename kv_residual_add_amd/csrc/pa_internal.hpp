@@ -86,6 +86,9 @@ PrefillPlan prefill_plan(int M, int K, int nkv);
 hipError_t launch_prefill(const Args& a, const PrefillPlan& p);
 hipError_t launch_pack_prefill(const uint8_t* w, const uint8_t* ws, uint8_t* wp, uint8_t* sp,
                                int N, int K, hipStream_t s);
+// Whether every E8M0 code of the k, v and index_k rows admits the exact bf16
+// widening (synchronizes s).
+hipError_t prefill_weight_range_ok(const uint8_t* we, int N, int K, hipStream_t s, bool& ok);
 size_t prefill_packed_weight_bytes(int N, int K);
 size_t prefill_packed_scale_bytes(int N, int K);
 

@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -625,7 +626,22 @@ __device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, 
     }
     float ssf = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     ssf += __shfl_xor(ssf, 32, 64);
-    const float rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
+    float rf;
+    if (__builtin_expect(!(ssf <= 3.4028234663852886e38f), 0)) {
+      // the float32 sum of squares overflowed (head values past about 2^63):
+      // again in float64, where a float32 square is exact (the pair of lanes
+      // holding the token takes this branch together)
+      double sd = 0.0;
+      for (int i = 0; i < 64; i += 4) {
+        const float4 v = x.chunk(c0 + (i >> 2));
+        sd += static_cast<double>(v.x) * v.x + static_cast<double>(v.y) * v.y + static_cast<double>(v.z) * v.z +
+              static_cast<double>(v.w) * v.w;
+      }
+      sd += __shfl_xor(sd, 32, 64);
+      rf = static_cast<float>(1.0 / __builtin_sqrt(sd / static_cast<double>(kHeadDim) + static_cast<double>(a.eps)));
+    } else {
+      rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
+    }
     u32x4 o1[4], o2[4];  // bf16 dims i .. i + 7 and i + 32 .. i + 39 for i = 0, 8, 16, 24
     uint32_t f8a[8], f8b[8];  // E4M3 q of the lane's dims 0 .. 31 and 32 .. 63 (when requested)
     const bool fp8_row = h < k0 && live && a.q_fp8 != nullptr;
@@ -930,6 +946,39 @@ __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __res
     sp[hk * 256 + l * 4 + m] = we[static_cast<size_t>(row) * (K / 32) + ks * 2 + (l >> 5)];
 }
 
+// The precondition of the exact widening on the k, v and index_k heads: every
+// weight value code * 2^(e - 127) is a normal bf16 number, i.e. the block's
+// E8M0 code e lies in [kPreciseMinE8m0, kPreciseMaxE8m0] (the smallest nonzero
+// code is 2^-9, the largest 448 < 2^9). One word per device records a code
+// outside that range for the check at pack time.
+constexpr int kPreciseMinE8m0 = 10;
+constexpr int kPreciseMaxE8m0 = 246;
+__device__ uint32_t g_precise_range_bad;
+
+__global__ void clear_range_flag() { g_precise_range_bad = 0u; }
+
+// One thread per dword of the precise rows' E8M0 codes (rows of the k and v
+// heads, then the index_k head's).
+__global__ void check_precise_e8m0(const uint8_t* __restrict__ we, int N, int K, int nkv) {
+  const size_t per_row = static_cast<size_t>(K) / 32;  // codes per row, a multiple of 4
+  const size_t kv_rows = static_cast<size_t>(2 * nkv) * kHeadDim;
+  const size_t words = (kv_rows + kHeadDim) * per_row / 4;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= words) return;
+  const size_t r = i * 4 / per_row;  // among the precise rows
+  const size_t row = r < kv_rows ? static_cast<size_t>(16 * nkv) * kHeadDim + r
+                                 : static_cast<size_t>(19 * nkv) * kHeadDim + (r - kv_rows);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(we + row * per_row + (i * 4 - r * per_row));
+  bool bad = false;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int c = static_cast<int>((w >> (8 * b)) & 0xffu);
+    bad |= c < kPreciseMinE8m0 || c > kPreciseMaxE8m0;
+  }
+  if (bad) atomicOr(&g_precise_range_bad, 1u);
+  (void)N;
+}
+
 // Norm pass launch: one CTA per resident slot (the CTAs per CU that the
 // kernel's registers allow, times the CUs), each walking the rows at the grid
 // stride, so the next row's loads overlap the current row's work.
@@ -1046,6 +1095,26 @@ hipError_t launch_pack_prefill(const uint8_t* w, const uint8_t* we, uint8_t* wp,
   const unsigned blocks = static_cast<unsigned>((pieces + 255) / 256);
   hipLaunchKernelGGL(pack_prefill, dim3(blocks), dim3(256), 0, s, w, we, wp, sp, N, K);
   return hipGetLastError();
+}
+
+hipError_t prefill_weight_range_ok(const uint8_t* we, int N, int K, hipStream_t s, bool& ok) {
+  static std::mutex mu;  // one device word per device, shared by the calling threads
+  std::lock_guard<std::mutex> lock(mu);
+  const int nkv = (N / kHeadDim - 1) / 19;
+  const size_t words = static_cast<size_t>(2 * nkv + 1) * kHeadDim * (K / 32) / 4;
+  hipLaunchKernelGGL(clear_range_flag, dim3(1), dim3(1), 0, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(check_precise_e8m0, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s, we, N,
+                     K, nkv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint32_t bad = 0;
+  if ((e = hipMemcpyFromSymbolAsync(&bad, HIP_SYMBOL(g_precise_range_bad), sizeof(bad), 0, hipMemcpyDeviceToHost,
+                                    s)) != hipSuccess)
+    return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  ok = bad == 0u;
+  return hipSuccess;
 }
 
 }  // namespace pa

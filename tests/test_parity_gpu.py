@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the oracle, element by
 element, on seeded synthetic inputs: small shapes that span several tiles and
-ragged tails, degenerate cases, and the five full workloads (the prefill ones
-checked on sampled tokens plus the full written-byte sets)."""
+ragged tails, degenerate cases, slots outside the cache, wide weight block
+exponents, and the five full workloads (every token of each)."""
 
 import sys
 
@@ -48,6 +48,11 @@ DECODE_SMALL = [
     (20, 4736, 1, {}),  # 37 k slices: the epilogue in a launch of its own
     (8, 16384, 1, {}),  # hidden past the fused norm's reach, 32 k slices
     (4, 16384, 2, {}),  # more CTAs than are resident at once
+    # slots at or past the cache's end write nothing, in every launch structure
+    (5, 1024, 1, {"oob_frac": 0.4}),               # one launch
+    (8, 6144, 1, {"oob_frac": 0.25}),              # norm + GEMV, then the epilogue
+    (40, 2048, 2, {"oob_frac": 0.2, "skip_frac": 0.1}),  # norm, then GEMV + epilogue
+    (20, 4736, 1, {"oob_frac": 0.2}),              # three launches
 ]
 
 
@@ -69,6 +74,8 @@ PREFILL_SMALL = [
     (130, 512, 1, {}),
     (300, 1024, 4, {"skip_frac": 0.1}),
     (257, 384, 2, {"outlier_frac": 0.01}),
+    (300, 1024, 2, {"oob_frac": 0.1, "skip_frac": 0.05}),  # slots past the cache's end
+    (2560, 256, 4, {"oob_frac": 0.05}),                   # the same with 256-token CTAs
 ]
 
 
@@ -231,22 +238,69 @@ def test_decode_parity_full_workloads(key):
     _say(f"  {stats}")
 
 
+def prefill_chunks(inp, chunk=2048):
+    """The oracle over every token of a prefill call, in token chunks (host
+    memory): yields (rows, oracle output for those rows)."""
+    S = inp["ar"].shape[0]
+    for r0 in range(0, S, chunk):
+        rows = np.arange(r0, min(S, r0 + chunk))
+        yield rows, oracle.prefill(parity.subset(inp, rows))
+
+
+def merge_stats(acc, stats):
+    """Worst case over chunks of the statistics parity.compare returns."""
+    for k, v in stats.items():
+        if k == "failures":
+            continue
+        acc[k] = v + acc.get(k, 0) if k == "live_slots" else max(v, acc.get(k, v))
+    return acc
+
+
 @pytest.mark.parametrize("key", ["c4", "c5"])
-def test_prefill_parity_full_workloads_sampled(key):
+def test_prefill_parity_full_workloads(key):
+    # every token of the workload against the oracle (in token chunks), the
+    # full written-byte sets and every activation code
     wl = synth.named_config(key)
-    _say(f"prefill full {wl.name} (sampled tokens)")
+    _say(f"prefill full {wl.name} (every token)")
     inp = synth.make_workload(wl, seed=0)
     p, got = _gpu(inp)
-    rng = np.random.default_rng(1)
-    S = wl.tokens
-    rows = np.unique(np.concatenate([[0, S - 1, 127, 128], rng.choice(S, 60, replace=False)]))
-    ref = oracle.prefill(parity.subset(inp, rows))
-    stats = parity.compare(inp, ref, got, rows=rows)
-    parity.check_written_sets(inp, got)
-    parity.check_activation_codes(p.workspace.cpu().numpy(), ref, S, wl.hidden, rows=rows)
-    _say(f"  {stats}")
+    ws = p.workspace.cpu().numpy()
     del p
     torch.cuda.empty_cache()
+    S = wl.tokens
+    stats, xq, xs = {}, [], []
+    for rows, ref in prefill_chunks(inp):
+        merge_stats(stats, parity.compare(inp, ref, got, rows=rows))
+        xq.append(ref["xq"])
+        xs.append(ref["xs"])
+        _say(f"  tokens {rows[0]}..{rows[-1]} ok")
+    assert stats["live_slots"] == S
+    parity.check_written_sets(inp, got)
+    parity.check_activation_codes(ws, {"xq": np.concatenate(xq), "xs": np.concatenate(xs)}, S, wl.hidden)
+    _say(f"  {stats}")
+
+
+def test_prefill_wide_weight_exponents():
+    # Weight block exponents far from the synthetic 113..114, across the range
+    # the header states for exact widening of the k, v and index_k heads
+    # (E8M0 10..246; here up to 200 so the projection stays in float32's range):
+    # half the rows take a band of four exponents around a per-row base in
+    # [10, 196], the other half a uniform exponent per block in [10, 200].
+    wl = _wl("prefill", 300, 1024, 2, skip_frac=0.05)
+    _say(f"prefill wide exponents {wl.name}")
+    inp = synth.make_workload(wl, seed=77)
+    rng = np.random.default_rng(78)
+    N, nb = inp["w_e8m0"].shape
+    base = rng.integers(10, 197, size=(N, 1))
+    band = base + rng.integers(0, 4, size=(N, nb))
+    wide = rng.integers(10, 201, size=(N, nb))
+    inp["w_e8m0"] = np.where((np.arange(N) % 2 == 0)[:, None], band, wide).astype(np.uint8)
+    assert inp["w_e8m0"].min() == 10 and inp["w_e8m0"].max() >= 198
+    ref = oracle.prefill(inp)
+    p, got = _gpu(inp)
+    stats = parity.compare(inp, ref, got)
+    parity.check_written_sets(inp, got)
+    _say(f"  {stats}")
 
 
 # decode shapes for each launch structure: few tokens with a small weight (norm,
@@ -408,3 +462,31 @@ def test_decode_timeline_stamps(S, K, nkv):
     t = buf.cpu().numpy()
     assert (t[small * 8:] == sentinel).all(), "a stamp landed past a short buffer"
     assert (t[: S * 8].reshape(S, 8)[:, 0] > 0).all()
+
+
+def test_prefill_pack_checks_precise_exponents():
+    # pa_pack_weight_prefill returns PA_ERR_WEIGHT_RANGE when an E8M0 code of a
+    # k, v or index_k row lies outside [10, 246] (the exact bf16 widening's
+    # range); codes of q and index_q rows are not restricted
+    from kv_residual_add_amd import _binding as B
+
+    nkv, K = 2, 256
+    N = (19 * nkv + 1) * 128
+    w = torch.zeros((N, K), dtype=torch.uint8, device="cuda:0")
+    wp = torch.empty(B.pa_packed_weight_bytes(B.PA_MODE_PREFILL, N, K), dtype=torch.uint8, device="cuda:0")
+    sp = torch.empty(B.pa_packed_scale_bytes(B.PA_MODE_PREFILL, N, K), dtype=torch.uint8, device="cuda:0")
+    ok = torch.full((N, K // 32), 120, dtype=torch.uint8, device="cuda:0")
+    B.pa_pack_weight_prefill(w, ok, wp, sp)
+    edge = ok.clone()
+    edge[16 * nkv * 128] = 10
+    edge[19 * nkv * 128 + 127] = 246
+    edge[0, 3] = 0  # a q row: any code
+    edge[18 * nkv * 128, 0] = 255  # an index_q row: any code
+    B.pa_pack_weight_prefill(w, edge, wp, sp)
+    for row, code in ((16 * nkv * 128, 9), (17 * nkv * 128 + 5, 247), (19 * nkv * 128 + 127, 0),
+                      (18 * nkv * 128 - 1, 255)):
+        bad = ok.clone()
+        bad[row, K // 32 - 1] = code
+        with pytest.raises(B.PaError) as e:
+            B.pa_pack_weight_prefill(w, bad, wp, sp)
+        assert e.value.status == B.PA_ERR_WEIGHT_RANGE, (row, code)

@@ -12,6 +12,7 @@ import pytest
 import oracle
 import synth
 from tests import parity
+from tests.test_parity_gpu import merge_stats, prefill_chunks
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,7 @@ DECODE_CASES = [
     (40, 2048, 2, {"outlier_frac": 0.01}),  # norm, then GEMV + epilogue
     (20, 4736, 1, {"skip_frac": 0.1}),    # 37 k slices: three launches
     (16, 1024, 4, {"skip_frac": 0.25}),   # nkv = 4: 77 heads, 8 K/V slots a page
+    (24, 1024, 1, {"oob_frac": 0.25}),    # slots past the cache's end write nothing
 ]
 
 
@@ -87,6 +89,7 @@ PREFILL_CASES = [
     (300, 1024, 4, {"skip_frac": 0.1}),   # 128-token CTAs, ragged tail
     (2560, 256, 4, {}),                   # 256-token CTAs
     (130, 512, 1, {"outlier_frac": 0.01}),  # nkv = 1, a ragged 128-token tile
+    (200, 512, 2, {"oob_frac": 0.1}),     # slots past the cache's end write nothing
 ]
 
 
@@ -104,20 +107,19 @@ def test_prefill_variants(S, K, nkv, kw, variant):
 
 @pytest.mark.parametrize("key", ["c3", "c4"])
 def test_variants_full_workload(key):
-    """Both variants at once on a full workload (prefill: sampled tokens)."""
+    """Both variants at once on a full workload, every token."""
     wl = synth.named_config(key)
     _say(f"variants full {wl.name}")
     inp = _with_variant(synth.make_workload(wl, seed=0), True, 0.008, True)
     p, got = _run_gpu(inp)
-    rows = None
-    if wl.mode == "decode":
-        ref = oracle.decode(inp)
-    else:
-        rng = np.random.default_rng(2)
-        rows = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 40, replace=False)]))
-        ref = oracle.prefill(parity.subset(inp, rows))
-    _say(f"  {_check(inp, ref, got, rows=rows)}")
     del p
+    if wl.mode == "decode":
+        _say(f"  {_check(inp, oracle.decode(inp), got)}")
+        return
+    stats = {}
+    for rows, ref in prefill_chunks(inp):  # every token
+        merge_stats(stats, _check(inp, ref, got, rows=rows))
+    _say(f"  {stats}")
 
 
 def test_plain_and_ex_calls_agree():
@@ -175,23 +177,21 @@ def test_prefill_nvfp4(S, K, nkv, kw, scales):
 
 @pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
 def test_nvfp4_full_workload(key):
-    """NVFP4 caches with the FP8 q output on a full workload (prefill: sampled
-    tokens for the values, every slot for the written-byte set)."""
+    """NVFP4 caches with the FP8 q output on a full workload, every token."""
     wl = synth.named_config(key)
     _say(f"nvfp4 full {wl.name}")
     inp = synth.with_nvfp4_caches(synth.make_workload(wl, seed=0), 0.37, 1.9)
     inp["q_fp8_scale"] = 0.008
     inp["q_bf16"] = True
     p, got = _run_gpu(inp)
-    rows = None
-    if wl.mode == "decode":
-        ref = oracle.decode(inp)
-    else:
-        rng = np.random.default_rng(3)
-        rows = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 40, replace=False)]))
-        ref = oracle.prefill(parity.subset(inp, rows))
-    _say(f"  {_nvfp4_check(inp, ref, got, rows=rows)}")
     del p
+    if wl.mode == "decode":
+        _say(f"  {_nvfp4_check(inp, oracle.decode(inp), got)}")
+        return
+    stats = {}
+    for rows, ref in prefill_chunks(inp):  # every token
+        merge_stats(stats, _nvfp4_check(inp, ref, got, rows=rows))
+    _say(f"  {stats}")
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
