@@ -189,6 +189,27 @@ int pre_attn_decode(const pa_dims* dims, const uint16_t* ar, const uint16_t* res
                     uint8_t* index_cache, uint16_t* q_out, uint16_t* iq_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pre_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Its workspace is a library-owned array of
+ * 24 MiB per GPU (PA_NOALLOC_SCRATCH_BYTES), held until the process ends and
+ * cleared by a fill kernel on `stream` at the first call on each GPU; the call
+ * itself allocates nothing. A call whose pa_workspace_bytes(dims,
+ * PA_MODE_DECODE) exceeds that size returns PA_ERR_WORKSPACE (hidden 6144 at
+ * nkv <= 2 fits up to 64 tokens; at nkv = 4 up to 48). Every call on one GPU
+ * shares the array, and each call leaves its synchronization words cleared
+ * for the next: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. Other arguments and
+ * results as pre_attn_decode. */
+#define PA_NOALLOC_SCRATCH_BYTES (24u << 20)
+int pre_attn_decode_noalloc(const pa_dims* dims, const uint16_t* ar, const uint16_t* res,
+                            uint16_t* h_out, const uint16_t* g_in, const uint8_t* w_packed,
+                            const float* w_scale, const uint16_t* g_q, const uint16_t* g_k,
+                            const uint16_t* g_iq, const uint16_t* g_ik, const uint16_t* cos_sin,
+                            const int64_t* positions, const int64_t* slot_mapping,
+                            uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                            uint8_t* index_cache, uint16_t* q_out, uint16_t* iq_out, void* stream);
+
 /* Prefill prologue (MXFP8 activations and weight).
  *   w_packed, s_packed  from pa_pack_weight_prefill. */
 int pre_attn_prefill(const pa_dims* dims, const uint16_t* ar, const uint16_t* res,

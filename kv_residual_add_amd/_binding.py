@@ -55,6 +55,7 @@ EXPORTS = (
     "pre_attn_prefill",
     "pre_attn_decode_ex",
     "pre_attn_prefill_ex",
+    "pre_attn_decode_noalloc",
     "pa_set_kernel_events",
     "pa_set_timeline",
     "pa_strerror",
@@ -152,6 +153,8 @@ def load() -> ctypes.CDLL:
         lib.pre_attn_decode_ex.restype = ctypes.c_int
         lib.pre_attn_prefill_ex.argtypes = [dims_p, opts_p] + [P] * 21 + [sz, P]
         lib.pre_attn_prefill_ex.restype = ctypes.c_int
+        lib.pre_attn_decode_noalloc.argtypes = [dims_p] + [P] * 20 + [P]
+        lib.pre_attn_decode_noalloc.restype = ctypes.c_int
         lib.pa_set_timeline.argtypes = [P, sz]
         lib.pa_set_timeline.restype = ctypes.c_int
         lib.pa_set_kernel_events.argtypes = [P, P]
@@ -369,3 +372,33 @@ def pre_attn_prefill_ex(dims, opts, ar, res, h_out, g_in, w_packed, s_packed, g_
          g_q, g_k, g_iq, g_ik, cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale,
          v_scale, index_cache, q_out, iq_out, workspace, stream, opts)
 
+
+def pre_attn_decode_noalloc(dims, ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik,
+                            cos_sin, positions, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                            index_cache, q_out, iq_out, stream=None) -> None:
+    """pre_attn_decode with the library's per-GPU scratch as its workspace (no
+    allocation; calls on one GPU must not overlap). As in include/pre_attn.h."""
+    S, K, nkv = dims.tokens, dims.hidden, dims.nkv
+    P, L = dims.num_pages, dims.max_pos
+    N = (19 * nkv + 1) * HEAD_DIM
+    dev = ar.device
+    bf, u8, f32, i64 = torch.bfloat16, torch.uint8, torch.float32, torch.int64
+    args = [
+        _ptr(ar, "ar", bf, S * K, dev), _ptr(res, "res", bf, S * K, dev),
+        _ptr(h_out, "h_out", bf, S * K, dev), _ptr(g_in, "g_in", bf, K, dev),
+        _ptr(w_packed, "w_packed", u8, pa_packed_weight_bytes(PA_MODE_DECODE, N, K), dev),
+        _ptr(w_scale, "w_scale", f32, N, dev),
+        _ptr(g_q, "g_q", bf, HEAD_DIM, dev), _ptr(g_k, "g_k", bf, HEAD_DIM, dev),
+        _ptr(g_iq, "g_iq", bf, HEAD_DIM, dev), _ptr(g_ik, "g_ik", bf, HEAD_DIM, dev),
+        _ptr(cos_sin, "cos_sin", bf, L * 64, dev),
+        _ptr(positions, "positions", i64, S, dev), _ptr(slot_mapping, "slot_mapping", i64, S, dev),
+        _ptr(k_cache, "k_cache", u8, P * nkv * PAGE_BYTES, dev),
+        _ptr(v_cache, "v_cache", u8, P * nkv * PAGE_BYTES, dev),
+        _ptr(k_scale, "k_scale", f32, P * nkv * PAGE, dev),
+        _ptr(v_scale, "v_scale", f32, P * nkv * PAGE, dev),
+        _ptr(index_cache, "index_cache", u8, P * PAGE * HEAD_DIM, dev),
+        _ptr(q_out, "q_out", bf, S * 16 * nkv * HEAD_DIM, dev),
+        _ptr(iq_out, "iq_out", bf, S * nkv * HEAD_DIM, dev),
+    ]
+    _check(load().pre_attn_decode_noalloc(ctypes.byref(dims), *args, _stream(stream)),
+           "pre_attn_decode_noalloc")

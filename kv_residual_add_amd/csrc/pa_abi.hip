@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "pa_internal.hpp"
 #include "pre_attn.h"
@@ -213,6 +214,37 @@ int check_pack(int32_t n_rows, int32_t hidden) {
   return PA_OK;
 }
 
+// The allocation-free decode call's workspace: one array per GPU, held until
+// the process ends. Host code never passes its name to a kernel (on the host
+// it is a stand-in, not a device address); it uses the address
+// hipGetSymbolAddress returns for the current device, taken once per device
+// with that device current.
+constexpr size_t kScratchBytes = size_t(24) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, cleared on its first use (the
+// synchronization words must start at zero; calls leave them zero).
+int scratch_for_current_device(void*& out, void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if ((e = pa::launch_fill_zero(ptr, kScratchBytes, static_cast<hipStream_t>(stream))) != hipSuccess)
+      return hip_fail(e, "scratch clear");
+    g_scratch_ptr[dev] = ptr;
+  }
+  out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,6 +338,27 @@ int pre_attn_decode(const pa_dims* dims, const uint16_t* ar, const uint16_t* res
                positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
                q_out, iq_out, workspace};
   return run(PA_MODE_DECODE, dims, p, nullptr, workspace_bytes, stream);
+}
+
+int pre_attn_decode_noalloc(const pa_dims* dims, const uint16_t* ar, const uint16_t* res, uint16_t* h_out,
+                            const uint16_t* g_in, const uint8_t* w_packed, const float* w_scale,
+                            const uint16_t* g_q, const uint16_t* g_k, const uint16_t* g_iq,
+                            const uint16_t* g_ik, const uint16_t* cos_sin, const int64_t* positions,
+                            const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                            float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
+                            uint16_t* iq_out, void* stream) {
+  int st = check_dims(dims, PA_MODE_DECODE);
+  if (st) return st;
+  if (workspace_for(dims, PA_MODE_DECODE) > kScratchBytes) return PA_ERR_WORKSPACE;
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(ws, stream);
+  if (st) return st;
+  const Ptrs p{ar, res, h_out, g_in, w_packed, w_scale, g_q, g_k, g_iq, g_ik, cos_sin,
+               positions, slot_mapping, k_cache, v_cache, k_scale, v_scale, index_cache,
+               q_out, iq_out, ws};
+  return run(PA_MODE_DECODE, dims, p, nullptr, kScratchBytes, stream);
 }
 
 int pre_attn_decode_ex(const pa_dims* dims, const pa_head_options* opts, const uint16_t* ar,
