@@ -130,16 +130,26 @@ int pa_decode_structure(const pa_dims* dims);
 
 /* Prepares a freshly allocated workspace of `bytes` bytes for use (clears the
  * library's counters with a fill kernel on `stream`). Needed once per
- * allocation; calls leave it ready for the next call. */
+ * allocation; calls leave it ready for the next call. The first time on each
+ * device it also checks where the dispatcher places workgroups (blocks with
+ * equal index mod 8 must share an XCD for the decode launches' hand-offs; if
+ * they do not, decode runs its stages in separate launches on that device),
+ * and for that synchronizes `stream` once. */
 int pa_workspace_init(void* workspace, size_t bytes, void* stream);
 
-/* Whether every call on this workspace since pa_workspace_init ran to
- * completion inside the kernels. A CTA that waits for another CTA's result
- * (the one-launch decode paths) gives up after a bounded spin, so that no
- * launch can hang, and then marks the workspace; the outputs of that call are
- * not valid. Returns PA_OK, or PA_ERR_SYNC once marked (until the next
- * pa_workspace_init). Unlike the other entry points this one synchronizes:
- * it waits for `stream` to finish, then reads one word of the workspace. */
+/* Whether every call on this workspace since pa_workspace_init produced valid
+ * outputs: they are valid exactly when this returns PA_OK, so a caller that
+ * must be certain checks it after its calls. Decode launches hand values
+ * between the CTAs of one XCD through its L2 (workgroups go to the XCDs
+ * round-robin, so blocks with equal index mod 8 share one; pa_workspace_init
+ * checks that once per device). No CTA waits for one that has not started,
+ * every wait is bounded, and a GEMV CTA whose wait for the token statistics
+ * gives up computes them itself. A call marks the workspace when a wait for
+ * the k slices' partial sums gave up (a started CTA never arrived); that
+ * call's outputs are not valid. Returns PA_OK, or PA_ERR_SYNC once marked
+ * (until the next pa_workspace_init). Unlike the other entry points this one
+ * synchronizes: it waits for `stream` to finish, then reads one word of the
+ * workspace. */
 int pa_workspace_status(const void* workspace, void* stream);
 
 /* Bytes of the packed weight (and packed block scales) for N rows x hidden. */

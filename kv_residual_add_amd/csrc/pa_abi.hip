@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -139,6 +140,17 @@ int check_ptrs(const Ptrs& p, bool has_q_fp8, bool nvfp4) {
   return PA_OK;
 }
 
+// Test hook: PA_DECODE_FORCE_PATHS=1 makes every decode GEMV CTA compute the
+// token statistics itself, =2 makes no k slice wait for the others (the slice
+// that arrives last runs every share of the head epilogue), =3 both. The
+// outputs are the same bits either way.
+uint32_t forced_paths() {
+  const char* v = std::getenv("PA_DECODE_FORCE_PATHS");
+  if (!v) return 0u;
+  const int f = std::atoi(v);
+  return ((f & 1) ? pa::kOptLocalStats : 0u) | ((f & 2) ? pa::kOptNoSliceWait : 0u);
+}
+
 pa::Args make_args(const pa_dims* d, const Ptrs& p, void* stream) {
   pa::Args a{};
   a.S = d->tokens;
@@ -190,7 +202,7 @@ int run(int mode, const pa_dims* dims, const Ptrs& p, const pa_head_options* opt
   pa::Args a = make_args(dims, p, stream);
   a.q_fp8 = o.q_fp8;
   a.q_fp8_inv = o.q_fp8_inv;
-  a.opts = (o.static_kv ? pa::kOptStaticKv : 0u) | (o.nvfp4 ? pa::kOptNvfp4 : 0u);
+  a.opts = (o.static_kv ? pa::kOptStaticKv : 0u) | (o.nvfp4 ? pa::kOptNvfp4 : 0u) | forced_paths();
   a.k_gs = o.k_gs;
   a.v_gs = o.v_gs;
   hipError_t e;
@@ -237,6 +249,8 @@ int scratch_for_current_device(void*& out, void* stream) {
     void* ptr = nullptr;
     if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
       return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if ((e = pa::probe_placement(ptr, static_cast<hipStream_t>(stream))) != hipSuccess)
+      return hip_fail(e, "scratch set-up");
     if ((e = pa::launch_fill_zero(ptr, kScratchBytes, static_cast<hipStream_t>(stream))) != hipSuccess)
       return hip_fail(e, "scratch clear");
     g_scratch_ptr[dev] = ptr;
@@ -280,7 +294,11 @@ int pa_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
   int st = check_device();
   if (st) return st;
-  hipError_t e = pa::launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (bytes >= pa::kSyncBytes && (e = pa::probe_placement(workspace, s)) != hipSuccess)
+    return hip_fail(e, "pa_workspace_init");
+  e = pa::launch_fill_zero(workspace, bytes, s);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_workspace_init");
 }
 

@@ -39,6 +39,12 @@
 // bf16 first).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -54,8 +60,9 @@ constexpr int kFusedMaxK = 8192;
 constexpr int kSxStride = 64;    // scale floats per XCD copy (and published words per XCD)
 constexpr int kMaxKsplit = kSyncMaxSlices;  // slice flags per head
 constexpr size_t kFusedEpiMaxWeight = 4u << 20;  // weight bytes up to which whole heads per XCD pay
-// GEMV + epilogue launch: a head's slices wait for each other, so they must be
-// resident together on the head's XCD: at most one slice per CU of an XCD
+// GEMV + epilogue launch: a head's slices sit on one XCD and hand their partial
+// sums over in its L2; at most one slice per CU of an XCD and one bit each in
+// a 32-bit mask
 constexpr int kGemvEpiMaxKsplit = 32;
 
 // Block reductions over up to 16 waves: each wave's result goes to LDS, then
@@ -303,27 +310,37 @@ constexpr int kSpinMax = 1 << 18;  // polls before a wait gives up (well under a
 struct Publish {
   const uint64_t* rstd;  // this XCD's per-token rstd bits (0: not yet; a real rstd is > 0)
   const uint64_t* srec;  // this XCD's per-token scale bits, tagged 1 in the upper half (0: not yet)
-  uint32_t* err;         // set if a wait gave up
+  float* sx;             // this XCD's per-token scales, read by the head epilogue
   uint32_t* done;        // this XCD's count of GEMV CTAs done with the values
+  uint32_t* err;         // the call's failure word
+  bool handoff;          // take the statistics from the XCD's norm CTAs (else compute them here)
 };
+
+// Records that this call's outputs are not valid (read by pa_workspace_status).
+__device__ __forceinline__ void mark_invalid(uint32_t* err) {
+  __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Waits until the XCD's S tokens are published and returns this lane's token's
 // rstd and scale (lanes t < S; the others get token 0's). Each value is one
 // naturally aligned 8-byte word written once per call, and it carries its own
 // readiness, so no flag and no store order is needed; a lane polls its token's
 // two words with agent-scope loads (not served by the CU's L1; they read the
-// XCD's L2, where the norm CTAs' plain stores land). Bounded like wait_flags.
-__device__ __forceinline__ void wait_stats(const Publish& pub, int S, double& rstd, float& sc) {
+// XCD's L2, where the norm CTAs' plain stores land). The norm CTAs come first
+// in dispatch order, so they are running or done; the wait is still bounded,
+// and returns false if it gave up (the caller then computes the values itself).
+__device__ __forceinline__ bool wait_stats(const Publish& pub, int S, double& rstd, float& sc) {
   const int lane = threadIdx.x & 63;
   const int t = lane < S ? lane : 0;
   uint64_t r = 0, c = 0;
+  bool ok = true;
   for (int it = 0;; ++it) {
     r = __hip_atomic_load(const_cast<uint64_t*>(pub.rstd) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     c = __hip_atomic_load(const_cast<uint64_t*>(pub.srec) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool ready = r != 0 && (c >> 32) == 1;
     if (__builtin_amdgcn_ballot_w64(lane < S && !ready) == 0ull) break;
     if (it == kSpinMax) {
-      if (lane == 0) __hip_atomic_store(pub.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = false;
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -331,36 +348,90 @@ __device__ __forceinline__ void wait_stats(const Publish& pub, int S, double& rs
   asm volatile("" ::: "memory");
   rstd = __longlong_as_double(static_cast<long long>(r));
   sc = __uint_as_float(static_cast<uint32_t>(c));
+  return ok;
 }
 
 
-// Waits until flags 0 .. n - 1 (n <= 64) are set: lane t polls flag t with an
-// agent-scope atomic load (not served by the CU's L1; it reads the XCD's L2,
-// where the setters' plain stores land). The wait is bounded: on giving up it
-// records the failure and returns, so every wave finishes.
-__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t* err) {
-  const int lane = threadIdx.x & 63;
-  const int t = lane < n ? lane : 0;
+// Waits until the counter reaches n (an agent-scope load, served by the XCD's
+// L2, where the counter's atomics execute). Bounded: returns false if it gave
+// up, so every wave finishes.
+__device__ __forceinline__ bool wait_count(const uint32_t* counter, uint32_t n) {
+  bool ok = true;
   for (int it = 0;; ++it) {
-    const uint32_t f =
-        __hip_atomic_load(const_cast<uint32_t*>(flags) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_ballot_w64(lane < n && f == 0u) == 0ull) break;
+    if (__hip_atomic_load(const_cast<uint32_t*>(counter), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
     if (it == kSpinMax) {
-      if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = false;
       break;
     }
     __builtin_amdgcn_s_sleep(2);
   }
   asm volatile("" ::: "memory");  // the loads after the wait stay after it
+  return ok;
+}
+
+// The token statistics (rstd and FP8 scale) of every row, computed by this CTA
+// alone: the fall-back of a GEMV CTA whose wait for its XCD's published values
+// gave up (and the path the host can force for tests). The same numbers as
+// norm_token's: the sum of squares in the same per-thread chains and block
+// reduction order (thread t owns the 8-element vectors t, t + 256, ...), then
+// the largest |xn| over the row, which is the value norm_token's owner finds.
+// Lane t of every wave gets token t's values, and thread 0 writes the XCD's
+// copy of each row's scale. Few registers: the forced path runs it before the
+// weight stream is issued, and the weights are in registers when a wait gives
+// up only in that rare case.
+template <int NV>
+__device__ __forceinline__ void local_stats(const KArgs& a, float* sx, double* red, double& rstd_l, float& sc_l) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int K = a.K, nvec = K >> 3;
+  for (int t = 0; t < a.S; ++t) {
+    const size_t base = static_cast<size_t>(t) * K;
+    double ssp[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma nounroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * 256;
+      if (v >= nvec) break;
+      const u32x4 av = *reinterpret_cast<const u32x4*>(a.ar + base + 8 * v);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(a.res + base + 8 * v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double lo = static_cast<double>(bf16_at_f32(av, 2 * q) + bf16_at_f32(bv, 2 * q));
+        const double hi = static_cast<double>(bf16_at_f32(av, 2 * q + 1) + bf16_at_f32(bv, 2 * q + 1));
+        ssp[q] = __builtin_fma(lo, lo, ssp[q]);
+        ssp[q] = __builtin_fma(hi, hi, ssp[q]);
+      }
+    }
+    const double ss = block_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), red);
+    const double rstd = 1.0 / __builtin_sqrt(ss / static_cast<double>(K) + static_cast<double>(a.eps));
+    double amax = 0.0;
+#pragma nounroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * 256;
+      if (v >= nvec) break;
+      const u32x4 av = *reinterpret_cast<const u32x4*>(a.ar + base + 8 * v);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(a.res + base + 8 * v);
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(a.g_in + 8 * v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float acc = bf16_at_f32(av, e) + bf16_at_f32(bv, e);
+        const double xn = (static_cast<double>(acc) * rstd) * (1.0 + static_cast<double>(bf16_at_f32(gv, e)));
+        amax = __builtin_fmax(amax, __builtin_fabs(xn));
+      }
+    }
+    amax = block_max_f64(amax, red);
+    const float sc = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
+    if (lane == t) rstd_l = rstd, sc_l = sc;
+    if (tid == 0) sx[t] = sc;
+  }
 }
 
 // One GEMV CTA: head h, k chunks [ks * CPC, + CPC). With a Publish (FUSED),
 // the weight stream and the CTA's slice of ar, res and g_in go out first;
 // once the XCD's norm CTAs have published each token's rstd and scale, the CTA
 // forms its slice's FP8 codes itself (codes8) straight into LDS.
-template <int CPC, int NT, bool FUSED>
+template <int CPC, int NT, bool FUSED, int NV = 1>
 __device__ __forceinline__ uint32_t gemv_tile(const KArgs& a, int h, int ks, const uint8_t* x8, float* part, int tlb,
-                                              const Publish& pub) {
+                                              const Publish& pub, double* red = nullptr) {
   uint32_t done_before = 0;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -369,6 +440,11 @@ __device__ __forceinline__ uint32_t gemv_tile(const KArgs& a, int h, int ks, con
   constexpr int ldw = CPC * 128 + kLdsPad;
   stamp(a.timeline, a.timeline_slots, tlb, 0);
 
+  double rstd_l = 0.0;  // FUSED: token lane's rstd and scale
+  float sc_l = 0.f;
+  if constexpr (FUSED) {
+    if (!pub.handoff) local_stats<NV>(a, pub.sx, red, rstd_l, sc_l);  // uniform over the launch
+  }
   const int per_row = CPC * 8;  // 16-byte pieces per token row
   constexpr int kMaxPieces = 64 * CPC * 8 / 256;
   i32x4 xv[kMaxPieces];
@@ -437,9 +513,15 @@ __device__ __forceinline__ uint32_t gemv_tile(const KArgs& a, int h, int ks, con
       }
   }
   if constexpr (FUSED) {
-    double rstd_l;
-    float sc_l;
-    wait_stats(pub, S, rstd_l, sc_l);  // lane t holds token t's values
+    // lane t holds token t's values: from the XCD's norm CTAs, or computed
+    // here when the wait gives up (every wave of the CTA decides alike)
+    if (pub.handoff) {
+      __shared__ int s_ok[4];
+      const bool ok = wait_stats(pub, S, rstd_l, sc_l);
+      if (lane == 0) s_ok[wave] = ok;
+      __syncthreads();
+      if (!(s_ok[0] && s_ok[1] && s_ok[2] && s_ok[3])) local_stats<NV>(a, pub.sx, red, rstd_l, sc_l);
+    }
 #pragma unroll
     for (int r = 0; r < kGroups; ++r) {
       const int i = tid + 256 * r;
@@ -507,7 +589,7 @@ template <int CPC, int NT>
 __global__ __launch_bounds__(256) void decode_gemv(KArgs a, size_t off_x8, size_t off_part) {
   const int tlb = a.S + blockIdx.y * gridDim.x + blockIdx.x;  // timeline slot
   gemv_tile<CPC, NT, false>(a, blockIdx.x, blockIdx.y, a.ws + off_x8, reinterpret_cast<float*>(a.ws + off_part), tlb,
-                     Publish{nullptr, nullptr, nullptr, nullptr});
+                            Publish{});
 }
 
 // ---------------------------------------------------------------------------
@@ -712,17 +794,20 @@ __device__ __forceinline__ void xcd_clear(const KArgs& a, uint32_t done_before, 
 //  - The GEMV CTAs follow. They stream their weights and their slice of ar,
 //    res and g_in at once, wait for their XCD's statistics, form the slice's
 //    FP8 codes (the norm's expressions) and store partial sums.
-//  - With EPI, head h runs all its k slices on XCD h % 8, and the head's last
-//    slice (the last of its CTAs in block order) waits for the other slices'
-//    flags, sums the partials (all in its L2) and runs the head's epilogue for
-//    every token. Whole heads per XCD can load some XCDs with more weight
-//    than others, so without EPI the slices spread evenly and the epilogue is
-//    the next launch.
-// No cache write-back or invalidate is needed and nothing crosses XCDs. The
-// norm CTAs come first in block order, so they are placed before any CTA that
-// waits for them, and the only wait is bounded. The GEMV CTA of an XCD that is
-// the last to be done with the XCD's published values clears them, a head's
-// epilogue CTA the slice flags, for the next call.
+//  - With EPI, head h runs all its k slices on XCD h % 8. Each slice stores its
+//    partial sums and takes an arrival ticket on the head's counter; the slice
+//    that arrives last (every partial is then in its L2) runs the head's
+//    epilogue for every token. No slice waits for another. Whole heads per XCD
+//    can load some XCDs with more weight than others, so without EPI the slices
+//    spread evenly and the epilogue is the next launch.
+// No cache write-back or invalidate is needed and nothing crosses XCDs (the
+// library checks once per device, when a workspace is set up, that blocks with
+// equal b % 8 share an XCD, and otherwise plans no hand-off inside a launch).
+// The only wait, a GEMV CTA's for its XCD's statistics, is on norm CTAs that
+// come first in dispatch order (so they are running or done), and is bounded;
+// if it gives up the CTA computes the statistics itself. The GEMV CTA of an
+// XCD that is the last to be done with the XCD's published values clears them,
+// a head's last slice its counter, for the next call.
 template <int CPC, int NV, bool EPI, bool OPT>
 __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
   __shared__ double red[64];
@@ -730,13 +815,15 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
   float* sx = reinterpret_cast<float*>(a.ws + p.off_sx) + x * kSxStride;
   uint64_t* pub_r = reinterpret_cast<uint64_t*>(a.ws + p.off_rstd) + x * 2 * kSxStride;
   uint64_t* pub_s = pub_r + kSxStride;
+  uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + p.off_err);
+  const bool stats_handoff = !(a.opts & kOptLocalStats);
   if (b < 8 * S) {
     const int tok = b >> 3;
     double rstd;
     float sc;
     bool owner;
     norm_token<NV, false>(a, tok, nullptr, sx, red, x == 0 ? tok : -1, x == 0, &rstd, &sc, &owner);
-    if (owner) {  // the thread that holds the row's scale
+    if (owner && stats_handoff) {  // the thread that holds the row's scale
       __builtin_amdgcn_s_waitcnt(0);  // sx (read by the epilogue) is in the L2 before the values are
       pub_r[tok] = static_cast<uint64_t>(__double_as_longlong(rstd));
       pub_s[tok] = (uint64_t{1} << 32) | __float_as_uint(sc);
@@ -756,26 +843,26 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
   }
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   uint32_t* done = reinterpret_cast<uint32_t*>(a.ws + p.off_done) + x * 32;
-  const uint32_t done_before =
-      gemv_tile<CPC, 1, true>(a, h, ks, nullptr, part, S + ks * H + h,
-                              Publish{pub_r, pub_s, reinterpret_cast<uint32_t*>(a.ws + p.off_err), done});
+  const uint32_t done_before = gemv_tile<CPC, 1, true, NV>(a, h, ks, nullptr, part, S + ks * H + h,
+                                                           Publish{pub_r, pub_s, sx, done, err, stats_handoff}, red);
   if constexpr (!EPI) {
     if (threadIdx.x == 0) xcd_clear(a, done_before, (H * ksplit - x + 7) / 8, done, pub_r, pub_s);
     return;
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
   __syncthreads();
-  uint32_t* hflags = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;
-  if (ks < ksplit - 1) {  // publish the slice to the head's epilogue CTA
-    if (threadIdx.x == 0) hflags[ks] = 1u;
-  } else {
-    // the head's epilogue CTA: dispatched after every other slice of the head
-    if (threadIdx.x < 64) wait_flags(hflags, ksplit - 1, reinterpret_cast<uint32_t*>(a.ws + p.off_err));
-    __syncthreads();
+  __shared__ uint32_t s_last;
+  uint32_t* harrive = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit + 1;
+  if (threadIdx.x == 0) {
+    s_last = __hip_atomic_fetch_add(harrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(ksplit - 1);
+  }
+  __syncthreads();
+  if (s_last) {  // every other slice of the head has stored its partial sums
+    if (threadIdx.x == 0) __hip_atomic_store(harrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int wave = threadIdx.x >> 6;
     for (int tok = wave; tok < S; tok += 4)
       head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, S + H * ksplit + tok * H + h);
-    if (threadIdx.x < ksplit - 1) hflags[threadIdx.x] = 0u;  // cleared for the next call
   }
   if (threadIdx.x == 0) xcd_clear(a, done_before, (H - x + 7) / 8 * ksplit, done, pub_r, pub_s);
 }
@@ -783,12 +870,17 @@ __global__ __launch_bounds__(256) void decode_fused(KArgs a, DecodePlan p) {
 // The GEMV with the head epilogue in the same launch, after a norm launch (more
 // tokens than the fused launch takes). Head h runs all its k slices on XCD
 // h % 8 (blocks with equal b % 8 share an XCD), so its partial sums stay in
-// that XCD's L2. Each slice stores its partial, sets its flag, waits for the
-// head's other flags, and then runs the head's epilogue for its share of the
-// tokens (ks, ks + ksplit, ...), reading the partials from the L2. The last
-// slice past the wait (a per-head counter) clears the flags for the next call.
-// A head's slices are dispatched together (a contiguous run of its XCD's
-// blocks, at most one per CU of the XCD), and every wait is bounded.
+// that XCD's L2, and each slice runs the head's epilogue for its share of the
+// tokens (ks, ks + ksplit, ...) once every slice's partial sums are stored.
+// Per head, four counters in the XCD's L2: started, arrived, the slices that
+// left their share to others, and done. A slice counts itself started before
+// its GEMV; after storing its partials it waits for the others only if all of
+// them have started (so it never waits for a CTA that has not begun, whatever
+// the dispatcher does), and otherwise leaves its share to the last arriver.
+// The slice that arrives last never waits: it runs its own share and every
+// share left to it. A wait can only give up if a started slice never arrives;
+// the call's outputs are then marked invalid. The slice that is done last
+// clears the counters for the next call.
 template <int CPC, int NT, bool OPT>
 __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   const int b = blockIdx.x, x = b & 7, j = b >> 3, H = a.heads(), ksplit = p.ksplit;
@@ -797,25 +889,50 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   const float* sx = reinterpret_cast<const float*>(a.ws + p.off_sx);
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + p.off_err);
-  gemv_tile<CPC, NT, false>(a, h, ks, a.ws + p.off_x8, part, a.S + ks * H + h, Publish{nullptr, nullptr, nullptr, nullptr});
+  uint32_t* hc = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;  // started, arrived, left, done
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(hc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  gemv_tile<CPC, NT, false>(a, h, ks, a.ws + p.off_x8, part, a.S + ks * H + h, Publish{});
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached the L2
   __syncthreads();
-  uint32_t* hflags = reinterpret_cast<uint32_t*>(a.ws + p.off_hdone) + h * kMaxKsplit;
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(a.ws + p.off_hcnt) + h;
-  if (threadIdx.x == 0) hflags[ks] = 1u;
-  if (threadIdx.x < 64) wait_flags(hflags, ksplit, err);
+  __shared__ uint32_t s_role, s_mask;  // role: 0 leaves its share, 1 waits, 2 arrived last
+  if (threadIdx.x == 0) {
+    const uint32_t me = 1u << ks;
+    const bool all_started =
+        __hip_atomic_load(hc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit) &&
+        !(a.opts & kOptNoSliceWait);
+    if (!all_started) {
+      __hip_atomic_fetch_or(hc + 2, me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);  // in the L2 before the arrival below
+    }
+    const bool last = __hip_atomic_fetch_add(hc + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      static_cast<uint32_t>(ksplit - 1);
+    s_role = last ? 2u : (all_started ? 1u : 0u);
+    s_mask = last ? (__hip_atomic_load(hc + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) | me)
+                  : (all_started ? me : 0u);
+  }
   __syncthreads();
+  uint32_t mask = s_mask;
+  if (s_role == 1u) {
+    __shared__ int s_ok;
+    if (threadIdx.x == 0) {
+      s_ok = wait_count(hc + 1, static_cast<uint32_t>(ksplit));
+      if (!s_ok) mark_invalid(err);
+    }
+    __syncthreads();
+    if (!s_ok) mask = 0u;
+  }
   stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 4);
-  // the counter's round trip is made by the last wave, which holds the fewest
-  // epilogue tokens (wave 0 holds the most)
+  // done with the counters; the slice done last clears them for the next call
   if (threadIdx.x == 192 &&
-      __hip_atomic_fetch_add(hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit - 1)) {
-    for (int f = 0; f < ksplit; ++f) hflags[f] = 0u;  // every slice is past its wait
-    __hip_atomic_store(hcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(hc + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(ksplit - 1)) {
+    for (int f = 0; f < 4; ++f) __hip_atomic_store(hc + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int wave = threadIdx.x >> 6;
-  for (int tok = ks + ksplit * wave; tok < a.S; tok += 4 * ksplit)
-    head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+  for (; mask != 0u; mask &= mask - 1u) {
+    const int sl = __builtin_ctz(mask);
+    for (int tok = sl + ksplit * wave; tok < a.S; tok += 4 * ksplit)
+      head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+  }
   stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 5);
 }
 
@@ -917,6 +1034,87 @@ hipError_t launch_fused(const Args& a, const DecodePlan& p) {
   return has_options(a) ? launch_fused_e<CPC, true, true>(a, p) : launch_fused_e<CPC, true, false>(a, p);
 }
 
+// CTAs of one launch that fit on a CU at once, from the occupancy API (cached
+// per kernel, LDS size and device), or, without a device, the counts the
+// compiler reports for these kernels (registers) and the 160 KB of LDS.
+int resident_per_cu(const void* fn, size_t lds, int fallback) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, fn, lds);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, lds) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = fallback;
+    if (lds > 0) n = std::min<int>(n, static_cast<int>((160u << 10) / lds));
+  }
+  cache[key] = n;
+  return n;
+}
+
+template <int C>
+int gemv_per_cu_c(int S, int K, bool fused, bool epi, bool gemv_epi) {
+  const size_t lds = static_cast<size_t>(S) * (C * 128 + kLdsPad);
+  const int nv = (K / 8 + 255) / 256;
+  if (fused) {
+    const void* f = nullptr;
+    switch (nv) {
+      case 1: f = epi ? (const void*)&decode_fused<C, 1, true, false> : (const void*)&decode_fused<C, 1, false, false>; break;
+      case 2: f = epi ? (const void*)&decode_fused<C, 2, true, false> : (const void*)&decode_fused<C, 2, false, false>; break;
+      case 3: f = epi ? (const void*)&decode_fused<C, 3, true, false> : (const void*)&decode_fused<C, 3, false, false>; break;
+      default: f = epi ? (const void*)&decode_fused<C, 4, true, false> : (const void*)&decode_fused<C, 4, false, false>; break;
+    }
+    return resident_per_cu(f, lds, nv == 1 ? 3 : (nv == 4 ? 1 : 2));
+  }
+  if (gemv_epi)
+    return resident_per_cu(S <= 32 ? (const void*)&decode_gemv_epi<C, 1, false> : (const void*)&decode_gemv_epi<C, 2, false>,
+                           lds, 3);
+  return resident_per_cu(S <= 32 ? (const void*)&decode_gemv<C, 1> : (const void*)&decode_gemv<C, 2>, lds, 7);
+}
+
+int gemv_per_cu(int c, int S, int K, bool fused, bool epi, bool gemv_epi) {
+  switch (c) {
+    case 1: return gemv_per_cu_c<1>(S, K, fused, epi, gemv_epi);
+    case 2: return gemv_per_cu_c<2>(S, K, fused, epi, gemv_epi);
+    case 3: return gemv_per_cu_c<3>(S, K, fused, epi, gemv_epi);
+    default: return gemv_per_cu_c<4>(S, K, fused, epi, gemv_epi);
+  }
+}
+
+// Whether the launches of the current device may hand values between CTAs
+// inside one XCD's L2: set once per device from a placement probe, true until
+// then.
+constexpr int kMaxDev = 64;
+std::atomic<int> g_handoff[kMaxDev];  // 0 not probed, 1 blocks with equal b % 8 share an XCD, -1 not
+
+bool handoff_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return g_handoff[dev].load(std::memory_order_relaxed) >= 0;
+}
+
+// Each block records its XCD (1 + the XCC_ID hardware register).
+__global__ void xcd_probe(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = 1u + (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int S, int K, int nkv) {
@@ -926,48 +1124,49 @@ DecodePlan decode_plan(int S, int K, int nkv) {
   const int heads = N / kHeadDim;
   // The largest chunk count that still gives every CU a CTA, among those whose
   // whole grid is resident at once (a grid in two rounds streams its second
-  // half only after the first has finished). CTAs per CU for 1..4 chunks,
-  // from register counts the compiler once reported for the GEMV with two
-  // token tiles (70, 94, 114, 150). The kernels have changed since (now 68-84
-  // for the GEMV alone, 124 with the epilogue in its launch), and only the
-  // choice of split depends on the table: a head's slices in the GEMV +
-  // epilogue launch need one CTA a CU, whatever the table says.
+  // half only after the first has finished). The CTAs a CU holds come from the
+  // occupancy API on the kernel the split would launch (its registers and LDS).
+  // No correctness depends on it: no CTA waits for one that has not started.
   // When no grid is resident at once (many heads and a long k), the largest
   // chunk count, i.e. the fewest CTAs, is taken.
   // In the one-launch structure the 8 S norm CTAs also occupy CUs: counted
-  // towards the 256, they let c2 take 4 chunks a CTA (240 GEMV CTAs + 64 norm
-  // CTAs): 12.2 vs 12.8 us a step with 3 chunks (320 + 64).
+  // towards the CU count, they let c2 take 4 chunks a CTA (240 GEMV CTAs + 64
+  // norm CTAs): 12.2 vs 12.8 us a step with 3 chunks (320 + 64).
   static const int kCands[] = {4, 3, 2, 1};
-  static const int kPerCu[] = {0, 7, 5, 4, 3};
-  const int norm_ctas = S <= kFusedMaxS && K <= kFusedMaxK ? 8 * S : 0;
+  const int cus = device_cus();
+  const bool fusable = S <= kFusedMaxS && K <= kFusedMaxK;
+  const bool epi_whole_heads = heads % 8 == 0 || static_cast<size_t>(N) * K <= kFusedEpiMaxWeight;
+  const int norm_ctas = fusable ? 8 * S : 0;
   int pick = 0, fewest = 0;
   for (int c : kCands) {
     if (nchk % c) continue;
     if (static_cast<size_t>(S) * (c * 128 + kLdsPad) > kMaxLds) continue;
     if (fewest == 0) fewest = c;
-    if (heads * (nchk / c) > 256 * kPerCu[c]) continue;
+    const int ks = nchk / c;
+    const int per_cu = gemv_per_cu(c, S, K, fusable, fusable && epi_whole_heads && ks <= kMaxKsplit,
+                                   !fusable && ks <= kGemvEpiMaxKsplit);
+    if (heads * ks > cus * per_cu) continue;
     pick = c;  // smallest fitting candidate so far
-    if (heads * (nchk / c) + norm_ctas >= 256) break;
+    if (heads * ks + norm_ctas >= cus) break;
   }
   if (pick == 0) pick = fewest;  // c = 1 always fits the LDS: S * 144 bytes
   p.chunks_per_cta = pick;
   p.ksplit = pick ? nchk / pick : 0;
-  p.fused = pick > 0 && S <= kFusedMaxS && K <= kFusedMaxK;
+  const bool handoff = handoff_ok();
+  p.fused = handoff && pick > 0 && S <= kFusedMaxS && K <= kFusedMaxK;
   // the head's epilogue in the same launch: heads then sit whole on XCDs, which
   // is balanced when they divide evenly, and cheap when the weight is small
-  p.fused_epilogue = p.fused && p.ksplit <= kMaxKsplit &&
-                     (heads % 8 == 0 || static_cast<size_t>(N) * K <= kFusedEpiMaxWeight);
+  p.fused_epilogue = p.fused && p.ksplit <= kMaxKsplit && epi_whole_heads;
   // more tokens: the epilogue joins the GEMV's launch, which saves the partial
   // sums' round trip through memory (ksplit x S x N floats)
-  p.gemv_epilogue = pick > 0 && !p.fused && p.ksplit <= kGemvEpiMaxKsplit;
+  p.gemv_epilogue = handoff && pick > 0 && !p.fused && p.ksplit <= kGemvEpiMaxKsplit;
   p.off_err = kSyncErr;
   p.off_done = kSyncDone;
   p.off_rstd = kSyncPub;  // published rstd and scale words
   p.off_hdone = kSyncHeadFlags;
-  p.off_hcnt = kSyncHeadCnt;
   size_t off = kSyncBytes;
-  p.off_x8 = off;  // the FP8 rows (not fused)
-  off = align_up(off + (p.fused ? 0 : static_cast<size_t>(S) * K), 256);
+  p.off_x8 = off;  // the FP8 rows (not fused; sized either way, so the size never depends on the structure)
+  off = align_up(off + static_cast<size_t>(S) * K, 256);
   p.off_sx = off;  // per-token scales: one copy per XCD when fused
   off = align_up(off + sizeof(float) * (p.fused ? 8 * kSxStride : S), 256);
   p.off_part = off;
@@ -1023,6 +1222,29 @@ hipError_t launch_pack_decode(const uint8_t* w, uint8_t* wp, int N, int K, hipSt
   const unsigned blocks = static_cast<unsigned>((pieces + 255) / 256);
   hipLaunchKernelGGL(pack_decode, dim3(blocks), dim3(256), 0, s, w, wp, N, K);
   return hipGetLastError();
+}
+
+// Checks once per device, on a workspace of at least kSyncBytes, that
+// workgroups with equal b % 8 run on one XCD (the dispatcher hands them to the
+// XCDs round-robin; its starting XCD may move from launch to launch, which the
+// hand-offs do not mind); otherwise decode plans no hand-off inside a launch.
+// Synchronizes `s` the first time.
+hipError_t probe_placement(void* ws, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev || g_handoff[dev].load(std::memory_order_relaxed) != 0) return hipSuccess;
+  constexpr int kBlocks = 2048;
+  static_assert(kBlocks * 4 <= static_cast<int>(kSyncBytes), "probe fits the synchronization words");
+  uint32_t rec[kBlocks];
+  hipLaunchKernelGGL(xcd_probe, dim3(kBlocks), dim3(64), 0, s, static_cast<uint32_t*>(ws));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipMemcpyAsync(rec, ws, sizeof(rec), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  bool ok = true;
+  for (int b = 0; b < kBlocks; ++b) ok = ok && rec[b] != 0u && rec[b] == rec[b % 8];
+  g_handoff[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  return hipSuccess;
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

@@ -16,6 +16,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // so the block does not grow with it.
 constexpr uint32_t kOptStaticKv = 1u;  // unit K / V scales
 constexpr uint32_t kOptNvfp4 = 2u;     // NVFP4 caches (k_cache = K/V cache, index_cache NVFP4)
+// Fall-back paths of the decode hand-offs, forced from the host for tests
+// (PA_DECODE_FORCE_PATHS): every GEMV CTA computes the token statistics itself;
+// no k slice waits for the others (the last arriver runs every share).
+constexpr uint32_t kOptLocalStats = 4u;
+constexpr uint32_t kOptNoSliceWait = 8u;
 
 struct KArgs {
   int S, K, nkv, num_pages, max_pos;
@@ -54,13 +59,15 @@ struct Args : KArgs {
 // offsets, whatever the call's dims and mode, and every call leaves them zero.
 // Data regions start past them, so one workspace can serve calls of any shape
 // in turn without a stale data byte ever reading as a flag.
-constexpr size_t kSyncErr = 0;             // failure word: a bounded wait gave up
+constexpr size_t kSyncErr = 0;             // failure word: a call's outputs are not valid
 constexpr size_t kSyncDone = 256;          // per-XCD GEMV counters, 128 bytes apart
 constexpr size_t kSyncPub = 1280;          // per-XCD published rstd and scale words
 constexpr size_t kSyncPubBytes = 2 * 8 * 64 * sizeof(uint64_t);
-constexpr size_t kSyncHeadFlags = kSyncPub + kSyncPubBytes;  // per-head slice flags
+// per-head counters of the k slices (started, arrived, bailed-out mask, done),
+// one 256-byte record per head
+constexpr size_t kSyncHeadFlags = kSyncPub + kSyncPubBytes;
 constexpr int kSyncMaxHeads = 19 * 4 + 1;  // heads at the largest nkv
-constexpr int kSyncMaxSlices = 64;         // slice flags per head
+constexpr int kSyncMaxSlices = 64;         // words per head record
 constexpr size_t kSyncHeadCnt = kSyncHeadFlags + kSyncMaxHeads * kSyncMaxSlices * sizeof(uint32_t);
 constexpr size_t kSyncBytes = 32768;
 static_assert(kSyncHeadCnt + kSyncMaxHeads * sizeof(uint32_t) <= kSyncBytes, "synchronization words overflow");
@@ -72,7 +79,7 @@ struct DecodePlan {
   bool fused;          // norm and GEMV in one launch (a per-XCD copy of the FP8 rows)
   bool fused_epilogue; // the head epilogue in that launch too
   bool gemv_epilogue;  // not fused: the head epilogue in the GEMV's launch
-  size_t off_x8, off_sx, off_rstd, off_part, off_done, off_hdone, off_hcnt, off_err, total;
+  size_t off_x8, off_sx, off_rstd, off_part, off_done, off_hdone, off_err, total;
 };
 DecodePlan decode_plan(int S, int K, int nkv);
 hipError_t launch_decode(const Args& a, const DecodePlan& p);
@@ -93,6 +100,7 @@ size_t prefill_packed_weight_bytes(int N, int K);
 size_t prefill_packed_scale_bytes(int N, int K);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t probe_placement(void* ws, hipStream_t s);
 
 inline hipError_t mark(hipEvent_t ev, hipStream_t s) {
   return ev ? hipEventRecord(ev, s) : hipSuccess;

@@ -384,13 +384,13 @@ def test_norm_scale_with_exact_ties(S, K):
     parity.check_written_sets(inp, got)
     ws = p.workspace.cpu().numpy()
     base = parity.SYNC_BYTES
+    off = base + -(-(S * K) // 256) * 256  # past the room for the codes [S][K]
     if fused:  # no activation codes in the workspace; 8 copies of the scales, 64 apart
         for x in range(8):
-            sx = ws[base + 4 * 64 * x: base + 4 * (64 * x + S)].view(np.float32)
+            sx = ws[off + 4 * 64 * x: off + 4 * (64 * x + S)].view(np.float32)
             assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (x, sx, ref["s_x"])
     else:  # codes [S][K], then the scales from the next 256-byte boundary
         assert np.array_equal(ws[base: base + S * K].reshape(S, K), ref["x8"])
-        off = base + -(-(S * K) // 256) * 256
         sx = ws[off: off + 4 * S].view(np.float32)
         assert np.array_equal(sx.view(np.uint32), ref["s_x"].view(np.uint32)), (sx, ref["s_x"])
 
@@ -490,3 +490,29 @@ def test_prefill_pack_checks_precise_exponents():
         with pytest.raises(B.PaError) as e:
             B.pa_pack_weight_prefill(w, bad, wp, sp)
         assert e.value.status == B.PA_ERR_WEIGHT_RANGE, (row, code)
+
+
+@pytest.mark.parametrize("force", [1, 2, 3])
+@pytest.mark.parametrize("S,K,nkv", [(1, 1024, 1), (8, 6144, 1), (40, 2048, 2), (64, 6144, 2)],
+                         ids=lambda v: str(v))
+def test_decode_forced_fallback_paths(monkeypatch, S, K, nkv, force):
+    # The hand-offs' fall-back paths, forced from the host: every GEMV CTA of
+    # the one-launch structures computes the token statistics itself (1), and
+    # no k slice of the GEMV + epilogue launch waits for the others, so the
+    # slice that arrives last runs every share of the head epilogue (2). The
+    # outputs are the plain call's, bit for bit, and the oracle's.
+    from kv_residual_add_amd.runner import Problem
+
+    wl = _wl("decode", S, K, nkv, skip_frac=0.1)
+    _say(f"forced paths {force} {wl.name}")
+    inp = synth.make_workload(wl, seed=S + K + nkv)
+    plain = Problem(inp)
+    plain.run()
+    want = plain.outputs()
+    monkeypatch.setenv("PA_DECODE_FORCE_PATHS", str(force))
+    p = Problem(inp)
+    p.run()
+    got = p.outputs()
+    for k in want:
+        assert np.array_equal(want[k].view(np.uint8), got[k].view(np.uint8)), k
+    parity.compare(inp, oracle.decode(inp), got)
