@@ -173,7 +173,8 @@ int pa_pack_weight_decode(const uint8_t* w, uint8_t* w_packed, int32_t n_rows,
  *   s_packed  output, pa_packed_scale_bytes(PA_MODE_PREFILL, ...) bytes
  * The k, v and index_k heads (whose per-token FP8 scales and codes must follow
  * the exact projection to 1e-6) are computed on bf16 MFMAs from the MXFP8
- * values widened exactly to bf16, which holds while every weight value
+ * values widened exactly to bf16 (the packed weight carries a bf16 copy of
+ * those 2 nkv + 1 heads' rows), which holds while every weight value
  * code * 2^(e - 127) is a normal bf16 number: each E8M0 code e of those rows
  * must lie in [10, 246]. This call checks that and returns PA_ERR_WEIGHT_RANGE
  * otherwise (the packed buffers are written either way). Unlike the other

@@ -201,11 +201,24 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
 // Packed weight: head h, k step ks, 32-row tile m -> 2 KB block at
 // ((h * nks + ks) * 4 + m) * 2048 in the activation's lane order (row
 // 32m + l % 32). Scales: dword (h * nks + ks) * 64 + l holds tiles m = 0..3 in
-// bytes 0..3, each the row's E8M0 for block 2 ks + l / 32. The precise heads
-// (k, v, index_k) read the same FP8 tiles and widen them to bf16 themselves.
+// bytes 0..3, each the row's E8M0 for block 2 ks + l / 32.
+// After the FP8 blocks of every head, the precise heads (k heads, v heads,
+// then index_k: precise index p) carry a bf16 copy of their weight, each value
+// code * 2^(e - 127) exactly (E8M0 codes in [10, 246]), in the bf16 MFMA's
+// operand order: a 16 KB block per k step; in it row tile m and MFMA step j
+// (16 k) hold 1 KB at m * 4096 + j * 1024, lane l's 8 values at 16 l: row
+// 32 m + l % 32, k = 64 ks + 32 (j / 2) + 16 (l / 32) + 8 (j % 2) + [0, 8)
+// (the k order the activation operand takes from its FP8 fragment).
+constexpr int kBf16StepBytes = 16384;
 
 __device__ __forceinline__ bool precise_head(int h, int nkv) {
   return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv;
+}
+
+__host__ __device__ __forceinline__ int precise_index(int h, int nkv) { return h < 18 * nkv ? h - 16 * nkv : 2 * nkv; }
+
+__host__ __device__ __forceinline__ size_t precise_panel_offset(int N, int K, int p) {
+  return static_cast<size_t>(N) * K + static_cast<size_t>(p) * kHeadDim * K * 2;
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
@@ -253,21 +266,26 @@ struct Panels {
   __amdgpu_buffer_rsrc_t a, sa, b, sb;
 };
 
-template <int NTW>
+template <bool PRECISE, int NTW>
 __device__ __forceinline__ Panels make_panels(const KArgs& a, int h, int tt0, const uint8_t* xq, const uint8_t* xs) {
   const size_t nks = a.K / kKStep;
   Panels p;
-  p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
+  if (PRECISE)  // the head's bf16 panel
+    p.a = panel(a.w_packed + precise_panel_offset(a.N(), a.K, precise_index(h, a.nkv)), nks * kBf16StepBytes);
+  else
+    p.a = panel(a.w_packed + static_cast<size_t>(h) * nks * 4 * kTileBytes, nks * 4 * kTileBytes);
   p.sa = panel(a.s_packed + static_cast<size_t>(h) * nks * 256, nks * 256);
   p.b = panel(xq + static_cast<size_t>(tt0) * nks * kTileBytes, NTW * nks * kTileBytes);
   p.sb = panel(xs + static_cast<size_t>(tt0) * nks * 64, NTW * nks * 64);
   return p;
 }
 
-// Vector-memory instructions one stage issues per wave (the waits count them).
-template <int NTW, int SUB>
+// Vector-memory instructions one stage issues per wave (the waits count them):
+// per k step the weight tile's LDS copies (FP8: 2, bf16: 4) and, FP8 only, the
+// weight scale dword, then two activation loads and a scale byte per token tile.
+template <bool PRECISE, int NTW, int SUB>
 constexpr int step_vm_ops() {
-  return SUB * (2 + 1 + 2 * NTW + NTW);
+  return SUB * ((PRECISE ? 4 : 3) + 2 * NTW + NTW);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory instructions of
@@ -284,7 +302,7 @@ __device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW, SUB>& st, const 
 #pragma unroll
   for (int u = 0; u < SUB; ++u) {
     const int ks = stage * SUB + u;
-    st.sa[u] = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
+    if constexpr (!PRECISE) st.sa[u] = __builtin_amdgcn_raw_buffer_load_b32(p.sa, lane * 4, ks * 256, 0);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
       const int blk = n * nks + ks;
@@ -294,14 +312,23 @@ __device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW, SUB>& st, const 
     }
   }
   // weight tiles: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16
-  // of step u's tile, which land at the same offset of the slot's half u
+  // of step u's tile, which land at the same offset of the slot's part u
+  // (FP8: two 8 KB steps a slot; bf16: one 16 KB step a slot, SUB = 1)
+  if constexpr (PRECISE) {
+    static_assert(SUB == 1, "a bf16 weight step fills a ring slot");
 #pragma unroll
-  for (int u = 0; u < SUB; ++u)
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p.a, (__attribute__((address_space(3))) void*)(slot + q * 4096 + wave * 1024),
+                                               16, tid * 16, stage * kBf16StepBytes + q * 4096, 0, 0);
+  } else {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          p.a, (__attribute__((address_space(3))) void*)(slot + u * 8192 + q * 4096 + wave * 1024), 16, tid * 16,
-          (stage * SUB + u) * 4 * kTileBytes + q * 4096, 0, 0);
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            p.a, (__attribute__((address_space(3))) void*)(slot + u * 8192 + q * 4096 + wave * 1024), 16, tid * 16,
+            (stage * SUB + u) * 4 * kTileBytes + q * 4096, 0, 0);
+  }
 }
 
 // The MFMAs of one k step: weight scale dword sa0, activation fragments b0 and
@@ -311,11 +338,12 @@ __device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2
                                           const uint8_t* slot, f32x16 (&acc)[NTW][4]) {
   const int lane = threadIdx.x & 63;
   if (PRECISE) {
-    // bf16 MFMA step j takes bytes 8j .. 8j + 7 of each lane's 32-byte fragment
-    // (k = 32 (j / 2) + 16 (lane / 32) + 8 (j % 2) + [0, 8)), widened exactly
-    // with the block scale; bytes 0..15 are MX block 0 and 16..31 block 1, and
-    // the lane ^ 32 partner holds the scales of the other block.
-    const uint32_t sa_x = __shfl_xor(sa0, 32, 64);
+    // bf16 MFMA step j takes bytes 8j .. 8j + 7 of each lane's 32-byte
+    // activation fragment (k = 32 (j / 2) + 16 (lane / 32) + 8 (j % 2) + [0, 8)),
+    // widened exactly with the block scale (bytes 0..15 are MX block 0 and
+    // 16..31 block 1; the lane ^ 32 partner holds the scale of the other
+    // block); the weight operand is the same k of the slot's bf16 tile.
+    (void)sa0;
     uint32_t sb_x[NTW];
 #pragma unroll
     for (int n = 0; n < NTW; ++n) sb_x[n] = __shfl_xor(sb0[n], 32, 64);
@@ -329,11 +357,9 @@ __device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2
         const i32x4& src = b0[n][j >> 1];
         B[n] = fp8x8_to_bf16(src[2 * (j & 1)], src[2 * (j & 1) + 1], e8m0_to_f32((own ? sb0[n] : sb_x[n]) & 0xffu));
       }
-      const uint32_t sw = own ? sa0 : sa_x;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint2 af = *reinterpret_cast<const uint2*>(slot + m * kTileBytes + (j >> 1) * 1024 + lane * 16 + (j & 1) * 8);
-        const bf16x8 A = fp8x8_to_bf16(af.x, af.y, e8m0_to_f32((sw >> (8 * m)) & 0xffu));
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(slot + m * 4096 + j * 1024 + lane * 16);
 #pragma unroll
         for (int n = 0; n < NTW; ++n) acc[n][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[n], acc[n][m], 0, 0, 0);
       }
@@ -376,7 +402,7 @@ template <bool PRECISE, int NTW, int SUB, int I>
 __device__ __forceinline__ void pipeline_step(Stage<PRECISE, NTW, SUB> (&st)[kSlots], uint8_t* const (&ring)[kSlots],
                                               const Panels& p, int nks, int s, int wave, f32x16 (&acc)[NTW][4]) {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kPrefetch - 1) * step_vm_ops<NTW, SUB>()));
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kPrefetch - 1) * step_vm_ops<PRECISE, NTW, SUB>()));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const int last = nks / SUB - 1;
@@ -393,7 +419,7 @@ __device__ __forceinline__ void mainloop(const KArgs& a, int h, int tt0, const u
   const int nks = a.K / kKStep;
   const int nst = nks / SUB;  // stages (hidden is a multiple of 128: nks is even)
   const int last = nst - 1;
-  const Panels p = make_panels<NTW>(a, h, tt0, xq, xs);
+  const Panels p = make_panels<PRECISE, NTW>(a, h, tt0, xq, xs);
   Stage<PRECISE, NTW, SUB> st[kSlots];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
@@ -815,10 +841,11 @@ __device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, 
 // (workgroups are dispatched round-robin over the eight XCDs), and each XCD
 // takes a list of heads across every token tile, so the CTAs running together
 // re-read those heads' weight panels and the token tiles' activation panels
-// from that XCD's L2. A precise head (bf16 MFMA) costs 2.2 FP8 heads (measured
-// main loop 146 vs 67 us at 256 tokens); the lists balance that cost (longest
-// first, each to the least loaded XCD) and put the precise heads first, so the
-// longest CTAs of an XCD start earliest.
+// from that XCD's L2. A precise head (bf16 MFMA) costs 1.7 FP8 heads in the
+// lists (the span was shortest at that weight among 1.4, 1.7 and 2.2, on c4 and
+// c5 alike); the lists balance that cost (longest first, each to the least
+// loaded XCD) and put the precise heads first, so the longest CTAs of an XCD
+// start earliest.
 constexpr int kMaxHeads = 19 * 4 + 1;  // 128-row heads at nkv = 4, the largest nkv accepted
 
 struct HeadMap {
@@ -881,10 +908,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* _
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[n][m][r] = 0.f;
-  // one-tile CTAs have the registers for two k steps a stage: twice the lookahead
+  // one-tile FP8 CTAs have the registers for two k steps a stage: twice the
+  // lookahead (a bf16 weight step fills a ring slot by itself)
   constexpr int SUB = NTW == 1 ? kSubSingle : 1;
   if (precise_head(h, a.nkv))
-    mainloop<true, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
+    mainloop<true, NTW, 1>(a, h, tt0, xq, xs, ring, wave, acc);
   else
     mainloop<false, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
 #pragma unroll
@@ -924,6 +952,26 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* _
   static_assert(NTW <= 2, "the epilogue calls above cover two token tiles");
   stamp(a.timeline, a.timeline_slots, b, 2);
   stamp_place(a.timeline, a.timeline_slots, b, 7);
+}
+
+// The precise heads' bf16 panels (one thread per 16-byte piece: 8 values).
+__global__ void pack_prefill_bf16(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
+                                  uint8_t* __restrict__ wp, int N, int K) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nkv = (N / kHeadDim - 1) / 19;
+  const size_t per_head = static_cast<size_t>(kHeadDim) * K * 2 / 16;  // pieces of one panel
+  if (idx >= per_head * (2 * nkv + 1)) return;
+  const int pidx = static_cast<int>(idx / per_head);
+  const size_t r = idx % per_head;
+  const int ks = static_cast<int>(r / 1024), q = static_cast<int>(r % 1024);
+  const int m = q >> 8, j = (q >> 6) & 3, l = q & 63;
+  const int h = pidx < 2 * nkv ? 16 * nkv + pidx : 19 * nkv;
+  const int row = h * kHeadDim + 32 * m + (l & 31);
+  const int k = ks * kKStep + 32 * (j >> 1) + 16 * (l >> 5) + 8 * (j & 1);
+  const uint2 codes = *reinterpret_cast<const uint2*>(w + static_cast<size_t>(row) * K + k);
+  const uint32_t e = we[static_cast<size_t>(row) * (K / 32) + k / 32];
+  *reinterpret_cast<bf16x8*>(wp + precise_panel_offset(N, K, pidx) + static_cast<size_t>(ks) * kBf16StepBytes +
+                             m * 4096 + j * 1024 + l * 16) = fp8x8_to_bf16(codes.x, codes.y, e8m0_to_f32(e));
 }
 
 __global__ void pack_prefill(const uint8_t* __restrict__ w, const uint8_t* __restrict__ we,
@@ -1018,7 +1066,10 @@ PrefillPlan prefill_plan(int M, int K, int nkv) {
   return p;
 }
 
-size_t prefill_packed_weight_bytes(int N, int K) { return static_cast<size_t>(N) * K; }
+size_t prefill_packed_weight_bytes(int N, int K) {
+  const int nkv = (N / kHeadDim - 1) / 19;
+  return precise_panel_offset(N, K, 2 * nkv + 1);
+}
 size_t prefill_packed_scale_bytes(int N, int K) { return static_cast<size_t>(N) * K / 32; }
 
 // Token tiles of 32 per wave: 1 (128-token CTAs) or 2 (256-token CTAs, half
@@ -1039,14 +1090,14 @@ HeadMap make_head_map(int nkv) {
   auto precise = [&](int h) { return (h >= 16 * nkv && h < 18 * nkv) || h == 19 * nkv; };
   int load[8] = {0}, count[8] = {0};  // in tenths of an FP8 head
   int owner[kMaxHeads];
-  for (int pass = 0; pass < 2; ++pass)  // precise heads (cost 22) first, then FP8 heads (cost 10)
+  for (int pass = 0; pass < 2; ++pass)  // precise heads (cost 17) first, then FP8 heads (cost 10)
     for (int h = 0; h < H; ++h) {
       if (precise(h) != (pass == 0)) continue;
       int best = 0;
       for (int x = 1; x < 8; ++x)
         if (load[x] < load[best] || (load[x] == load[best] && count[x] < count[best])) best = x;
       owner[h] = best;
-      load[best] += precise(h) ? 22 : 10;
+      load[best] += precise(h) ? 17 : 10;
       ++count[best];
     }
   HeadMap m{};
@@ -1094,6 +1145,12 @@ hipError_t launch_pack_prefill(const uint8_t* w, const uint8_t* we, uint8_t* wp,
   const size_t pieces = static_cast<size_t>(N) * K / 16;
   const unsigned blocks = static_cast<unsigned>((pieces + 255) / 256);
   hipLaunchKernelGGL(pack_prefill, dim3(blocks), dim3(256), 0, s, w, we, wp, sp, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkv = (N / kHeadDim - 1) / 19;
+  const size_t bf_pieces = static_cast<size_t>(2 * nkv + 1) * kHeadDim * K * 2 / 16;
+  hipLaunchKernelGGL(pack_prefill_bf16, dim3(static_cast<unsigned>((bf_pieces + 255) / 256)), dim3(256), 0, s, w, we,
+                     wp, N, K);
   return hipGetLastError();
 }
 

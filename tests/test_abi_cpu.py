@@ -90,7 +90,7 @@ def test_workspace_sync_words_fixed():
 def test_packed_sizes():
     assert K.pa_packed_weight_bytes(0, 2560, 6144) == 2560 * 6144
     # FP8 codes of every row + bf16 copies of the k, v and index_k heads
-    assert K.pa_packed_weight_bytes(1, 9856, 6144) == 9856 * 6144
+    assert K.pa_packed_weight_bytes(1, 9856, 6144) == 9856 * 6144 + 9 * 128 * 6144 * 2
     assert K.pa_packed_scale_bytes(1, 9856, 6144) == 9856 * 6144 // 32
     assert K.pa_packed_weight_bytes(0, 2561, 6144) == 0
     assert K.pa_packed_weight_bytes(0, 19 * 3 * 128 + 128, 6144) == 0  # nkv = 3
