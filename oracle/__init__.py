@@ -1,11 +1,14 @@
-"""CPU oracle for the MiniMax-M3 pre-attention prologue.
+"""CPU oracle for the MiniMax-M3 pre-attention prologue and the DSpark drafter's
+attention.
 
 TEST INFRASTRUCTURE ONLY. This package is a plain, slow, NumPy (float64 unless
 the method fixes float32) statement of what the prologue computes, written from
 the vLLM API pages ``vllm.models.minimax_m3.amd.mono.kernels.pre_attn`` (the
 "K1 mono_pre" decode kernel) and
 ``vllm.models.minimax_m3.nvidia.ops.qkv_index_fused_epilogue`` (the MXFP8
-prefill GEMM with a fused epilogue). Only the tests, the smoke check and the
+prefill GEMM with a fused epilogue), and, in ``drafter.py``, from
+``vllm.models.minimax_m3.amd.mono.drafter.attention`` (the drafter's
+split-KV attention). Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import it; the HIP library never calls it and
 shares no code, table or constant generator with it.
 
@@ -40,3 +43,4 @@ from .prologue import (  # noqa: F401
     project_mxfp8,
     quantize_per_token,
 )
+from . import drafter  # noqa: F401,E402

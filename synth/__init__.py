@@ -1,4 +1,5 @@
-"""Seeded synthetic workloads for the MiniMax-M3 pre-attention prologue.
+"""Seeded synthetic workloads for the MiniMax-M3 pre-attention prologue and the
+DSpark drafter's attention.
 
 This module only draws random inputs (activations, gammas, weights, RoPE table,
 positions, slot mappings, sentinel-filled caches). It holds none of the
@@ -16,3 +17,4 @@ from .inputs import (  # noqa: F401
     named_config,
     with_nvfp4_caches,
 )
+from .drafter import make_drafter  # noqa: F401,E402
