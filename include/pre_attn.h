@@ -306,11 +306,77 @@ int pre_attn_prefill_ex(const pa_dims* dims, const pa_head_options* opts, const 
                         float* k_scale, float* v_scale, uint8_t* index_cache, uint16_t* q_out,
                         uint16_t* iq_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- The DSpark drafter's attention ------------------------------------------
+ * Source: the vLLM API page "vllm.models.minimax_m3.amd.mono.drafter.attention"
+ * (module docstring; window; kv_load; block_math; block_acc; qkv_rows;
+ * merge_task; store_partial). Per request r (query rows 7 r .. 7 r + 6, one KV
+ * head shared by 16 q heads of 128 dims):
+ *   - each q head of a row and the row's new k: Gemma RMSNorm over the head
+ *     (qn / kn, eps), NeoX RoPE on dims 0..63 (cos_sin row of the row's
+ *     position), E4M3 with unit scale (nearest even, saturating); the new v:
+ *     E4M3. The new k and v codes are written to the cache at the row's slot.
+ *   - the window: p0 = the first row's position, lo = max(p0 - 4095, 0),
+ *     hi = min(seq_len - 1, (lo / 128 + 34) * 128 - 1); key kp is visible to a
+ *     row at position qp iff kp > qp - 4096 and lo <= kp <= hi (no causal mask
+ *     among the 7 rows).
+ *   - the blocks lo / 128 .. hi / 128 are cut into partitions of `split`
+ *     blocks; per partition and (row, head) an online softmax block by block:
+ *     s = q8 . k8 (decoded codes), m' = max(m, block max), alpha =
+ *     2^((m - m') C), p = 2^(s C - (m' C - 8)) with C = log2(e) / sqrt(128),
+ *     l = l alpha + sum p, o = o alpha + sum E4M3(p) v8 (P in e4m3).
+ *   - the partitions are merged in order (weights 2^((m_i - M) C)); o / l is
+ *     rounded to bf16 and quantized to MXFP8 (OCP MX: E8M0 scale
+ *     2^(floor(log2 amax) - 8) per 32 values, E4M3 codes, saturating). A head
+ *     that sees no key outputs zeros.
+ * The result depends on `split` (P is rounded relative to each partition's
+ * running maximum). The FP8 products are summed exactly widened to bf16 on
+ * bf16 MFMAs with float32 accumulation.
+ * Layouts (device memory, caller-owned):
+ *   q            bf16 [7 R][16][128];  k, v  bf16 [7 R][128]   (new rows)
+ *   qn, kn       bf16 [128];  cos_sin  bf16 [max_pos][64] (cos | sin)
+ *   positions    int64 [7 R];  slots  int64 [7 R] (cache slot of the row's new
+ *                key: block slot / 128, key slot % 128; < 0 or past the cache:
+ *                not written)
+ *   kv_cache     uint8 [num_blocks][128][256]: key entry = 128 K codes then
+ *                128 V codes
+ *   block_table  int32 [R][table_width] (physical block of each logical block;
+ *                out-of-range entries are clamped, never dereferenced)
+ *   seq_lens     int32 [R] (keys 0 .. seq_len - 1 exist, the new rows included)
+ *   out_codes    uint8 [7 R][16 * 128] E4M3;  out_scales uint8 [7 R][64] E8M0
+ *   out_bf16     bf16 [7 R][16][128], optional (NULL: not written)
+ * Alignment: kv_cache, out_bf16 and the workspace 16 bytes; out_codes 8;
+ * positions and slots 8; block_table and seq_lens 4; the bf16 inputs 2.
+ * Three launches on `stream`; no allocation, no synchronization. Errors as the
+ * prologue's (PA_ERR_DIMS for a bad field of the dims). */
+#define PA_DRAFTER_ROWS 7
+#define PA_DRAFTER_HEADS 16
+#define PA_DRAFTER_BLOCK 128
+#define PA_DRAFTER_MAX_SPLIT 34
+typedef struct pa_drafter_dims {
+  int32_t requests;     /* R, 1 .. 2^20 */
+  int32_t num_blocks;   /* blocks of kv_cache, >= 1 */
+  int32_t table_width;  /* columns of block_table, >= 1 */
+  int32_t max_pos;      /* rows of cos_sin, >= 1 */
+  int32_t split;        /* blocks per split-KV partition, 1 .. 34 */
+  float eps;            /* the head norms' epsilon */
+} pa_drafter_dims;
+
+/* Workspace bytes of a drafter call (0 on bad dims). */
+size_t pa_drafter_workspace_bytes(const pa_drafter_dims* dims);
+
+int pa_drafter_attention(const pa_drafter_dims* dims, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const uint16_t* qn, const uint16_t* kn,
+                         const uint16_t* cos_sin, const int64_t* positions, const int64_t* slots,
+                         uint8_t* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                         uint8_t* out_codes, uint8_t* out_scales, uint16_t* out_bf16,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Instrumentation: from now on, calls on this host thread record `start` and
  * `stop` (hipEvent_t, created by the caller) on their stream immediately
  * before and after their dominant kernel (decode: the projection GEMV;
  * prefill: the MFMA GEMM with the fused epilogue), so that
- * hipEventElapsedTime gives that kernel's duration. Both NULL turns it off.
+ * hipEventElapsedTime gives that kernel's duration (the drafter: its split-KV
+ * attention launch). Both NULL turns it off.
  * The events stay owned by the caller. */
 int pa_set_kernel_events(void* start, void* stop);
 

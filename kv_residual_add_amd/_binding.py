@@ -56,11 +56,24 @@ EXPORTS = (
     "pre_attn_decode_ex",
     "pre_attn_prefill_ex",
     "pre_attn_decode_noalloc",
+    "pa_drafter_workspace_bytes",
+    "pa_drafter_attention",
     "pa_set_kernel_events",
     "pa_set_timeline",
     "pa_strerror",
     "pa_last_error_detail",
 )
+
+
+class pa_drafter_dims(ctypes.Structure):
+    _fields_ = [
+        ("requests", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("table_width", ctypes.c_int32),
+        ("max_pos", ctypes.c_int32),
+        ("split", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
 
 
 class pa_dims(ctypes.Structure):
@@ -155,6 +168,11 @@ def load() -> ctypes.CDLL:
         lib.pre_attn_prefill_ex.restype = ctypes.c_int
         lib.pre_attn_decode_noalloc.argtypes = [dims_p] + [P] * 20 + [P]
         lib.pre_attn_decode_noalloc.restype = ctypes.c_int
+        ddims_p = ctypes.POINTER(pa_drafter_dims)
+        lib.pa_drafter_workspace_bytes.argtypes = [ddims_p]
+        lib.pa_drafter_workspace_bytes.restype = sz
+        lib.pa_drafter_attention.argtypes = [ddims_p] + [P] * 15 + [sz, P]
+        lib.pa_drafter_attention.restype = ctypes.c_int
         lib.pa_set_timeline.argtypes = [P, sz]
         lib.pa_set_timeline.restype = ctypes.c_int
         lib.pa_set_kernel_events.argtypes = [P, P]
@@ -402,3 +420,34 @@ def pre_attn_decode_noalloc(dims, ar, res, h_out, g_in, w_packed, w_scale, g_q, 
     ]
     _check(load().pre_attn_decode_noalloc(ctypes.byref(dims), *args, _stream(stream)),
            "pre_attn_decode_noalloc")
+
+
+def pa_drafter_workspace_bytes(dims: pa_drafter_dims) -> int:
+    return load().pa_drafter_workspace_bytes(ctypes.byref(dims))
+
+
+def pa_drafter_attention(dims, q, k, v, qn, kn, cos_sin, positions, slots, kv_cache, block_table,
+                         seq_lens, out_codes, out_scales, out_bf16, workspace, stream=None) -> None:
+    """The DSpark drafter's attention; argument meaning as in include/pre_attn.h
+    (out_bf16 may be None)."""
+    R, W, NB, L = dims.requests, dims.table_width, dims.num_blocks, dims.max_pos
+    T = 7 * R
+    dev = q.device
+    bf, u8, i32, i64 = torch.bfloat16, torch.uint8, torch.int32, torch.int64
+    need = pa_drafter_workspace_bytes(dims)
+    if need == 0:
+        _check(PA_ERR_DIMS, "pa_drafter_attention")
+    if workspace.dtype != u8 or workspace.device != dev or not workspace.is_contiguous() or workspace.numel() < need:
+        raise ValueError(f"workspace: need a contiguous uint8 tensor of {need} bytes on {dev}")
+    args = [
+        _ptr(q, "q", bf, T * 16 * HEAD_DIM, dev), _ptr(k, "k", bf, T * HEAD_DIM, dev),
+        _ptr(v, "v", bf, T * HEAD_DIM, dev), _ptr(qn, "qn", bf, HEAD_DIM, dev), _ptr(kn, "kn", bf, HEAD_DIM, dev),
+        _ptr(cos_sin, "cos_sin", bf, L * 64, dev), _ptr(positions, "positions", i64, T, dev),
+        _ptr(slots, "slots", i64, T, dev), _ptr(kv_cache, "kv_cache", u8, NB * 128 * 256, dev),
+        _ptr(block_table, "block_table", i32, R * W, dev), _ptr(seq_lens, "seq_lens", i32, R, dev),
+        _ptr(out_codes, "out_codes", u8, T * 2048, dev), _ptr(out_scales, "out_scales", u8, T * 64, dev),
+        None if out_bf16 is None else _ptr(out_bf16, "out_bf16", bf, T * 2048, dev),
+        workspace.data_ptr(),
+    ]
+    _check(load().pa_drafter_attention(ctypes.byref(dims), *args, workspace.numel(), _stream(stream)),
+           "pa_drafter_attention")

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpre_attn.so")
-SOURCES = ["pa_abi.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_abi.hip", "pa_decode.hip", "pa_prefill.hip", "pa_drafter.hip"]
 
 
 def hipcc() -> str:

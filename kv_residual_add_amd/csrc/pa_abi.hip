@@ -421,6 +421,57 @@ int pre_attn_prefill_ex(const pa_dims* dims, const pa_head_options* opts, const 
   return run(PA_MODE_PREFILL, dims, p, opts, workspace_bytes, stream);
 }
 
+size_t pa_drafter_workspace_bytes(const pa_drafter_dims* d) {
+  if (!d || d->requests < 1 || d->requests > (1 << 20) || d->split < 1 || d->split > PA_DRAFTER_MAX_SPLIT)
+    return 0;
+  return pa::drafter_plan(d->requests, d->split).total;
+}
+
+int pa_drafter_attention(const pa_drafter_dims* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* qn, const uint16_t* kn, const uint16_t* cos_sin,
+                         const int64_t* positions, const int64_t* slots, uint8_t* kv_cache,
+                         const int32_t* block_table, const int32_t* seq_lens, uint8_t* out_codes,
+                         uint8_t* out_scales, uint16_t* out_bf16, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!d) return PA_ERR_NULL;
+  if (d->requests < 1 || d->requests > (1 << 20)) return PA_ERR_TOKENS;
+  if (d->num_blocks < 1 || d->table_width < 1 || d->max_pos < 1 || d->split < 1 ||
+      d->split > PA_DRAFTER_MAX_SPLIT || !std::isfinite(d->eps) || d->eps < 0.0f)
+    return PA_ERR_DIMS;
+  const void* req[] = {q, k, v, qn, kn, cos_sin, positions, slots, kv_cache, block_table, seq_lens,
+                       out_codes, out_scales, workspace};
+  for (const void* p : req)
+    if (!p) return PA_ERR_NULL;
+  const void* a2[] = {q, k, v, qn, kn, cos_sin};
+  for (const void* p : a2)
+    if (!aligned(p, 2)) return PA_ERR_ALIGN;
+  if (!aligned(kv_cache, 16) || !aligned(workspace, 16) || (out_bf16 && !aligned(out_bf16, 16)) ||
+      !aligned(out_codes, 8) || !aligned(positions, 8) || !aligned(slots, 8) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  const pa::DrafterPlan plan = pa::drafter_plan(d->requests, d->split);
+  if (workspace_bytes < plan.total) return PA_ERR_WORKSPACE;
+  int st = check_device();
+  if (st) return st;
+  pa::DArgs a{};
+  a.requests = d->requests;
+  a.num_blocks = d->num_blocks;
+  a.table_width = d->table_width;
+  a.max_pos = d->max_pos;
+  a.split = d->split;
+  a.eps = d->eps;
+  a.q = q, a.k = k, a.v = v, a.qn = qn, a.kn = kn, a.cos_sin = cos_sin;
+  a.positions = positions, a.slots = slots, a.kv_cache = kv_cache;
+  a.block_table = block_table, a.seq_lens = seq_lens;
+  a.out_codes = out_codes, a.out_scales = out_scales, a.out_bf16 = out_bf16;
+  a.ws = static_cast<uint8_t*>(workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  a.ev_start = g_ev_start;
+  a.ev_stop = g_ev_stop;
+  const hipError_t e = pa::launch_drafter(a, plan);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_drafter_attention");
+}
+
 const char* pa_strerror(int status) {
   switch (status) {
     case PA_OK: return "success";

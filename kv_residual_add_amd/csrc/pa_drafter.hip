@@ -1,0 +1,349 @@
+// Attention of the DSpark drafter on gfx950: the split-KV partitions with the q
+// and k head norms and RoPE in front of them, and the merge that writes MXFP8
+// for o_proj (the vLLM API page vllm.models.minimax_m3.amd.mono.drafter.
+// attention: module docstring, window, kv_load, block_math, block_acc,
+// qkv_rows, merge_task, store_partial).
+//
+// Three launches on the caller's stream:
+//   1. drafter_rows   one CTA per query row: its 16 q heads and its new k get
+//                     the head RMSNorm (Gemma form) and NeoX RoPE on dims 0..63
+//                     in float64 and are cast to E4M3 (unit scale, saturating);
+//                     the new v is cast to E4M3. q codes go to the workspace,
+//                     the new k and v codes into the paged cache at the row's
+//                     slot.
+//   2. drafter_split  one CTA per (request, partition of `split` blocks): the
+//                     128-key blocks of the request's window, each staged in
+//                     LDS as bf16 (K row-major, V transposed with its keys in
+//                     the PV operand's order), then one wave per query row runs
+//                     the online softmax for its 16 heads: S^T = K Q^T on
+//                     16x16x32 bf16 MFMAs leaves keys 16 i + 4 g .. + 3 of a
+//                     head in one lane, which is exactly the PV operand's k
+//                     slice, so P never leaves the registers: P = 256
+//                     exp((s - m) / sqrt(128)) is rounded to E4M3 and O^T =
+//                     V^T P^T accumulates on the same MFMAs. The partial
+//                     (m, l, o) goes to the workspace.
+//   3. drafter_merge  one CTA per query row: the partitions merged in order,
+//                     o / l rounded to bf16 and quantized to MXFP8 (E8M0 per 32
+//                     values, OCP MX rule).
+//
+// The page computes q . k and P V on FP8 MFMAs; those sum their products at a
+// reduced internal precision, so here every FP8 operand is widened exactly to
+// bf16 and the products are summed in float32 (the same exact products).
+#include <hip/hip_runtime.h>
+
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kQpr = 7;          // query rows per request
+constexpr int kHeads = 16;       // q heads per row
+constexpr int kBlock = 128;      // keys per cache block
+constexpr int kKeyBytes = 256;   // K codes | V codes
+constexpr int kWindow = 4096;
+constexpr int kMaxB = 34;        // blocks a request's window may span
+constexpr float kQkC = 0.127517430824598679f;  // log2(e) / sqrt(128)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_pos) {
+  return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+}
+
+// Step d1 for one query row: 16 q heads, then k, then v, four waves taking
+// the 18 tasks in turn. Lane l holds dims l and l + 64; the RoPE partner of
+// dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
+__global__ __launch_bounds__(256) void drafter_rows(DArgs a) {
+#pragma clang fp contract(off)
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t pos = clamp_pos(a.positions[t], a.max_pos);
+  const double c = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + (lane & 31)]));
+  const double sn = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + 32 + (lane & 31)]));
+  const int64_t slot = a.slots[t];
+  const bool store = slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * kBlock;
+  uint8_t* key = a.kv_cache + (store ? slot : 0) * kKeyBytes;
+  for (int task = wave; task < kHeads + 2; task += 4) {
+    if (task == kHeads + 1) {  // v: its E4M3 codes (bf16 values, exact in float64)
+      const uint16_t* v = a.v + static_cast<size_t>(t) * kHeadDim;
+      const uint32_t c2 = e4m3x2_scaled(bf16_to_f32(v[lane]), bf16_to_f32(v[lane + 64]), fp8_scale(0));
+      if (store) {
+        key[kHeadDim + lane] = static_cast<uint8_t>(c2);
+        key[kHeadDim + lane + 64] = static_cast<uint8_t>(c2 >> 8);
+      }
+      continue;
+    }
+    const uint16_t* x = task < kHeads ? a.q + (static_cast<size_t>(t) * kHeads + task) * kHeadDim
+                                      : a.k + static_cast<size_t>(t) * kHeadDim;
+    const uint16_t* g = task < kHeads ? a.qn : a.kn;
+    const double y0 = bf16_to_f32(x[lane]), y1 = bf16_to_f32(x[lane + 64]);
+    const double ss = wave_sum_f64(y0 * y0 + y1 * y1);
+    const double r = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
+    const double n0 = (y0 * r) * (1.0 + static_cast<double>(bf16_to_f32(g[lane])));
+    const double n1 = (y1 * r) * (1.0 + static_cast<double>(bf16_to_f32(g[lane + 64])));
+    const double partner = __shfl_xor(n0, 32, 64);
+    const double o0 = lane < 32 ? n0 * c - partner * sn : n0 * c + partner * sn;
+    const uint32_t c2 = e4m3x2_scaled(o0, n1, fp8_scale(0));
+    if (task < kHeads) {
+      uint8_t* q8 = a.q8 + (static_cast<size_t>(t) * kHeads + task) * kHeadDim;
+      q8[lane] = static_cast<uint8_t>(c2);
+      q8[lane + 64] = static_cast<uint8_t>(c2 >> 8);
+    } else if (store) {
+      key[lane] = static_cast<uint8_t>(c2);
+      key[lane + 64] = static_cast<uint8_t>(c2 >> 8);
+    }
+  }
+}
+
+// The request's window (step d2): first / last visible key and block.
+struct Window {
+  int lo, hi, b0, b1;
+};
+
+__device__ __forceinline__ Window request_window(const DArgs& a, int r) {
+  const int p0 = static_cast<int>(clamp_pos(a.positions[r * kQpr], 1 << 30));
+  const int seq = a.seq_lens[r];
+  Window w;
+  w.lo = p0 - (kWindow - 1) > 0 ? p0 - (kWindow - 1) : 0;
+  const int cap = (w.lo / kBlock + kMaxB) * kBlock - 1;
+  w.hi = seq - 1 < cap ? seq - 1 : cap;
+  w.b0 = w.lo / kBlock;
+  w.b1 = w.hi >= w.lo ? w.hi / kBlock : w.b0 - 1;  // no block when the window is empty
+  return w;
+}
+
+// Key slot o (0..31) of a 32-key group in the V^T tile: the PV operand's lane
+// group g takes keys 4g .. 4g + 3 of the group's two 16-key S tiles, so key
+// 16 a + 4 g + e sits at 8 g + 4 a + e.
+__device__ __forceinline__ int vt_slot(int o) { return ((o >> 2) & 3) * 8 + (o >> 4) * 4 + (o & 3); }
+
+// Step d3 for one partition of one request: 8 waves; wave j < 7 holds query
+// row j (its 16 heads: lane l has head l % 16). LDS: K of the block as bf16
+// [key][dim] and V^T as bf16 [dim][key slot], 32 KB each, rows of 256 bytes
+// whose 16-byte chunks are XOR-swizzled by row % 8 against bank conflicts.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 7)); }
+
+__global__ __launch_bounds__(512) void drafter_split(DArgs a) {
+  __shared__ __align__(16) bf16x8_t k_lds[kBlock * 16];     // 128 rows x 16 chunks of 8 bf16
+  __shared__ __align__(16) __bf16 vt_lds[kHeadDim * kBlock];  // 128 rows x 128 bf16
+  const int part = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const Window w = request_window(a, r);
+  const int bs = w.b0 + part * a.split;
+  const int be = bs + a.split - 1 < w.b1 ? bs + a.split - 1 : w.b1;
+  const int row = r * kQpr + wave;  // this wave's query row (waves < 7)
+  const int qp = wave < kQpr ? static_cast<int>(clamp_pos(a.positions[row], 1 << 30)) : 0;
+
+  // Q^T operand: head l16, dims 32 kk + 8 g4 .. + 7, widened exactly
+  bf16x8_t qb[4];
+  if (wave < kQpr) {
+    const uint8_t* q8 = a.q8 + (static_cast<size_t>(row) * kHeads + l16) * kHeadDim + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint2 c = *reinterpret_cast<const uint2*>(q8 + 32 * kk);
+      qb[kk] = fp8x8_to_bf16(c.x, c.y, 1.0f);
+    }
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int blk = bs; blk <= be; ++blk) {
+    // the block's keys: clamped metadata keeps every address inside the table
+    // row and the cache (kv_load); keys outside [lo, hi] read as zeros
+    const int col = blk < a.table_width ? blk : a.table_width - 1;
+    int phys = a.block_table[static_cast<size_t>(r) * a.table_width + (col < 0 ? 0 : col)];
+    phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+    const uint8_t* base = a.kv_cache + static_cast<size_t>(phys) * kBlock * kKeyBytes;
+    __syncthreads();  // the previous block's tiles are no longer read
+    {
+      // K: thread t widens dims 32 (t % 4) .. + 31 of key t / 4
+      const int km = tid >> 2, kq = tid & 3;
+      const int kp = blk * kBlock + km;
+      const bool live = kp >= w.lo && kp <= w.hi;
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq);
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq + 16);
+      const uint32_t z = live ? ~0u : 0u;
+      k_lds[swz(km, 4 * kq + 0)] = fp8x8_to_bf16(c0[0] & z, c0[1] & z, 1.0f);
+      k_lds[swz(km, 4 * kq + 1)] = fp8x8_to_bf16(c0[2] & z, c0[3] & z, 1.0f);
+      k_lds[swz(km, 4 * kq + 2)] = fp8x8_to_bf16(c1[0] & z, c1[1] & z, 1.0f);
+      k_lds[swz(km, 4 * kq + 3)] = fp8x8_to_bf16(c1[2] & z, c1[3] & z, 1.0f);
+      // V: thread t widens dims 32 (t / 128) .. + 31 of key t % 128 into V^T
+      const int vk = tid & 127, vc = tid >> 7;
+      const int vp = blk * kBlock + vk;
+      const uint32_t vz = (vp >= w.lo && vp <= w.hi) ? ~0u : 0u;
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + vk * kKeyBytes + kHeadDim + 32 * vc);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + vk * kKeyBytes + kHeadDim + 32 * vc + 16);
+      const int ks = (vk & ~31) + vt_slot(vk & 31);
+      const uint32_t words[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8_t b = fp8x8_to_bf16(words[2 * q] & vz, words[2 * q + 1] & vz, 1.0f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * vc + 8 * q + e;
+          vt_lds[d * kBlock + ((((ks >> 3) ^ (d & 7)) << 3) | (ks & 7))] = b[e];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave >= kQpr) continue;
+
+    // S^T = K Q^T: s[4 i + e] is key 16 i + 4 g4 + e of the block for head l16
+    float s[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_lds[swz(16 * i + l16, 4 * kk + g4)], qb[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kp = blk * kBlock + 16 * i + 4 * g4 + e;
+        const bool vis = kp > qp - kWindow && kp >= w.lo && kp <= w.hi;
+        s[4 * i + e] = vis ? acc[e] : -__builtin_inff();
+      }
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int x = 1; x < 32; ++x) mb = fmaxf(mb, s[x]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);
+    const float ms = mn == -__builtin_inff() ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f((m - ms) * kQkC);
+    const float off = ms * kQkC - 8.0f;
+    float p[32], ps = 0.f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      p[x] = __builtin_amdgcn_exp2f(s[x] * kQkC - off);
+      ps += p[x];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = mn;
+    // P in e4m3 (p <= 256: no saturation), widened back exactly: the PV
+    // operand of key step t is keys 32 t + 4 g4 + [0, 4) and 32 t + 16 + 4 g4
+    // + [0, 4), i.e. p[8 t .. 8 t + 7]
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      int lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t], p[8 * t + 1], 0, false);
+      lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 2], p[8 * t + 3], lo8, true);
+      int hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 4], p[8 * t + 5], 0, false);
+      hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 6], p[8 * t + 7], hi8, true);
+      pb[t] = fp8x8_to_bf16(static_cast<uint32_t>(lo8), static_cast<uint32_t>(hi8), 1.0f);
+    }
+    // O^T += V^T P^T: o[n][e] is dim 16 n + 4 g4 + e of head l16
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      f32x4 acc = o[n] * alpha;
+      const int d = 16 * n + l16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ks = 32 * t + 8 * g4;  // 8 key slots
+        const bf16x8_t va =
+            *reinterpret_cast<const bf16x8_t*>(vt_lds + d * kBlock + ((((ks >> 3) ^ (d & 7)) << 3)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], acc, 0, 0, 0);
+      }
+      o[n] = acc;
+    }
+  }
+  if (wave >= kQpr) return;
+  // the partial of (row, partition): m and l per head, o [16][128]
+  float* pm = a.part + (static_cast<size_t>(row) * a.nsplit + part) * kHeads * (2 + kHeadDim);
+  if (g4 == 0) {
+    pm[l16] = m;
+    pm[kHeads + l16] = l;
+  }
+  float* po = pm + 2 * kHeads + l16 * kHeadDim;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(po + 16 * n + 4 * g4) = o[n];
+}
+
+// Step d4: thread (head tid / 16, dims 8 (tid % 16) .. + 7) merges the
+// partitions in order; four threads make one 32-value MX block.
+__global__ __launch_bounds__(256) void drafter_merge(DArgs a) {
+#pragma clang fp contract(off)
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int h = tid >> 4, d0 = 8 * (tid & 15);
+  const size_t stride = static_cast<size_t>(kHeads) * (2 + kHeadDim);
+  const float* pr = a.part + static_cast<size_t>(row) * a.nsplit * stride;
+  float M = -__builtin_inff();
+  for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, pr[i * stride + h]);
+  const float Ms = M == -__builtin_inff() ? 0.f : M;
+  float L = 0.f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < a.nsplit; ++i) {
+    const float* p = pr + i * stride;
+    const float wgt = __builtin_amdgcn_exp2f((p[h] - Ms) * kQkC);
+    L = L + wgt * p[kHeads + h];
+    const float4 o0 = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0);
+    const float4 o1 = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0 + 4);
+    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] = O[e] + wgt * ov[e];
+  }
+  const bool none = M == -__builtin_inff();
+  float ob[8];  // the bf16 outputs as float32
+  u32x4 hb;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float x0 = none ? 0.f : O[e] / L, x1 = none ? 0.f : O[e + 1] / L;
+    hb[e >> 1] = pack_bf16x2(x0, x1);
+    ob[e] = bf16_to_f32(hb[e >> 1] & 0xffffu);
+    ob[e + 1] = bf16_to_f32(hb[e >> 1] >> 16);
+  }
+  const size_t oi = static_cast<size_t>(row) * kHeads * kHeadDim + h * kHeadDim + d0;
+  if (a.out_bf16) *reinterpret_cast<u32x4*>(a.out_bf16 + oi) = hb;
+  // MX block of dims 32 b .. + 31: threads tid & ~3 .. + 3
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, __builtin_fabsf(ob[e]));
+  am = fmaxf(am, __shfl_xor(am, 1, 64));
+  am = fmaxf(am, __shfl_xor(am, 2, 64));
+  int code = static_cast<int>((__float_as_uint(am) >> 23) & 0xffu) - 8;  // floor(log2 amax) - 8 + 127
+  code = code < 0 ? 0 : (code > 254 ? 254 : code);
+  code = am != 0.f ? code : 127;
+  const Fp8Scale f = fp8_scale(code - 127);
+  const uint32_t w0 = e4m3x4_scaled(ob[0], ob[1], ob[2], ob[3], f);
+  const uint32_t w1 = e4m3x4_scaled(ob[4], ob[5], ob[6], ob[7], f);
+  *reinterpret_cast<uint2*>(a.out_codes + oi) = make_uint2(w0, w1);
+  if ((tid & 3) == 0) a.out_scales[oi / 32] = static_cast<uint8_t>(code);
+}
+
+}  // namespace
+
+DrafterPlan drafter_plan(int requests, int split) {
+  DrafterPlan p{};
+  p.nsplit = (kMaxB + split - 1) / split;
+  const size_t rows = static_cast<size_t>(requests) * kQpr;
+  size_t off = kSyncBytes;
+  p.off_q8 = off;
+  off = align_up(off + rows * kHeads * kHeadDim, 256);
+  p.off_part = off;
+  off = align_up(off + rows * p.nsplit * kHeads * (2 + kHeadDim) * sizeof(float), 256);
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_drafter(const DArgs& a0, const DrafterPlan& p) {
+  DArgs a = a0;
+  a.q8 = a.ws + p.off_q8;
+  a.part = reinterpret_cast<float*>(a.ws + p.off_part);
+  a.nsplit = p.nsplit;
+  const int rows = a.requests * kQpr;
+  hipLaunchKernelGGL(drafter_rows, dim3(rows), dim3(256), 0, a.stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(drafter_split, dim3(p.nsplit, a.requests), dim3(512), 0, a.stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(a.ev_stop, a.stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(drafter_merge, dim3(rows), dim3(256), 0, a.stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

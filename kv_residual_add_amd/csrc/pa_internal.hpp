@@ -99,6 +99,29 @@ hipError_t prefill_weight_range_ok(const uint8_t* we, int N, int K, hipStream_t 
 size_t prefill_packed_weight_bytes(int N, int K);
 size_t prefill_packed_scale_bytes(int N, int K);
 
+// The DSpark drafter's attention (pa_drafter.hip).
+struct DArgs {
+  int requests, num_blocks, table_width, max_pos, split, nsplit;
+  float eps;
+  const uint16_t *q, *k, *v, *qn, *kn, *cos_sin;
+  const int64_t *positions, *slots;
+  uint8_t* kv_cache;
+  const int32_t *block_table, *seq_lens;
+  uint8_t *out_codes, *out_scales;
+  uint16_t* out_bf16;  // optional
+  uint8_t* ws;
+  uint8_t* q8;         // workspace: the rows' q codes [7 R][16][128]
+  float* part;         // workspace: partials [7 R][nsplit][16][2 + 128]
+  hipStream_t stream;
+  hipEvent_t ev_start, ev_stop;
+};
+struct DrafterPlan {
+  int nsplit;  // partitions per request (34 blocks / split, rounded up)
+  size_t off_q8, off_part, total;
+};
+DrafterPlan drafter_plan(int requests, int split);
+hipError_t launch_drafter(const DArgs& a, const DrafterPlan& p);
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t probe_placement(void* ws, hipStream_t s);
 

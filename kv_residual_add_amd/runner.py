@@ -123,3 +123,42 @@ class Problem:
         for k in ("k_cache", "v_cache", "index_cache", "k_scale", "v_scale"):
             out[k] = self.t[k].cpu().numpy()
         return out
+
+
+class DrafterProblem:
+    """All device buffers of one drafter attention call (inputs from
+    synth.make_drafter)."""
+
+    def __init__(self, arrays: dict, device="cuda:0"):
+        self.device = torch.device(device)
+        dev = self.device
+        R = int(arrays["requests"])
+        T = 7 * R
+        bt = np.ascontiguousarray(arrays["block_table"], np.int32)
+        self.dims = B.pa_drafter_dims(R, int(arrays["kv_cache"].shape[0]), int(bt.shape[1]),
+                                      int(arrays["cos_sin"].shape[0]), int(arrays["split"]), float(arrays["eps"]))
+        t = {}
+        for key in ("q", "k", "v", "qn", "kn", "cos_sin"):
+            t[key] = _to_dev(arrays[key].view(np.int16), dev, torch.bfloat16)
+        t["positions"] = _to_dev(arrays["positions"].astype(np.int64), dev)
+        t["slots"] = _to_dev(arrays["slots"].astype(np.int64), dev)
+        t["kv_cache"] = _to_dev(arrays["kv_cache"], dev)
+        t["block_table"] = _to_dev(bt, dev)
+        t["seq_lens"] = _to_dev(np.asarray(arrays["seq_lens"], np.int32), dev)
+        t["out_codes"] = torch.empty((T, 2048), dtype=torch.uint8, device=dev)
+        t["out_scales"] = torch.empty((T, 64), dtype=torch.uint8, device=dev)
+        t["out_bf16"] = torch.empty((T, 16, 128), dtype=torch.bfloat16, device=dev)
+        self.t = t
+        self.workspace = torch.empty(B.pa_drafter_workspace_bytes(self.dims), dtype=torch.uint8, device=dev)
+
+    def run(self, stream=None, **over) -> None:
+        t = dict(self.t, **over)
+        B.pa_drafter_attention(self.dims, t["q"], t["k"], t["v"], t["qn"], t["kn"], t["cos_sin"],
+                               t["positions"], t["slots"], t["kv_cache"], t["block_table"], t["seq_lens"],
+                               t["out_codes"], t["out_scales"], t["out_bf16"], self.workspace, stream=stream)
+
+    def outputs(self) -> dict:
+        torch.cuda.synchronize(self.device)
+        return {"out_codes": self.t["out_codes"].cpu().numpy(), "out_scales": self.t["out_scales"].cpu().numpy(),
+                "out_bf16": self.t["out_bf16"].view(torch.int16).cpu().numpy().view(np.uint16),
+                "kv_cache": self.t["kv_cache"].cpu().numpy()}
