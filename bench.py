@@ -37,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 KEYS = ["c1", "c2", "c3", "c4", "c5"]
+DRAFTER = "d1"  # the DSpark drafter's attention: 16 requests x 7 draft rows
+BF16_PEAK_TFLOPS = 2500.0
 HEADLINE = "c5"  # the largest configuration
 METRIC = "decode tokens/s + HBM GB/s (% of peak); prefill FP8 TFLOP/s (% MFMA peak)"
 
@@ -46,8 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="all", choices=["all"] + KEYS,
-                    help="one workload, or all five (headlined by c5)")
+    ap.add_argument("--config", default="all", choices=["all"] + KEYS + [DRAFTER],
+                    help="one workload, or all (headlined by c5); d1 is the drafter's attention")
     ap.add_argument("--pool-mb", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="approximate CPU time of each oracle baseline measurement (0 = skip)")
@@ -113,7 +115,7 @@ def algorithmic(wl, structure=0, head_options="none"):
 
 
 def source_sha(mode: str) -> str:
-    name = "pa_decode.hip" if mode == "decode" else "pa_prefill.hip"
+    name = {"decode": "pa_decode.hip", "prefill": "pa_prefill.hip", "drafter": "pa_drafter.hip"}[mode]
     with open(os.path.join(ROOT, "kv_residual_add_amd", "csrc", name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -339,6 +341,129 @@ def run_config(key, args):
     return rec
 
 
+def drafter_inputs(seed=0):
+    """d1: 16 requests of 7 draft rows, seq_len ~ U[2048, 12000], 2-block partitions."""
+    import synth
+    return synth.make_drafter(16, 12000, seed=seed, split=2, min_seq=2048)
+
+
+def drafter_work(inp):
+    """(algorithmic bytes, flops) of one drafter attention call: the K and V codes
+    of every key some row of its request sees (256 bytes a key), the rows' q codes
+    and MXFP8 outputs, the new rows' bf16 q / k / v; flops 2 x 2 x 16 x 128 per
+    (row, visible key) for Q K^T and P V."""
+    from oracle import drafter as D
+
+    pos = inp["positions"]
+    keys, pairs = 0, 0
+    for r in range(inp["requests"]):
+        lo, hi, _, _ = D.window(int(pos[7 * r]), int(inp["seq_lens"][r]))
+        keys += hi - lo + 1
+        for j in range(7):
+            qp = int(pos[7 * r + j])
+            pairs += hi - max(lo, qp - 4095) + 1
+    T = 7 * inp["requests"]
+    nbytes = keys * 256 + T * (2048 + 2048 + 64) + T * (16 * 256 + 2 * 256)
+    return nbytes, 4 * 16 * 128 * pairs
+
+
+def run_drafter(args):
+    import numpy as np
+    import torch
+
+    from kv_residual_add_amd import _binding as B
+    from kv_residual_add_amd.runner import DrafterProblem
+
+    inp = drafter_inputs()
+    nbytes, flops = drafter_work(inp)
+    prob = DrafterProblem(inp)
+    # a pool of caches (and block tables shifted over them) past the Infinity Cache
+    set_bytes = prob.t["kv_cache"].numel()
+    n_sets = max(2, math.ceil(args.pool_mb * 2**20 / set_bytes), min(args.steps, 64))
+    caches = [prob.t["kv_cache"]] + [prob.t["kv_cache"].clone() for _ in range(n_sets - 1)]
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device=prob.device)
+    flush_dst = torch.empty_like(flush_src)
+
+    def step(i):
+        prob.run(kv_cache=caches[i % n_sets])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                step(args.warmup + i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    flush_dst.copy_(flush_src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = max(time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3)
+    del graph
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    flush_dst.copy_(flush_src)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        B.pa_set_kernel_events(*evs[i])
+        step(args.warmup + i)
+    B.pa_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    rows = 7 * inp["requests"]
+    gbs = nbytes / (kern_ms / 1e3) / 1e9
+    tfs = flops / (kern_ms / 1e3) / 1e12
+    prof = _profile_record("kernel_times.json", DRAFTER, "drafter")
+    rec = {
+        "workload": "drafter_attention_r16_seq2k_12k_split2", "metric": "drafter rows/s", "unit": "rows/s",
+        "value": round(rows * args.steps / elapsed, 1), "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "dtype": "fp8_e4m3 (bf16 MFMA on exact widening)",
+        "config": {"workload": "drafter_attention_r16_seq2k_12k_split2", "requests": inp["requests"],
+                   "rows": rows, "split_blocks": inp["split"], "seq_lens": inp["seq_lens"].tolist(),
+                   "pool_sets": n_sets, "cache_flush_mb": 512, "timing": "hip graph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "drafter_split",
+                     "kernel_ms": round(kern_ms, 5), "kernel_ms_from": "hip events, eager pass",
+                     "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+                     "mfma_bf16_tflops": round(tfs, 1), "mfma_bf16_frac": round(tfs / BF16_PEAK_TFLOPS, 4)},
+    }
+    if prof:
+        rec["roofline"]["kernel_ms_rocprof"] = round(prof["avg_ns"] / 1e6, 5)
+        rec["roofline"]["frac_rocprof"] = round(nbytes / (prof["avg_ns"] / 1e9) / 1e9 / HBM_PEAK_GBS, 4)
+    del caches, prob, flush_src, flush_dst
+    torch.cuda.empty_cache()
+    if args.cpu_seconds > 0:
+        from oracle import drafter as D
+        import synth
+
+        sub = synth.make_drafter(2, 12000, seed=1, split=2, min_seq=2048)
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            D.attention(sub)
+            times.append(time.perf_counter() - t1)
+            if (time.perf_counter() - t_start > args.cpu_seconds and len(times) >= 2) or len(times) >= 100:
+                break
+        rec["cpu_baseline"] = {"value": 14 / float(np.median(times)), "unit": "rows/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"2 requests (14 rows) of the same recipe per call, median of "
+                                         f"{len(times)} calls ({sum(times):.1f} s), float64 NumPy"}
+    return rec
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -352,12 +477,12 @@ def main():
     import torch
 
     torch.cuda.set_device(0)
-    keys = KEYS if args.config == "all" else [args.config]
+    keys = KEYS + [DRAFTER] if args.config == "all" else [args.config]
     head = HEADLINE if args.config == "all" else args.config
     recs = {}
     for key in keys:
         print(f"bench: {key} ...", file=sys.stderr, flush=True)
-        recs[key] = run_config(key, args)
+        recs[key] = run_drafter(args) if key == DRAFTER else run_config(key, args)
         r = recs[key]
         print(f"bench: {key} {r['value']:.1f} {r['unit']}, {r['ms_per_step'] * 1e3:.2f} us a step, "
               f"roofline frac {r['roofline']['frac']}", file=sys.stderr, flush=True)
