@@ -51,19 +51,21 @@ __device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_pos) {
   return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
 }
 
-// Step d1 for one query row: 16 q heads, then k, then v, four waves taking
-// the 18 tasks in turn. Lane l holds dims l and l + 64; the RoPE partner of
-// dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
+// Step d1 for one query row: its 18 tasks (16 q heads, k, v) one wave each,
+// four to a CTA (blockIdx.y picks the four). Lane l holds dims l and l + 64;
+// the RoPE partner of dim l < 64 is dim l ^ 32, i.e. lane l ^ 32.
 __global__ __launch_bounds__(256) void drafter_rows(DArgs a) {
 #pragma clang fp contract(off)
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int task = static_cast<int>(blockIdx.y) * 4 + wave;
+  if (task >= kHeads + 2) return;
   const int64_t pos = clamp_pos(a.positions[t], a.max_pos);
   const double c = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + (lane & 31)]));
   const double sn = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + 32 + (lane & 31)]));
   const int64_t slot = a.slots[t];
   const bool store = slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * kBlock;
   uint8_t* key = a.kv_cache + (store ? slot : 0) * kKeyBytes;
-  for (int task = wave; task < kHeads + 2; task += 4) {
+  {
     if (task == kHeads + 1) {  // v: its E4M3 codes (bf16 values, exact in float64)
       const uint16_t* v = a.v + static_cast<size_t>(t) * kHeadDim;
       const uint32_t c2 = e4m3x2_scaled(bf16_to_f32(v[lane]), bf16_to_f32(v[lane + 64]), fp8_scale(0));
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void drafter_rows(DArgs a) {
         key[kHeadDim + lane] = static_cast<uint8_t>(c2);
         key[kHeadDim + lane + 64] = static_cast<uint8_t>(c2 >> 8);
       }
-      continue;
+      return;
     }
     const uint16_t* x = task < kHeads ? a.q + (static_cast<size_t>(t) * kHeads + task) * kHeadDim
                                       : a.k + static_cast<size_t>(t) * kHeadDim;
@@ -120,8 +122,14 @@ __device__ __forceinline__ int vt_slot(int o) { return ((o >> 2) & 3) * 8 + (o >
 // Step d3 for one partition of one request: 8 waves; wave j < 7 holds query
 // row j (its 16 heads: lane l has head l % 16). LDS: K of the block as bf16
 // [key][dim] and V^T as bf16 [dim][key slot], 32 KB each, rows of 256 bytes
-// whose 16-byte chunks are XOR-swizzled by row % 8 against bank conflicts.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 7)); }
+// whose 16-byte chunks are XOR-swizzled: K by row % 16 (the 16 rows an MFMA
+// operand read takes, and the 16 a staging write covers, fall on 16 chunk
+// positions); V^T by (d % 16) ^ (d / 16 % 16), which does the same for the
+// 16 dims of an operand read (d = 16 n + l) and of a staging write (d = 8 q + e).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+__device__ __forceinline__ int vt_off(int d, int ks) {  // element offset of V^T row d, key slot ks
+  return d * 128 + ((((ks >> 3) ^ ((d & 15) ^ ((d >> 4) & 15))) << 3) | (ks & 7));
+}
 
 __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
   __shared__ __align__(16) bf16x8_t k_lds[kBlock * 16];     // 128 rows x 16 chunks of 8 bf16
@@ -150,44 +158,58 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int blk = bs; blk <= be; ++blk) {
-    // the block's keys: clamped metadata keeps every address inside the table
-    // row and the cache (kv_load); keys outside [lo, hi] read as zeros
+  // One block's codes in this thread's registers: K bytes 32 (tid % 4) .. + 31
+  // of key tid / 4, and V bytes 8 (tid % 16) .. + 7 of keys 4 (tid / 16) .. + 3
+  // (the 8 dims the thread transposes; 16 lanes read each key's V line).
+  // Clamped metadata keeps every address inside the table row and the cache
+  // (kv_load); keys outside [lo, hi] stage as zeros.
+  struct Codes {
+    u32x4 k0, k1;
+    uint2 v[4];
+  };
+  const int km = tid >> 2, kq = tid & 3, vkg = tid >> 4, vdg = tid & 15;
+  auto load_block = [&](int blk, Codes& c) {
     const int col = blk < a.table_width ? blk : a.table_width - 1;
     int phys = a.block_table[static_cast<size_t>(r) * a.table_width + (col < 0 ? 0 : col)];
     phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
     const uint8_t* base = a.kv_cache + static_cast<size_t>(phys) * kBlock * kKeyBytes;
-    __syncthreads();  // the previous block's tiles are no longer read
-    {
-      // K: thread t widens dims 32 (t % 4) .. + 31 of key t / 4
-      const int km = tid >> 2, kq = tid & 3;
-      const int kp = blk * kBlock + km;
-      const bool live = kp >= w.lo && kp <= w.hi;
-      const u32x4 c0 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq);
-      const u32x4 c1 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq + 16);
-      const uint32_t z = live ? ~0u : 0u;
-      k_lds[swz(km, 4 * kq + 0)] = fp8x8_to_bf16(c0[0] & z, c0[1] & z, 1.0f);
-      k_lds[swz(km, 4 * kq + 1)] = fp8x8_to_bf16(c0[2] & z, c0[3] & z, 1.0f);
-      k_lds[swz(km, 4 * kq + 2)] = fp8x8_to_bf16(c1[0] & z, c1[1] & z, 1.0f);
-      k_lds[swz(km, 4 * kq + 3)] = fp8x8_to_bf16(c1[2] & z, c1[3] & z, 1.0f);
-      // V: thread t widens dims 32 (t / 128) .. + 31 of key t % 128 into V^T
-      const int vk = tid & 127, vc = tid >> 7;
-      const int vp = blk * kBlock + vk;
-      const uint32_t vz = (vp >= w.lo && vp <= w.hi) ? ~0u : 0u;
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + vk * kKeyBytes + kHeadDim + 32 * vc);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + vk * kKeyBytes + kHeadDim + 32 * vc + 16);
-      const int ks = (vk & ~31) + vt_slot(vk & 31);
-      const uint32_t words[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    c.k0 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq);
+    c.k1 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq + 16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x8_t b = fp8x8_to_bf16(words[2 * q] & vz, words[2 * q + 1] & vz, 1.0f);
+    for (int j = 0; j < 4; ++j)
+      c.v[j] = *reinterpret_cast<const uint2*>(base + (4 * vkg + j) * kKeyBytes + kHeadDim + 8 * vdg);
+  };
+  auto stage_block = [&](int blk, const Codes& c) {
+    const int kp = blk * kBlock + km;
+    const uint32_t z = kp >= w.lo && kp <= w.hi ? ~0u : 0u;
+    k_lds[swz(km, 4 * kq + 0)] = fp8x8_to_bf16(c.k0[0] & z, c.k0[1] & z, 1.0f);
+    k_lds[swz(km, 4 * kq + 1)] = fp8x8_to_bf16(c.k0[2] & z, c.k0[3] & z, 1.0f);
+    k_lds[swz(km, 4 * kq + 2)] = fp8x8_to_bf16(c.k1[0] & z, c.k1[1] & z, 1.0f);
+    k_lds[swz(km, 4 * kq + 3)] = fp8x8_to_bf16(c.k1[2] & z, c.k1[3] & z, 1.0f);
+    bf16x8_t vb[4];  // key 4 vkg + j, dims 8 vdg .. + 7
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 32 * vc + 8 * q + e;
-          vt_lds[d * kBlock + ((((ks >> 3) ^ (d & 7)) << 3) | (ks & 7))] = b[e];
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int vp = blk * kBlock + 4 * vkg + j;
+      const uint32_t vz = vp >= w.lo && vp <= w.hi ? ~0u : 0u;
+      vb[j] = fp8x8_to_bf16(c.v[j].x & vz, c.v[j].y & vz, 1.0f);
     }
+    // the four keys take four consecutive key slots of each dim's row
+    const int ks = (4 * vkg & ~31) + vt_slot(4 * vkg & 31);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * vdg + e;
+      const bf16x2 lo2 = {vb[0][e], vb[1][e]}, hi2 = {vb[2][e], vb[3][e]};
+      *reinterpret_cast<uint2*>(vt_lds + vt_off(d, ks)) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
+    }
+  };
+
+  Codes cur;
+  if (bs <= be) load_block(bs, cur);
+  for (int blk = bs; blk <= be; ++blk) {
+    __syncthreads();  // the previous block's tiles are no longer read
+    stage_block(blk, cur);
+    if (blk < be) load_block(blk + 1, cur);  // in flight during this block's math
     __syncthreads();
     if (wave >= kQpr) continue;
 
@@ -245,8 +267,7 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ks = 32 * t + 8 * g4;  // 8 key slots
-        const bf16x8_t va =
-            *reinterpret_cast<const bf16x8_t*>(vt_lds + d * kBlock + ((((ks >> 3) ^ (d & 7)) << 3)));
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt_lds + vt_off(d, ks));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], acc, 0, 0, 0);
       }
       o[n] = acc;
@@ -265,26 +286,53 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
 }
 
 // Step d4: thread (head tid / 16, dims 8 (tid % 16) .. + 7) merges the
-// partitions in order; four threads make one 32-value MX block.
+// partitions in order; four threads make one 32-value MX block. The partials
+// were written by the previous launch, so every load is a trip to the memory
+// side: m, l and the o slice of up to 17 partitions are all issued in one
+// straight run with clamped indices (no branch between them), and a second run
+// takes partitions 17 .. 33 when there are more.
+constexpr int kBatch = 17;
+
 __global__ __launch_bounds__(256) void drafter_merge(DArgs a) {
 #pragma clang fp contract(off)
   const int row = blockIdx.x, tid = threadIdx.x;
   const int h = tid >> 4, d0 = 8 * (tid & 15);
+  const int np = a.nsplit;
   const size_t stride = static_cast<size_t>(kHeads) * (2 + kHeadDim);
-  const float* pr = a.part + static_cast<size_t>(row) * a.nsplit * stride;
-  float M = -__builtin_inff();
-  for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, pr[i * stride + h]);
-  const float Ms = M == -__builtin_inff() ? 0.f : M;
-  float L = 0.f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < a.nsplit; ++i) {
-    const float* p = pr + i * stride;
-    const float wgt = __builtin_amdgcn_exp2f((p[h] - Ms) * kQkC);
-    L = L + wgt * p[kHeads + h];
-    const float4 o0 = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0);
-    const float4 o1 = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0 + 4);
-    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  const float* pr = a.part + static_cast<size_t>(row) * np * stride;
+  float M = -__builtin_inff(), L = 0.f, O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < np; g += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    float4 ov[kBatch][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) O[e] = O[e] + wgt * ov[e];
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = g + u < np ? g + u : np - 1;
+      const float* p = pr + i * stride;
+      mv[u] = p[h];
+      lv[u] = p[kHeads + h];
+      ov[u][0] = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0);
+      ov[u][1] = *reinterpret_cast<const float4*>(p + 2 * kHeads + h * kHeadDim + d0 + 4);
+    }
+    // the running maximum over the partitions so far; the sums carried so far
+    // are rescaled to it
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) Mn = fmaxf(Mn, mv[u]);
+    const float Ms = Mn == -__builtin_inff() ? 0.f : Mn;
+    const float carry = __builtin_amdgcn_exp2f((M - Ms) * kQkC);
+    L = L * carry;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] = O[e] * carry;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // in order
+      const float wgt = g + u < np ? __builtin_amdgcn_exp2f((mv[u] - Ms) * kQkC) : 0.f;
+      L = L + wgt * lv[u];
+      const float o8[8] = {ov[u][0].x, ov[u][0].y, ov[u][0].z, ov[u][0].w,
+                           ov[u][1].x, ov[u][1].y, ov[u][1].z, ov[u][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[e] = O[e] + wgt * o8[e];
+    }
+    M = Mn;
   }
   const bool none = M == -__builtin_inff();
   float ob[8];  // the bf16 outputs as float32
@@ -335,7 +383,7 @@ hipError_t launch_drafter(const DArgs& a0, const DrafterPlan& p) {
   a.part = reinterpret_cast<float*>(a.ws + p.off_part);
   a.nsplit = p.nsplit;
   const int rows = a.requests * kQpr;
-  hipLaunchKernelGGL(drafter_rows, dim3(rows), dim3(256), 0, a.stream, a);
+  hipLaunchKernelGGL(drafter_rows, dim3(rows, (kHeads + 2 + 3) / 4), dim3(256), 0, a.stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = mark(a.ev_start, a.stream)) != hipSuccess) return e;
