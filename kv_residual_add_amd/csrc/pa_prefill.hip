@@ -585,6 +585,110 @@ __device__ __forceinline__ void nv_k_half(const TileRow& x, const uint16_t* gam,
   nv_half_from_tile(x, c0, gs, has_gs, slot, t, half, false);
 }
 
+// The q / index_q head step straight from the accumulators, with no LDS hand-off.
+// In the 32x32 MFMA output, lane l holds token l % 32 and, in acc[m][r], dim
+// 32 m + 8 (r / 4) + 4 (l / 32) + r % 4: the lane's 64 dims of the token, the
+// other 64 in lane l ^ 32. A NeoX RoPE pair (i, i + 32), i < 32, is then
+// acc[0][r] and acc[1][r] of one lane. RopeRegs holds the cos / sin values of
+// the lane's rotary indices 8 g + 4 (l / 32) + [0, 4), g = 0..3, as bf16 pairs.
+struct RopeRegs {
+  uint32_t c[8], s[8];
+};
+
+__device__ __forceinline__ RopeRegs rope_loads(const KArgs& a, int64_t pos) {
+  const int hb = (threadIdx.x & 63) >> 5;
+  const uint16_t* row = a.cos_sin + pos * kRotary;
+  RopeRegs r;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint2 cv = *reinterpret_cast<const uint2*>(row + 8 * g + 4 * hb);
+    const uint2 sv = *reinterpret_cast<const uint2*>(row + 32 + 8 * g + 4 * hb);
+    r.c[2 * g] = cv.x, r.c[2 * g + 1] = cv.y;
+    r.s[2 * g] = sv.x, r.s[2 * g + 1] = sv.y;
+  }
+  return r;
+}
+
+// bf16 element e of a pair array: word e / 2, half e % 2
+__device__ __forceinline__ float bf16_pair_at(const uint32_t* w, int e) {
+  return bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+}
+
+// The q / index_q head step of the lane's token, with the pages' float32
+// precision (contraction off): the head's sum of squares in float32 (again in
+// float64 if it overflows), x / rms * (1 + gamma), the NeoX rotation of dims
+// 0..63, bf16 out, and for q heads the FP8 q codes when requested.
+__device__ __forceinline__ void q_tile_regs(const KArgs& a, const f32x16 (&acc)[4], const uint16_t* gam, int h,
+                                            int tok, const RopeRegs& cs) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, hb = lane >> 5;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s4[r & 3] = __builtin_fmaf(acc[m][r], acc[m][r], s4[r & 3]);
+  float ssf = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  ssf += __shfl_xor(ssf, 32, 64);
+  float rf;
+  if (__builtin_expect(!(ssf <= 3.4028234663852886e38f), 0)) {
+    // the float32 sum of squares overflowed: again in float64 (both lanes of
+    // the token take this branch together)
+    double sd = 0.0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sd += static_cast<double>(acc[m][r]) * acc[m][r];
+    sd += __shfl_xor(sd, 32, 64);
+    rf = static_cast<float>(1.0 / __builtin_sqrt(sd / static_cast<double>(kHeadDim) + static_cast<double>(a.eps)));
+  } else {
+    rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
+  }
+  const int nkv = a.nkv, k0 = 16 * nkv, iq0 = 18 * nkv;
+  uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
+                         : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim;
+  const bool live = tok < a.S;
+  const bool bf16_row = live && (h >= k0 || a.q_out != nullptr);
+  const bool fp8_row = live && h < k0 && a.q_fp8 != nullptr;
+  uint8_t* qf = fp8_row ? a.q_fp8 + (static_cast<size_t>(tok) * k0 + h) * kHeadDim : nullptr;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t gw[4][2];  // gamma of dims 32 m + 8 g + 4 hb + [0, 4)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint2 gv = *reinterpret_cast<const uint2*>(gam + 32 * m + 8 * g + 4 * hb);
+      gw[m][0] = gv.x, gw[m][1] = gv.y;
+    }
+    float o[4][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      const float x1 = (acc[0][r] * rf) * (1.0f + bf16_pair_at(gw[0], e));
+      const float x2 = (acc[1][r] * rf) * (1.0f + bf16_pair_at(gw[1], e));
+      const float c = bf16_pair_at(cs.c + 2 * g, e), sn = bf16_pair_at(cs.s + 2 * g, e);
+      o[0][e] = x1 * c - x2 * sn;
+      o[1][e] = x2 * c + x1 * sn;
+      o[2][e] = (acc[2][r] * rf) * (1.0f + bf16_pair_at(gw[2], e));
+      o[3][e] = (acc[3][r] * rf) * (1.0f + bf16_pair_at(gw[3], e));
+    }
+    if (bf16_row) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g + 4 * hb) =
+            make_uint2(pack_bf16x2(o[m][0], o[m][1]), pack_bf16x2(o[m][2], o[m][3]));
+    }
+    if (fp8_row) {  // E4M3 of the float32 products q * (1 / q_fp8_scale)
+      const float inv = a.q_fp8_inv;
+      const Fp8Scale unit = fp8_scale(0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<uint32_t*>(qf + 32 * m + 8 * g + 4 * hb) =
+            e4m3x4_scaled(o[m][0] * inv, o[m][1] * inv, o[m][2] * inv, o[m][3] * inv, unit);
+    }
+  }
+}
+
+// The k, v and index_k head step of the lane's token from the wave's output
+// tile in LDS (a lane holds 64 contiguous dims of its token).
 __device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, const uint16_t* gam, int h, int tok,
                                               int64_t slot, const EpiIn& in) {
 #pragma clang fp contract(off)
@@ -592,7 +696,7 @@ __device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, 
   const int half = lane >> 5;
   const bool live = tok < a.S;
   const int nkv = a.nkv;
-  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
+  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv;
   const int dbase = 64 * half;
   const int c0 = 16 * half;  // the lane's first chunk: dims dbase + 4 (c - c0) ..
 
@@ -634,105 +738,6 @@ __device__ __forceinline__ void tile_epilogue(const KArgs& a, const TileRow& x, 
         for (int e = 0; e < 4; ++e) vc[(i + e) * kPage] = static_cast<uint8_t>(w >> (8 * e));
       }
       if (lane < 32) a.v_scale[(page * nkv + j) * kPage + t] = s;
-    }
-    return;
-  }
-
-  if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: f32 norm and rotation, bf16 out
-    // Every lane computes (rows past the last token too: their rows are not
-    // stored), so the whole wave takes part in the row stores at the end.
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 64; i += 4) {
-      const float4 v = x.chunk(c0 + (i >> 2));
-      s4[0] = __builtin_fmaf(v.x, v.x, s4[0]);
-      s4[1] = __builtin_fmaf(v.y, v.y, s4[1]);
-      s4[2] = __builtin_fmaf(v.z, v.z, s4[2]);
-      s4[3] = __builtin_fmaf(v.w, v.w, s4[3]);
-    }
-    float ssf = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    ssf += __shfl_xor(ssf, 32, 64);
-    float rf;
-    if (__builtin_expect(!(ssf <= 3.4028234663852886e38f), 0)) {
-      // the float32 sum of squares overflowed (head values past about 2^63):
-      // again in float64, where a float32 square is exact (the pair of lanes
-      // holding the token takes this branch together)
-      double sd = 0.0;
-      for (int i = 0; i < 64; i += 4) {
-        const float4 v = x.chunk(c0 + (i >> 2));
-        sd += static_cast<double>(v.x) * v.x + static_cast<double>(v.y) * v.y + static_cast<double>(v.z) * v.z +
-              static_cast<double>(v.w) * v.w;
-      }
-      sd += __shfl_xor(sd, 32, 64);
-      rf = static_cast<float>(1.0 / __builtin_sqrt(sd / static_cast<double>(kHeadDim) + static_cast<double>(a.eps)));
-    } else {
-      rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
-    }
-    u32x4 o1[4], o2[4];  // bf16 dims i .. i + 7 and i + 32 .. i + 39 for i = 0, 8, 16, 24
-    uint32_t f8a[8], f8b[8];  // E4M3 q of the lane's dims 0 .. 31 and 32 .. 63 (when requested)
-    const bool fp8_row = h < k0 && live && a.q_fp8 != nullptr;
-#pragma unroll
-    for (int i = 0; i < 32; i += 8) {  // dims i .. i + 7 and their partners i + 32 .. i + 39
-      const float4 p0 = x.chunk(c0 + (i >> 2)), p1 = x.chunk(c0 + (i >> 2) + 1);
-      const float4 q0 = x.chunk(c0 + (i >> 2) + 8), q1 = x.chunk(c0 + (i >> 2) + 9);
-      const float f1[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      const float f2[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      const u32x4 ga = *reinterpret_cast<const u32x4*>(gam + dbase + i);       // dims of x1
-      const u32x4 gb = *reinterpret_cast<const u32x4*>(gam + dbase + 32 + i);  // dims of x2
-      float v1[8], v2[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x1 = (f1[e] * rf) * (1.0f + bf16_at_f32(ga, e));
-        const float x2 = (f2[e] * rf) * (1.0f + bf16_at_f32(gb, e));
-        const float c = bf16_at_f32(in.c[i >> 3], e), sn = bf16_at_f32(in.sn[i >> 3], e);
-        v1[e] = x1 * c - x2 * sn;
-        v2[e] = x2 * c + x1 * sn;
-      }
-      if (fp8_row) {  // E4M3 of the float32 products q * (1 / q_fp8_scale)
-        const float inv = a.q_fp8_inv;
-        const Fp8Scale unit = fp8_scale(0);
-#pragma unroll
-        for (int e = 0; e < 8; e += 4) {
-          f8a[(i >> 2) + (e >> 2)] = e4m3x4_scaled(v1[e] * inv, v1[e + 1] * inv, v1[e + 2] * inv, v1[e + 3] * inv, unit);
-          f8b[(i >> 2) + (e >> 2)] = e4m3x4_scaled(v2[e] * inv, v2[e + 1] * inv, v2[e + 2] * inv, v2[e + 3] * inv, unit);
-        }
-      }
-      o1[i >> 3] = u32x4{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
-                         pack_bf16x2(v1[6], v1[7])};
-      o2[i >> 3] = u32x4{pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3]), pack_bf16x2(v2[4], v2[5]),
-                         pack_bf16x2(v2[6], v2[7])};
-    }
-    if (fp8_row) {  // the lane's 64 contiguous codes of the token's 128-byte q row
-      uint8_t* qf = a.q_fp8 + (static_cast<size_t>(tok) * k0 + h) * kHeadDim + dbase;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        *reinterpret_cast<u32x4*>(qf + 16 * j) = u32x4{f8a[4 * j], f8a[4 * j + 1], f8a[4 * j + 2], f8a[4 * j + 3]};
-        *reinterpret_cast<u32x4*>(qf + 32 + 16 * j) =
-            u32x4{f8b[4 * j], f8b[4 * j + 1], f8b[4 * j + 2], f8b[4 * j + 3]};
-      }
-    }
-    if (h < k0 && a.q_out == nullptr) return;  // FP8 q only
-    // The wave's reads of its tile are done (one instruction stream, LDS in
-    // order): the token's bf16 row goes into the first 256 bytes of its f32 row,
-    // then the wave stores whole rows, 16 lanes (256 contiguous bytes) a row
-    // and 4 rows an instruction, instead of 64 scattered 16-byte pieces.
-    uint8_t* rowb = reinterpret_cast<uint8_t*>(const_cast<float*>(x.row));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(rowb + 2 * (dbase + 8 * j)) = o1[j];
-      *reinterpret_cast<u32x4*>(rowb + 2 * (dbase + 32 + 8 * j)) = o2[j];
-    }
-    const uint8_t* tileb = rowb - x.r * kHeadDim * 4;
-    const int tok0 = tok - x.r;  // the tile's first token
-    const int piece = lane & 15;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int rr = (lane >> 4) + 4 * k;
-      const int t = tok0 + rr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tileb + rr * kHeadDim * 4 + 16 * piece);
-      uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(t) * k0 + h) * kHeadDim
-                             : a.iq_out + (static_cast<size_t>(t) * nkv + (h - iq0)) * kHeadDim;
-      if (t < a.S) *reinterpret_cast<u32x4*>(dst + 8 * piece) = v;
     }
     return;
   }
@@ -911,15 +916,6 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* _
   // one-tile FP8 CTAs have the registers for two k steps a stage: twice the
   // lookahead (a bf16 weight step fills a ring slot by itself)
   constexpr int SUB = NTW == 1 ? kSubSingle : 1;
-  if (precise_head(h, a.nkv))
-    mainloop<true, NTW, 1>(a, h, tt0, xq, xs, ring, wave, acc);
-  else
-    mainloop<false, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
-#pragma unroll
-  for (int n = 0; n < NTW; ++n)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) pin_registers(acc[n][m]);
-  stamp(a.timeline, a.timeline_slots, b, 1);
   // The main loop ends with every load landed and every wave past its last LDS
   // read. Lane l holds token l % 32 and dims 32m + 8(r/4) + 4(l/32) + r%4 in
   // acc[n][m][r]: chunk 8m + 2(r/4) + l/32 of row l % 32.
@@ -947,9 +943,36 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* _
     if (n == 0) stamp(a.timeline, a.timeline_slots, b, 3);
     tile_epilogue(a, tr, gam_lds, h, (tt0 + n) * 32 + row, slot, in);
   };
-  epilogue(acc[0], 0, slot_n[0], pos_n[0]);
-  if constexpr (NTW > 1) epilogue(acc[1], 1, slot_n[1], pos_n[1]);
-  static_assert(NTW <= 2, "the epilogue calls above cover two token tiles");
+  auto epilogue_lds = [&]() __attribute__((always_inline)) {
+    epilogue(acc[0], 0, slot_n[0], pos_n[0]);
+    stamp(a.timeline, a.timeline_slots, b, 4);
+    if constexpr (NTW > 1) epilogue(acc[1], 1, slot_n[1], pos_n[1]);
+  };
+  static_assert(NTW <= 2, "the epilogue calls cover two token tiles");
+  auto pin_stamp = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pin_registers(acc[n][m]);
+    stamp(a.timeline, a.timeline_slots, b, 1);
+  };
+  if (precise_head(h, a.nkv)) {  // k, v and index_k
+    mainloop<true, NTW, 1>(a, h, tt0, xq, xs, ring, wave, acc);
+    pin_stamp();
+    epilogue_lds();
+  } else {  // q and index_q
+    mainloop<false, NTW, SUB>(a, h, tt0, xq, xs, ring, wave, acc);
+    pin_stamp();
+    // straight from the accumulators; every tile's cos / sin requested first,
+    // so the second tile's wait overlaps the first tile's work
+    RopeRegs cs[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) cs[n] = rope_loads(a, pos_n[n]);
+    stamp(a.timeline, a.timeline_slots, b, 3);
+    q_tile_regs(a, acc[0], gam_lds, h, tt0 * 32 + row, cs[0]);
+    stamp(a.timeline, a.timeline_slots, b, 4);
+    if constexpr (NTW > 1) q_tile_regs(a, acc[1], gam_lds, h, (tt0 + 1) * 32 + row, cs[1]);
+  }
   stamp(a.timeline, a.timeline_slots, b, 2);
   stamp_place(a.timeline, a.timeline_slots, b, 7);
 }
