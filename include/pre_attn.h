@@ -390,8 +390,11 @@ int pa_set_kernel_events(void* start, void* stop);
  * stored, 5 = its epilogue tokens done); the epilogue of token t and head h
  * at S + heads * ksplit + t * heads + h (0 = start, 1 = inputs loaded; only
  * the tokens a CTA's first wave runs).
- * Prefill: the GEMM CTAs' own phases. Stamps beyond `bytes` are dropped and
- * the outputs do not depend on the stamps. NULL turns it off. */
+ * Prefill: the GEMM CTAs' own phases. Drafter: the split-KV CTA of request r
+ * and partition p at r * partitions + p (0 = start, then for its first three
+ * blocks 1 + 2 i = block i staged in LDS and 2 + 2 i = its math done; 7 =
+ * partial stored). Stamps beyond `bytes` are dropped and the outputs do not
+ * depend on the stamps. NULL turns it off. */
 int pa_set_timeline(void* buffer, size_t bytes);
 
 /* Static text for a pa_status value. */

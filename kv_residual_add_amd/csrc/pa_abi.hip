@@ -468,6 +468,8 @@ int pa_drafter_attention(const pa_drafter_dims* d, const uint16_t* q, const uint
   a.stream = static_cast<hipStream_t>(stream);
   a.ev_start = g_ev_start;
   a.ev_stop = g_ev_stop;
+  a.timeline = g_timeline;
+  a.timeline_slots = g_timeline_slots;
   const hipError_t e = pa::launch_drafter(a, plan);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_drafter_attention");
 }

@@ -44,11 +44,29 @@ constexpr int kKeyBytes = 256;   // K codes | V codes
 constexpr int kWindow = 4096;
 constexpr int kMaxB = 34;        // blocks a request's window may span
 constexpr float kQkC = 0.127517430824598679f;  // log2(e) / sqrt(128)
+constexpr int kRecInts = 4 + kMaxB;  // a request's window record: lo, hi, b0, b1, physical blocks b0 .. b1
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_pos) {
   return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+}
+
+// The request's window (step d2): first / last visible key and block.
+struct Window {
+  int lo, hi, b0, b1;
+};
+
+__device__ __forceinline__ Window request_window(const DArgs& a, int r) {
+  const int p0 = static_cast<int>(clamp_pos(a.positions[r * kQpr], 1 << 30));
+  const int seq = a.seq_lens[r];
+  Window w;
+  w.lo = p0 - (kWindow - 1) > 0 ? p0 - (kWindow - 1) : 0;
+  const int cap = (w.lo / kBlock + kMaxB) * kBlock - 1;
+  w.hi = seq - 1 < cap ? seq - 1 : cap;
+  w.b0 = w.lo / kBlock;
+  w.b1 = w.hi >= w.lo ? w.hi / kBlock : w.b0 - 1;  // no block when the window is empty
+  return w;
 }
 
 // Step d1 for one query row: its 18 tasks (16 q heads, k, v) one wave each,
@@ -58,7 +76,24 @@ __global__ __launch_bounds__(256) void drafter_rows(DArgs a) {
 #pragma clang fp contract(off)
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int task = static_cast<int>(blockIdx.y) * 4 + wave;
-  if (task >= kHeads + 2) return;
+  if (task == kHeads + 2) {
+    // the request's window (step d2) and its physical blocks, once per request,
+    // for the split-KV launch (one round trip there instead of three dependent
+    // ones); blocks and table columns clamped as kv_load does
+    if (t % kQpr != 0) return;
+    const int r = t / kQpr;
+    const Window w = request_window(a, r);
+    int32_t* rec = a.blocks + static_cast<size_t>(r) * kRecInts;
+    if (lane == 0) rec[0] = w.lo, rec[1] = w.hi, rec[2] = w.b0, rec[3] = w.b1;
+    if (lane < kMaxB) {
+      const int blk = w.b0 + lane;
+      const int col = blk < a.table_width ? blk : a.table_width - 1;
+      const int phys = a.block_table[static_cast<size_t>(r) * a.table_width + (col < 0 ? 0 : col)];
+      rec[4 + lane] = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+    }
+    return;
+  }
+  if (task > kHeads + 2) return;
   const int64_t pos = clamp_pos(a.positions[t], a.max_pos);
   const double c = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + (lane & 31)]));
   const double sn = static_cast<double>(bf16_to_f32(a.cos_sin[pos * kRotary + 32 + (lane & 31)]));
@@ -97,23 +132,6 @@ __global__ __launch_bounds__(256) void drafter_rows(DArgs a) {
   }
 }
 
-// The request's window (step d2): first / last visible key and block.
-struct Window {
-  int lo, hi, b0, b1;
-};
-
-__device__ __forceinline__ Window request_window(const DArgs& a, int r) {
-  const int p0 = static_cast<int>(clamp_pos(a.positions[r * kQpr], 1 << 30));
-  const int seq = a.seq_lens[r];
-  Window w;
-  w.lo = p0 - (kWindow - 1) > 0 ? p0 - (kWindow - 1) : 0;
-  const int cap = (w.lo / kBlock + kMaxB) * kBlock - 1;
-  w.hi = seq - 1 < cap ? seq - 1 : cap;
-  w.b0 = w.lo / kBlock;
-  w.b1 = w.hi >= w.lo ? w.hi / kBlock : w.b0 - 1;  // no block when the window is empty
-  return w;
-}
-
 // Key slot o (0..31) of a 32-key group in the V^T tile: the PV operand's lane
 // group g takes keys 4g .. 4g + 3 of the group's two 16-key S tiles, so key
 // 16 a + 4 g + e sits at 8 g + 4 a + e.
@@ -131,27 +149,28 @@ __device__ __forceinline__ int vt_off(int d, int ks) {  // element offset of V^T
   return d * 128 + ((((ks >> 3) ^ ((d & 15) ^ ((d >> 4) & 15))) << 3) | (ks & 7));
 }
 
-__global__ __launch_bounds__(512) void drafter_split(DArgs a) {
+__global__ __launch_bounds__(512, 4) void drafter_split(DArgs a) {
   __shared__ __align__(16) bf16x8_t k_lds[kBlock * 16];     // 128 rows x 16 chunks of 8 bf16
   __shared__ __align__(16) __bf16 vt_lds[kHeadDim * kBlock];  // 128 rows x 128 bf16
   const int part = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const Window w = request_window(a, r);
+  const int32_t* rec = a.blocks + static_cast<size_t>(r) * kRecInts;
+  const Window w{rec[0], rec[1], rec[2], rec[3]};
   const int bs = w.b0 + part * a.split;
   const int be = bs + a.split - 1 < w.b1 ? bs + a.split - 1 : w.b1;
   const int row = r * kQpr + wave;  // this wave's query row (waves < 7)
+  const int tlb = r * a.nsplit + part;  // timeline record
+  stamp(a.timeline, a.timeline_slots, tlb, 0);
   const int qp = wave < kQpr ? static_cast<int>(clamp_pos(a.positions[row], 1 << 30)) : 0;
 
-  // Q^T operand: head l16, dims 32 kk + 8 g4 .. + 7, widened exactly
-  bf16x8_t qb[4];
+  // Q^T operand: head l16, dims 32 kk + 8 g4 .. + 7, kept as codes and widened
+  // exactly for each block (half the registers)
+  uint2 qc[4] = {};
   if (wave < kQpr) {
     const uint8_t* q8 = a.q8 + (static_cast<size_t>(row) * kHeads + l16) * kHeadDim + 8 * g4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint2 c = *reinterpret_cast<const uint2*>(q8 + 32 * kk);
-      qb[kk] = fp8x8_to_bf16(c.x, c.y, 1.0f);
-    }
+    for (int kk = 0; kk < 4; ++kk) qc[kk] = *reinterpret_cast<const uint2*>(q8 + 32 * kk);
   }
   float m = -__builtin_inff(), l = 0.f;
   f32x4 o[8];
@@ -168,11 +187,12 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
     uint2 v[4];
   };
   const int km = tid >> 2, kq = tid & 3, vkg = tid >> 4, vdg = tid & 15;
+  // the partition's physical blocks (already clamped), into LDS
+  __shared__ int s_phys[kMaxB];
+  if (tid < a.split && part * a.split + tid < kMaxB) s_phys[tid] = rec[4 + part * a.split + tid];
+  __syncthreads();
   auto load_block = [&](int blk, Codes& c) {
-    const int col = blk < a.table_width ? blk : a.table_width - 1;
-    int phys = a.block_table[static_cast<size_t>(r) * a.table_width + (col < 0 ? 0 : col)];
-    phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-    const uint8_t* base = a.kv_cache + static_cast<size_t>(phys) * kBlock * kKeyBytes;
+    const uint8_t* base = a.kv_cache + static_cast<size_t>(s_phys[blk - bs]) * kBlock * kKeyBytes;
     c.k0 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq);
     c.k1 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq + 16);
 #pragma unroll
@@ -180,12 +200,14 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
       c.v[j] = *reinterpret_cast<const uint2*>(base + (4 * vkg + j) * kKeyBytes + kHeadDim + 8 * vdg);
   };
   auto stage_block = [&](int blk, const Codes& c) {
-    const int kp = blk * kBlock + km;
+    int sk = km, sv = vdg;  // addresses formed here, not hoisted out of the loop (registers)
+    asm volatile("" : "+v"(sk), "+v"(sv));
+    const int kp = blk * kBlock + sk;
     const uint32_t z = kp >= w.lo && kp <= w.hi ? ~0u : 0u;
-    k_lds[swz(km, 4 * kq + 0)] = fp8x8_to_bf16(c.k0[0] & z, c.k0[1] & z, 1.0f);
-    k_lds[swz(km, 4 * kq + 1)] = fp8x8_to_bf16(c.k0[2] & z, c.k0[3] & z, 1.0f);
-    k_lds[swz(km, 4 * kq + 2)] = fp8x8_to_bf16(c.k1[0] & z, c.k1[1] & z, 1.0f);
-    k_lds[swz(km, 4 * kq + 3)] = fp8x8_to_bf16(c.k1[2] & z, c.k1[3] & z, 1.0f);
+    k_lds[swz(sk, 4 * kq + 0)] = fp8x8_to_bf16(c.k0[0] & z, c.k0[1] & z, 1.0f);
+    k_lds[swz(sk, 4 * kq + 1)] = fp8x8_to_bf16(c.k0[2] & z, c.k0[3] & z, 1.0f);
+    k_lds[swz(sk, 4 * kq + 2)] = fp8x8_to_bf16(c.k1[0] & z, c.k1[1] & z, 1.0f);
+    k_lds[swz(sk, 4 * kq + 3)] = fp8x8_to_bf16(c.k1[2] & z, c.k1[3] & z, 1.0f);
     bf16x8_t vb[4];  // key 4 vkg + j, dims 8 vdg .. + 7
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -197,7 +219,7 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
     const int ks = (4 * vkg & ~31) + vt_slot(4 * vkg & 31);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = 8 * vdg + e;
+      const int d = 8 * sv + e;
       const bf16x2 lo2 = {vb[0][e], vb[1][e]}, hi2 = {vb[2][e], vb[3][e]};
       *reinterpret_cast<uint2*>(vt_lds + vt_off(d, ks)) =
           make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
@@ -211,21 +233,35 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
     stage_block(blk, cur);
     if (blk < be) load_block(blk + 1, cur);  // in flight during this block's math
     __syncthreads();
+    if (blk - bs < 3) stamp(a.timeline, a.timeline_slots, tlb, 1 + 2 * (blk - bs));
     if (wave >= kQpr) continue;
+    // The operand addresses are formed in the loop from this copy of the lane's
+    // head index: hoisted out of it they would hold 64 registers for the whole
+    // loop, and two CTAs a CU need the kernel within 128.
+    int lh = l16;
+    asm volatile("" : "+v"(lh));
 
-    // S^T = K Q^T: s[4 i + e] is key 16 i + 4 g4 + e of the block for head l16
+    // S^T = K Q^T: s[4 i + e] is key 16 i + 4 g4 + e of the block for head l16;
+    // a block whose every key this row sees needs no mask (wave-uniform)
+    const int k0 = blk * kBlock;
+    const bool full = k0 > qp - kWindow && k0 >= w.lo && k0 + kBlock - 1 <= w.hi;
     float s[32];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_lds[swz(16 * i + l16, 4 * kk + g4)], qb[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_lds[swz(16 * i + lh, 4 * kk + g4)],
+                                                      fp8x8_to_bf16(qc[kk].x, qc[kk].y, 1.0f), acc, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kp = blk * kBlock + 16 * i + 4 * g4 + e;
-        const bool vis = kp > qp - kWindow && kp >= w.lo && kp <= w.hi;
-        s[4 * i + e] = vis ? acc[e] : -__builtin_inff();
+      for (int e = 0; e < 4; ++e) s[4 * i + e] = acc[e];
+    }
+    if (!full) {  // keys outside [max(lo, qp - 4095), hi] get -inf (selects, no branches)
+      const int vlo = w.lo > qp - kWindow + 1 ? w.lo : qp - kWindow + 1;
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int kp = k0 + 16 * (x >> 2) + 4 * g4 + (x & 3);
+        s[x] = kp >= vlo && kp <= w.hi ? s[x] : -__builtin_inff();
       }
     }
     float mb = s[0];
@@ -237,33 +273,39 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
     const float ms = mn == -__builtin_inff() ? 0.f : mn;
     const float alpha = __builtin_amdgcn_exp2f((m - ms) * kQkC);
     const float off = ms * kQkC - 8.0f;
-    float p[32], ps = 0.f;
+    // p = 256 exp((s - m) / sqrt(128)), eight keys at a time: summed (before
+    // rounding) and rounded to e4m3 (p <= 256: no saturation) as they come, so
+    // no more than eight of them are live. The PV operand of key step t is
+    // keys 32 t + 4 g4 + [0, 4) and 32 t + 16 + 4 g4 + [0, 4), i.e. p[8 t .. 8 t + 7].
+    float ps = 0.f;
+    uint32_t pc[8];
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      p[x] = __builtin_amdgcn_exp2f(s[x] * kQkC - off);
-      ps += p[x];
+    for (int t = 0; t < 4; ++t) {
+      float p8[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        p8[x] = __builtin_amdgcn_exp2f(s[8 * t + x] * kQkC - off);
+        ps += p8[x];
+      }
+      int lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p8[0], p8[1], 0, false);
+      lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p8[2], p8[3], lo8, true);
+      int hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p8[4], p8[5], 0, false);
+      hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p8[6], p8[7], hi8, true);
+      pc[2 * t] = static_cast<uint32_t>(lo8);
+      pc[2 * t + 1] = static_cast<uint32_t>(hi8);
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l = l * alpha + ps;
     m = mn;
-    // P in e4m3 (p <= 256: no saturation), widened back exactly: the PV
-    // operand of key step t is keys 32 t + 4 g4 + [0, 4) and 32 t + 16 + 4 g4
-    // + [0, 4), i.e. p[8 t .. 8 t + 7]
-    bf16x8_t pb[4];
+    bf16x8_t pb[4];  // widened back exactly
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      int lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t], p[8 * t + 1], 0, false);
-      lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 2], p[8 * t + 3], lo8, true);
-      int hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 4], p[8 * t + 5], 0, false);
-      hi8 = __builtin_amdgcn_cvt_pk_fp8_f32(p[8 * t + 6], p[8 * t + 7], hi8, true);
-      pb[t] = fp8x8_to_bf16(static_cast<uint32_t>(lo8), static_cast<uint32_t>(hi8), 1.0f);
-    }
+    for (int t = 0; t < 4; ++t) pb[t] = fp8x8_to_bf16(pc[2 * t], pc[2 * t + 1], 1.0f);
     // O^T += V^T P^T: o[n][e] is dim 16 n + 4 g4 + e of head l16
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       f32x4 acc = o[n] * alpha;
-      const int d = 16 * n + l16;
+      const int d = 16 * n + lh;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ks = 32 * t + 8 * g4;  // 8 key slots
@@ -272,6 +314,7 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
       }
       o[n] = acc;
     }
+    if (blk - bs < 3) stamp(a.timeline, a.timeline_slots, tlb, 2 + 2 * (blk - bs));
   }
   if (wave >= kQpr) return;
   // the partial of (row, partition): m and l per head, o [16][128]
@@ -283,6 +326,7 @@ __global__ __launch_bounds__(512) void drafter_split(DArgs a) {
   float* po = pm + 2 * kHeads + l16 * kHeadDim;
 #pragma unroll
   for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(po + 16 * n + 4 * g4) = o[n];
+  stamp(a.timeline, a.timeline_slots, tlb, 7);
 }
 
 // Step d4: thread (head tid / 16, dims 8 (tid % 16) .. + 7) merges the
@@ -373,6 +417,8 @@ DrafterPlan drafter_plan(int requests, int split) {
   off = align_up(off + rows * kHeads * kHeadDim, 256);
   p.off_part = off;
   off = align_up(off + rows * p.nsplit * kHeads * (2 + kHeadDim) * sizeof(float), 256);
+  p.off_blocks = off;
+  off = align_up(off + static_cast<size_t>(requests) * kRecInts * sizeof(int32_t), 256);
   p.total = off;
   return p;
 }
@@ -381,6 +427,7 @@ hipError_t launch_drafter(const DArgs& a0, const DrafterPlan& p) {
   DArgs a = a0;
   a.q8 = a.ws + p.off_q8;
   a.part = reinterpret_cast<float*>(a.ws + p.off_part);
+  a.blocks = reinterpret_cast<int32_t*>(a.ws + p.off_blocks);
   a.nsplit = p.nsplit;
   const int rows = a.requests * kQpr;
   hipLaunchKernelGGL(drafter_rows, dim3(rows, (kHeads + 2 + 3) / 4), dim3(256), 0, a.stream, a);

@@ -112,12 +112,15 @@ struct DArgs {
   uint8_t* ws;
   uint8_t* q8;         // workspace: the rows' q codes [7 R][16][128]
   float* part;         // workspace: partials [7 R][nsplit][16][2 + 128]
+  int32_t* blocks;     // workspace: per request lo, hi, first and last block, then its physical blocks
+  uint64_t* timeline;  // phase stamps (pa_set_timeline), or null
+  uint32_t timeline_slots;
   hipStream_t stream;
   hipEvent_t ev_start, ev_stop;
 };
 struct DrafterPlan {
   int nsplit;  // partitions per request (34 blocks / split, rounded up)
-  size_t off_q8, off_part, total;
+  size_t off_q8, off_part, off_blocks, total;
 };
 DrafterPlan drafter_plan(int requests, int split);
 hipError_t launch_drafter(const DArgs& a, const DrafterPlan& p);
