@@ -17,10 +17,12 @@ The FP8 q bar is the q bar in another encoding: the two sides' q values may
 differ by 2e-2 |q| + 1e-3 rms(head), and rounding each to the E4M3 grid adds
 at most one grid step between them. Away from zero that is a code distance of
 at most 1; near zero the absolute floor spans several of the finest steps. The
-q heads' f32 arithmetic (and, in prefill, the FP8 MFMAs at ~1e-4 relative)
-moves a code only where the exact value lies that close to a rounding midpoint,
-so the 1% ceiling catches a systematic rounding mistake (truncation instead of
-nearest-even moves about half of all codes).
+q heads' f32 arithmetic (and, in prefill, the block-scaled FP8 MFMAs, whose
+sums are off by up to ~3e-4 of the sum of the products' magnitudes) moves a
+code only where the exact value lies that close to a rounding midpoint: on
+every token of c4 with the FP8 q at scale 0.008, 1.0e-3 of the codes moved,
+up to 4 steps near zero. The 1% ceiling catches a systematic rounding mistake
+(truncation instead of nearest-even moves about half of all codes).
 
 Code distance: |ord(a) - ord(b)| with ord(c) = +-(c & 0x7F) by the sign bit,
 so +0 and -0 are equal.
