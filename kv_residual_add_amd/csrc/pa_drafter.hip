@@ -192,12 +192,13 @@ __global__ __launch_bounds__(512, 4) void drafter_split(DArgs a) {
   if (tid < a.split && part * a.split + tid < kMaxB) s_phys[tid] = rec[4 + part * a.split + tid];
   __syncthreads();
   auto load_block = [&](int blk, Codes& c) {
+    int ko = km * kKeyBytes + 32 * kq, vo = 4 * vkg * kKeyBytes + kHeadDim + 8 * vdg;
+    asm volatile("" : "+v"(ko), "+v"(vo));  // formed here, not held across the loop (registers)
     const uint8_t* base = a.kv_cache + static_cast<size_t>(s_phys[blk - bs]) * kBlock * kKeyBytes;
-    c.k0 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq);
-    c.k1 = *reinterpret_cast<const u32x4*>(base + km * kKeyBytes + 32 * kq + 16);
+    c.k0 = *reinterpret_cast<const u32x4*>(base + ko);
+    c.k1 = *reinterpret_cast<const u32x4*>(base + ko + 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      c.v[j] = *reinterpret_cast<const uint2*>(base + (4 * vkg + j) * kKeyBytes + kHeadDim + 8 * vdg);
+    for (int j = 0; j < 4; ++j) c.v[j] = *reinterpret_cast<const uint2*>(base + vo + j * kKeyBytes);
   };
   auto stage_block = [&](int blk, const Codes& c) {
     int sk = km, sv = vdg;  // addresses formed here, not hoisted out of the loop (registers)
@@ -257,7 +258,9 @@ __global__ __launch_bounds__(512, 4) void drafter_split(DArgs a) {
       for (int e = 0; e < 4; ++e) s[4 * i + e] = acc[e];
     }
     if (!full) {  // keys outside [max(lo, qp - 4095), hi] get -inf (selects, no branches)
-      const int vlo = w.lo > qp - kWindow + 1 ? w.lo : qp - kWindow + 1;
+      int qw = qp - kWindow + 1;
+      asm volatile("" : "+v"(qw));
+      const int vlo = w.lo > qw ? w.lo : qw;
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
         const int kp = k0 + 16 * (x >> 2) + 4 * g4 + (x & 3);
