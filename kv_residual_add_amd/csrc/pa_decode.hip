@@ -766,6 +766,148 @@ __device__ __forceinline__ void head_epilogue(const KArgs& a, int h, int tok, in
   }
 }
 
+// Sums and maxima over one half-wave (32 lanes): xor butterflies, so every lane
+// of the half ends with the same value.
+__device__ __forceinline__ double half_sum_f64(double v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ double half_max_f64(double v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v = __builtin_fmax(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// The head epilogue of two tokens of head h at once, one per half-wave (the
+// plain call, without head-step options): tok[0] in lanes 0..31, tok[1] in
+// lanes 32..63 (a negative token: that half computes and stores nothing). Lane
+// l of a half holds dims l, l + 32, l + 64 and l + 96, so both members (l, l +
+// 32) of a NeoX RoPE pair sit in one lane. The arithmetic is head_epilogue's:
+// the slice partials summed in slice order in float64, the same float64 head
+// norm and FP8 decisions (only the order of the head's sum of squares differs).
+template <bool COHERENT>
+__device__ __forceinline__ void head_epilogue_pair(const KArgs& a, int h, int tok0, int tok1,
+                                                   const float* __restrict__ part, const float* __restrict__ sx,
+                                                   int ksplit, int tlb) {
+#pragma clang fp contract(off)
+  const int N = a.N();
+  const int lane = threadIdx.x & 63, li = lane & 31;
+  const int tk = lane < 32 ? tok0 : tok1;
+  const bool live = tk >= 0;
+  const int tok = live ? tk : (tok0 >= 0 ? tok0 : 0);
+  const int nkv = a.nkv, S = a.S;
+  const int k0 = 16 * nkv, v0 = 17 * nkv, iq0 = 18 * nkv, ik0 = 19 * nkv;
+  stamp(a.timeline, a.timeline_slots, tlb, 0);
+
+  // every load first: the token's position (cos / sin depend on it), the
+  // slice partials (four dims a lane, sixteen slices in flight at a time), the
+  // scales, the slot and the gammas
+  int64_t pos = a.positions[tok];
+  const size_t stride = static_cast<size_t>(S) * N;
+  const float* p = part + static_cast<size_t>(tok) * N + h * kHeadDim + li;
+  const uint16_t* g = h < k0 ? a.g_q : (h < v0 ? a.g_k : (h < ik0 ? a.g_iq : a.g_ik));
+  double y[4] = {0.0, 0.0, 0.0, 0.0};
+  float sxf = 0.f, ws[4] = {0.f, 0.f, 0.f, 0.f};
+  int64_t slot = 0;
+  uint16_t gm[4] = {0, 0, 0, 0}, cs0 = 0, cs1 = 0;
+  for (int k16 = 0; k16 < ksplit; k16 += 16) {
+    float v[16][4];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {  // clamped indices: every load is unconditional
+      const size_t ks = static_cast<size_t>(min(k16 + u, ksplit - 1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[u][j] = load_partial<COHERENT>(p + ks * stride + 32 * j);
+    }
+    if (k16 == 0) {
+      sxf = load_partial<COHERENT>(sx + tok);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ws[j] = a.w_scale[h * kHeadDim + li + 32 * j], gm[j] = g[li + 32 * j];
+      slot = a.slot_mapping[tok];
+      pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
+      cs0 = a.cos_sin[pos * kRotary + li];
+      cs1 = a.cos_sin[pos * kRotary + 32 + li];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = k16 + u < ksplit;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] += in ? static_cast<double>(v[u][j]) : 0.0;
+    }
+  }
+  stamp(a.timeline, a.timeline_slots, tlb, 1);
+  const double sxv = static_cast<double>(sxf);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = (y[j] * sxv) * static_cast<double>(ws[j]);
+
+  const bool store_cache = live && slot >= 0 && slot < static_cast<int64_t>(a.num_pages) * kPage;
+  const int64_t page = slot_page(slot);
+  const int t = slot_row(slot);
+  const Fp8Scale unit = fp8_scale(0);
+
+  if (h >= v0 && h < iq0) {  // V: the raw projection, per-token scale
+    const int jv = h - v0;
+    const double amax = half_max_f64(__builtin_fmax(__builtin_fmax(__builtin_fabs(y[0]), __builtin_fabs(y[1])),
+                                                    __builtin_fmax(__builtin_fabs(y[2]), __builtin_fabs(y[3]))));
+    const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
+    if (store_cache) {
+      const double sd = static_cast<double>(s), rcp = 1.0 / sd;
+      uint8_t* vc = a.v_cache + (page * nkv + jv) * kPageBytes + t;
+      const uint32_t c01 = e4m3x2_scaled(div_rn(y[0], sd, rcp), div_rn(y[1], sd, rcp), unit);
+      const uint32_t c23 = e4m3x2_scaled(div_rn(y[2], sd, rcp), div_rn(y[3], sd, rcp), unit);
+      vc[(li + 0) * kPage] = static_cast<uint8_t>(c01);
+      vc[(li + 32) * kPage] = static_cast<uint8_t>(c01 >> 8);
+      vc[(li + 64) * kPage] = static_cast<uint8_t>(c23);
+      vc[(li + 96) * kPage] = static_cast<uint8_t>(c23 >> 8);
+      if (li == 0) a.v_scale[(page * nkv + jv) * kPage + t] = s;
+    }
+    return;
+  }
+
+  const double ss = half_sum_f64((y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]));
+  const double r = 1.0 / __builtin_sqrt(ss / static_cast<double>(kHeadDim) + static_cast<double>(a.eps));
+  double nm[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) nm[j] = (y[j] * r) * (1.0 + static_cast<double>(bf16_to_f32(gm[j])));
+  const double c = static_cast<double>(bf16_to_f32(cs0));
+  const double sn = static_cast<double>(bf16_to_f32(cs1));
+  const double o[4] = {nm[0] * c - nm[1] * sn, nm[1] * c + nm[0] * sn, nm[2], nm[3]};
+
+  if (h < k0 || (h >= iq0 && h < ik0)) {  // q / index_q: bf16 out
+    if (!live) return;
+    uint16_t* q = h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
+                         : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[li + 32 * j] = static_cast<uint16_t>(f32_to_bf16(static_cast<float>(o[j])));
+  } else if (h < v0) {  // K: per-token scale, shuffled page-16 layout
+    const int jk = h - k0;
+    const double amax = half_max_f64(__builtin_fmax(__builtin_fmax(__builtin_fabs(o[0]), __builtin_fabs(o[1])),
+                                                    __builtin_fmax(__builtin_fabs(o[2]), __builtin_fabs(o[3]))));
+    const float s = amax == 0.0 ? 1.0f : static_cast<float>(amax / kFp8Max);
+    if (store_cache) {
+      const double sd = static_cast<double>(s), rcp = 1.0 / sd;
+      uint8_t* kc = a.k_cache + (page * nkv + jk) * kPageBytes + t * 16;
+      const uint32_t c01 = e4m3x2_scaled(div_rn(o[0], sd, rcp), div_rn(o[1], sd, rcp), unit);
+      const uint32_t c23 = e4m3x2_scaled(div_rn(o[2], sd, rcp), div_rn(o[3], sd, rcp), unit);
+      const uint32_t cw[4] = {c01 & 0xffu, (c01 >> 8) & 0xffu, c23 & 0xffu, (c23 >> 8) & 0xffu};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = li + 32 * j;
+        kc[(d >> 4) * 256 + (d & 15)] = static_cast<uint8_t>(cw[j]);
+      }
+      if (li == 0) a.k_scale[(page * nkv + jk) * kPage + t] = s;
+    }
+  } else if (store_cache) {  // index_k: unit-scale E4M3 into the slot's row
+    uint8_t* ic = a.index_cache + slot * kHeadDim;
+    const uint32_t c01 = e4m3x2_scaled(o[0], o[1], unit);
+    const uint32_t c23 = e4m3x2_scaled(o[2], o[3], unit);
+    ic[li] = static_cast<uint8_t>(c01);
+    ic[li + 32] = static_cast<uint8_t>(c01 >> 8);
+    ic[li + 64] = static_cast<uint8_t>(c23);
+    ic[li + 96] = static_cast<uint8_t>(c23 >> 8);
+  }
+}
+
 template <bool OPT>
 __global__ __launch_bounds__(64) void decode_epilogue(KArgs a, size_t off_part, size_t off_sx, int ksplit) {
   const int H = a.heads();
@@ -928,10 +1070,24 @@ __global__ __launch_bounds__(256) void decode_gemv_epi(KArgs a, DecodePlan p) {
     for (int f = 0; f < 4; ++f) __hip_atomic_store(hc + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int wave = threadIdx.x >> 6;
-  for (; mask != 0u; mask &= mask - 1u) {
-    const int sl = __builtin_ctz(mask);
-    for (int tok = sl + ksplit * wave; tok < a.S; tok += 4 * ksplit)
-      head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+  if constexpr (OPT) {  // head-step options: one token a wave
+    for (; mask != 0u; mask &= mask - 1u) {
+      const int sl = __builtin_ctz(mask);
+      for (int tok = sl + ksplit * wave; tok < a.S; tok += 4 * ksplit)
+        head_epilogue<true, OPT>(a, h, tok, a.positions[tok], part, sx, ksplit, a.S + H * ksplit + tok * H + h);
+    }
+  } else {  // two tokens a wave, one per half; a share's token pairs dealt to the waves in turn
+    int pq = 0;
+    for (; mask != 0u; mask &= mask - 1u) {
+      const int sl = __builtin_ctz(mask);
+      const int cnt = sl < a.S ? (a.S - sl + ksplit - 1) / ksplit : 0;
+      for (int q = 0; 2 * q < cnt; ++q, ++pq) {
+        if ((pq & 3) != wave) continue;
+        const int t0 = sl + 2 * q * ksplit;
+        const int t1 = 2 * q + 1 < cnt ? t0 + ksplit : -1;
+        head_epilogue_pair<true>(a, h, t0, t1, part, sx, ksplit, a.S + H * ksplit + t0 * H + h);
+      }
+    }
   }
   stamp(a.timeline, a.timeline_slots, a.S + ks * H + h, 5);
 }

@@ -52,6 +52,7 @@ DECODE_SMALL = [
     (5, 1024, 1, {"oob_frac": 0.4}),               # one launch
     (8, 6144, 1, {"oob_frac": 0.25}),              # norm + GEMV, then the epilogue
     (40, 2048, 2, {"oob_frac": 0.2, "skip_frac": 0.1}),  # norm, then GEMV + epilogue
+    (24, 16384, 1, {"oob_frac": 0.2}),             # the same past the fused norm's hidden
     (20, 4736, 1, {"oob_frac": 0.2}),              # three launches
 ]
 
