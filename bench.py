@@ -18,7 +18,8 @@ captured into one HIP graph (as a serving engine replays decode steps); HIP
 events around the replay time them, queued right behind the untimed copy so
 that the host's submission is not counted. A second, eager pass over the same
 pool records HIP events around every launch of the dominant kernel to get its
-average duration for the roofline.
+average duration for the roofline. Prefill records also carry, as context,
+the time of the vendor library's plain FP8 GEMM (hipBLASLt) of the same shape.
 
 Workloads: c1 tiny decode, c2 decode batch, c3 speculative decode, c4 / c5
 prefill, and d1, the DSpark drafter's attention (16 requests of 7 draft rows).
@@ -179,6 +180,47 @@ def cpu_baseline(wl, inp, budget_s: float, one_core: bool = False):
                       f"({sum(times):.1f} s), float64 NumPy"}
 
 
+def library_gemm(M, N, K, dev, flush_src, flush_dst, reps):
+    """A plain FP8 GEMM of the projection's shape from the vendor library
+    (hipBLASLt through torch._scaled_mm: E4M3 operands, row-wise float32 scales,
+    bf16 out, no epilogue, no block scales), each launch timed by HIP events
+    after the same 512 MB cache flush. Context for the fused GEMM's time (what a
+    tuned library reaches on this shape and chip), not a baseline of the path."""
+    import numpy as np
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = (torch.randn(M, K, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    b = (torch.randn(N, K, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    sa = torch.ones(M, 1, device=dev)
+    sb = torch.ones(1, N, device=dev)
+
+    def gemm():
+        return torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+
+    try:
+        for _ in range(3):
+            gemm()
+        torch.cuda.synchronize()
+    except RuntimeError as e:  # a torch build without FP8 GEMMs for this device
+        return {"error": str(e)[:200]}
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        flush_dst.copy_(flush_src)
+        e0.record()
+        gemm()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    tflops = 2.0 * M * N * K / (ms / 1e3) / 1e12
+    del a, b
+    return {"what": "hipBLASLt FP8 GEMM via torch._scaled_mm, E4M3 x E4M3, row-wise scales, bf16 out, "
+                    "same M x N x K, no epilogue; mean of per-launch hip events after a 512 MB flush",
+            "M": M, "N": N, "K": K, "launches": reps, "kernel_ms": round(ms, 5),
+            "tflops": round(tflops, 1), "frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+
+
 def run_config(key, args):
     """Measures one workload; returns its record."""
     import numpy as np
@@ -333,6 +375,8 @@ def run_config(key, args):
         "eager_ms_per_step": round(eager_s / args.steps * 1e3, 5),
         **extra,
     }
+    if wl.mode == "prefill" and args.head_options == "none":
+        rec["library_fp8_gemm"] = library_gemm(S, N, K, dev, flush_src, flush_dst, min(args.steps, 20))
     del sets, prob, flush_src, flush_dst
     torch.cuda.empty_cache()
     if args.cpu_seconds > 0:
