@@ -19,7 +19,8 @@ events around the replay time them, queued right behind the untimed copy so
 that the host's submission is not counted. A second, eager pass over the same
 pool records HIP events around every launch of the dominant kernel to get its
 average duration for the roofline. Prefill records also carry, as context,
-the time of the vendor library's plain FP8 GEMM (hipBLASLt) of the same shape.
+the time of the vendor library's plain FP8 GEMM (hipBLASLt) of the same shape,
+and the full run the rates plain streaming kernels reach (hbm_context).
 
 Workloads: c1 tiny decode, c2 decode batch, c3 speculative decode, c4 / c5
 prefill, and d1, the DSpark drafter's attention (16 requests of 7 draft rows).
@@ -78,6 +79,54 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
                       "bytes_written_per_launch": n, "launches": 10}))
+
+
+def hbm_context(reps=20):
+    """What plain streaming kernels reach on this machine, after the same 512 MB
+    cache flush (HIP events, median of `reps`): a 354 MB device-to-device copy
+    (708 MB moved) and torch's bf16 add of two [8192, 6144] tensors (2 reads +
+    1 write, 302 MB, the prefill norm pass's shape). Context for the HBM
+    roofline fractions, which use the published 8 TB/s."""
+    import torch
+
+    dev = "cuda:0"
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+
+    def median_us(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            flush_dst.copy_(flush_src)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    g = torch.Generator(device=dev).manual_seed(0)  # random bits, like the workloads' data
+    x = torch.randn(354_000_000 // 4, dtype=torch.float32, device=dev, generator=g)
+    y = torch.empty_like(x)
+    copy_us = median_us(lambda: y.copy_(x))
+    copy_bytes = 2 * x.numel() * 4
+    del x, y
+    a = torch.randn(8192, 6144, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(8192, 6144, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty_like(a)
+    add_us = median_us(lambda: torch.add(a, b, out=c))
+    add_bytes = 3 * a.numel() * 2
+    del a, b, c, flush_src, flush_dst
+    torch.cuda.empty_cache()
+    return {"what": "plain streaming kernels on random data after a 512 MB flush, HIP events, median of %d" % reps,
+            "copy_bytes": copy_bytes, "copy_us": round(copy_us, 2),
+            "copy_tbs": round(copy_bytes / copy_us / 1e6, 3),
+            "bf16_add_bytes": add_bytes, "bf16_add_us": round(add_us, 2),
+            "bf16_add_tbs": round(add_bytes / add_us / 1e6, 3)}
 
 
 def algorithmic(wl, structure=0, head_options="none"):
@@ -552,6 +601,7 @@ def main():
     }
     if len(keys) > 1:
         line["configs"] = recs
+        line["hbm_context"] = hbm_context()
     else:
         line.update({k: v for k, v in h.items() if k not in line and k not in ("workload", "metric", "value",
                                                                                   "unit", "config")})
