@@ -618,8 +618,14 @@ __device__ __forceinline__ float bf16_pair_at(const uint32_t* w, int e) {
 // precision (contraction off): the head's sum of squares in float32 (again in
 // float64 if it overflows), x / rms * (1 + gamma), the NeoX rotation of dims
 // 0..63, bf16 out, and for q heads the FP8 q codes when requested.
+// The bf16 rows go out through `stage` (this wave's 8.5 KB of LDS, free after
+// the main loop): written there at the accumulator layout (row stride 272
+// bytes), read back 16 bytes a lane with 16 lanes a row, so that each global
+// store instruction writes four whole 256-byte rows; stored straight from the
+// accumulators, a row took sixteen 16-byte pieces.
+constexpr int kQStageRow = 272;
 __device__ __forceinline__ void q_tile_regs(const KArgs& a, const f32x16 (&acc)[4], const uint16_t* gam, int h,
-                                            int tok, const RopeRegs& cs) {
+                                            int tok, const RopeRegs& cs, uint8_t* stage) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, hb = lane >> 5;
   float s4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -644,11 +650,10 @@ __device__ __forceinline__ void q_tile_regs(const KArgs& a, const f32x16 (&acc)[
     rf = 1.0f / __builtin_sqrtf(ssf / static_cast<float>(kHeadDim) + a.eps);
   }
   const int nkv = a.nkv, k0 = 16 * nkv, iq0 = 18 * nkv;
-  uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(tok) * k0 + h) * kHeadDim
-                         : a.iq_out + (static_cast<size_t>(tok) * nkv + (h - iq0)) * kHeadDim;
   const bool live = tok < a.S;
-  const bool bf16_row = live && (h >= k0 || a.q_out != nullptr);
+  const bool bf16_rows = h >= k0 || a.q_out != nullptr;  // uniform
   const bool fp8_row = live && h < k0 && a.q_fp8 != nullptr;
+  uint8_t* const srow = stage + (lane & 31) * kQStageRow;
   uint8_t* qf = fp8_row ? a.q_fp8 + (static_cast<size_t>(tok) * k0 + h) * kHeadDim : nullptr;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -670,10 +675,10 @@ __device__ __forceinline__ void q_tile_regs(const KArgs& a, const f32x16 (&acc)[
       o[2][e] = (acc[2][r] * rf) * (1.0f + bf16_pair_at(gw[2], e));
       o[3][e] = (acc[3][r] * rf) * (1.0f + bf16_pair_at(gw[3], e));
     }
-    if (bf16_row) {
+    if (bf16_rows) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g + 4 * hb) =
+        *reinterpret_cast<uint2*>(srow + 2 * (32 * m + 8 * g + 4 * hb)) =
             make_uint2(pack_bf16x2(o[m][0], o[m][1]), pack_bf16x2(o[m][2], o[m][3]));
     }
     if (fp8_row) {  // E4M3 of the float32 products q * (1 / q_fp8_scale)
@@ -683,6 +688,20 @@ __device__ __forceinline__ void q_tile_regs(const KArgs& a, const f32x16 (&acc)[
       for (int m = 0; m < 4; ++m)
         *reinterpret_cast<uint32_t*>(qf + 32 * m + 8 * g + 4 * hb) =
             e4m3x4_scaled(o[m][0] * inv, o[m][1] * inv, o[m][2] * inv, o[m][3] * inv, unit);
+    }
+  }
+  if (bf16_rows) {  // LDS keeps one wave's accesses in order: no barrier
+    const int tok0 = tok - (lane & 31);  // the tile's first token
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 4 * u + (lane >> 4), c = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * kQStageRow + 16 * c);
+      const int t = tok0 + r;
+      if (t < a.S) {
+        uint16_t* dst = h < k0 ? a.q_out + (static_cast<size_t>(t) * k0 + h) * kHeadDim
+                               : a.iq_out + (static_cast<size_t>(t) * nkv + (h - iq0)) * kHeadDim;
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = v;
+      }
     }
   }
 }
@@ -969,9 +988,10 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm(KArgs a, const uint8_t* _
 #pragma unroll
     for (int n = 0; n < NTW; ++n) cs[n] = rope_loads(a, pos_n[n]);
     stamp(a.timeline, a.timeline_slots, b, 3);
-    q_tile_regs(a, acc[0], gam_lds, h, tt0 * 32 + row, cs[0]);
+    uint8_t* const stage = wave == 0 ? ring0 : wave == 1 ? ring1 : wave == 2 ? ring2 : ring3;  // free now
+    q_tile_regs(a, acc[0], gam_lds, h, tt0 * 32 + row, cs[0], stage);
     stamp(a.timeline, a.timeline_slots, b, 4);
-    if constexpr (NTW > 1) q_tile_regs(a, acc[1], gam_lds, h, (tt0 + 1) * 32 + row, cs[1]);
+    if constexpr (NTW > 1) q_tile_regs(a, acc[1], gam_lds, h, (tt0 + 1) * 32 + row, cs[1], stage);
   }
   stamp(a.timeline, a.timeline_slots, b, 2);
   stamp_place(a.timeline, a.timeline_slots, b, 7);
