@@ -77,6 +77,8 @@ PREFILL_SMALL = [
     (257, 384, 2, {"outlier_frac": 0.01}),
     (300, 1024, 2, {"oob_frac": 0.1, "skip_frac": 0.05}),  # slots past the cache's end
     (2560, 256, 4, {"oob_frac": 0.05}),                   # the same with 256-token CTAs
+    (40, 16384, 1, {}),                                   # hidden past 8192: the norm pass's 1024-thread form
+    (65, 12288, 2, {"skip_frac": 0.1}),                   # the same with 768 threads a row
 ]
 
 
