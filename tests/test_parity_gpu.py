@@ -46,6 +46,7 @@ DECODE_SMALL = [
     (33, 1536, 2, {"outlier_frac": 0.01}),
     (64, 2048, 1, {"skip_frac": 0.1}),
     (20, 4736, 1, {}),  # 37 k slices: the epilogue in a launch of its own
+    (12, 8192, 2, {}),  # the fused norm at its widest (four 8-element vectors a thread)
     (8, 16384, 1, {}),  # hidden past the fused norm's reach, 32 k slices
     (4, 16384, 2, {}),  # more CTAs than are resident at once
     # slots at or past the cache's end write nothing, in every launch structure
