@@ -37,6 +37,7 @@
 #include <atomic>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -250,11 +251,18 @@ constexpr int kSubSingle = 2;      // k steps per stage in one-tile CTAs
 
 // A stage is SUB consecutive k steps: their weight tiles share one ring slot
 // (8 KB each) and their register loads one set.
+//
+// The precise heads keep the activation scale as a byte: a register set can be
+// consumed after the loop's back edge, and a byte widened to 32 bits where it
+// is loaded would make the compiler wait for that load (and so for every load
+// issued before it) right there, draining the lookahead once a loop iteration.
+// Widened where it is used, after the stage's own wait, it costs nothing.
 template <bool PRECISE, int NTW, int SUB>
 struct Stage {
-  uint32_t sa[SUB];       // weight scale dword (row tiles in bytes 0..3) for block lane / 32
-  i32x4 b[SUB][NTW][2];   // activation bytes 0..15 and 16..31 of the lane
-  uint32_t sb[SUB][NTW];  // the lane's activation scale (its token, block lane / 32)
+  using ScaleByte = std::conditional_t<PRECISE, uint8_t, uint32_t>;
+  uint32_t sa[SUB];        // weight scale dword (row tiles in bytes 0..3) for block lane / 32
+  i32x4 b[SUB][NTW][2];    // activation bytes 0..15 and 16..31 of the lane
+  ScaleByte sb[SUB][NTW];  // the lane's activation scale (its token, block lane / 32)
 };
 
 // Loads of one k step go through buffer resources, one per operand panel (the
@@ -308,7 +316,7 @@ __device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW, SUB>& st, const 
       const int blk = n * nks + ks;
       st.b[u][n][0] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes, 0);
       st.b[u][n][1] = __builtin_amdgcn_raw_buffer_load_b128(p.b, lane * 16, blk * kTileBytes + 1024, 0);
-      st.sb[u][n] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0));
+      st.sb[u][n] = __builtin_amdgcn_raw_buffer_load_b8(p.sb, lane, blk * 64, 0);
     }
   }
   // weight tiles: instruction q of wave w moves bytes (256 q + 64 w + lane) * 16
@@ -333,8 +341,8 @@ __device__ __forceinline__ void stage_issue(Stage<PRECISE, NTW, SUB>& st, const 
 
 // The MFMAs of one k step: weight scale dword sa0, activation fragments b0 and
 // scales sb0, the weight tile at `slot`.
-template <bool PRECISE, int NTW>
-__device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2], const uint32_t (&sb0)[NTW],
+template <bool PRECISE, int NTW, typename ScaleByte>
+__device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2], const ScaleByte (&sb0)[NTW],
                                           const uint8_t* slot, f32x16 (&acc)[NTW][4]) {
   const int lane = threadIdx.x & 63;
   if (PRECISE) {
