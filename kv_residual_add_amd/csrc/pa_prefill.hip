@@ -373,11 +373,16 @@ __device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2
       }
     }
   } else {
+    i32x8 Am[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const i32x4 a0 = reinterpret_cast<const i32x4*>(slot + m * kTileBytes)[lane];
       const i32x4 a1 = reinterpret_cast<const i32x4*>(slot + m * kTileBytes + 1024)[lane];
-      const i32x8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      Am[m] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const i32x8 A = Am[m];
 #pragma unroll
       for (int n = 0; n < NTW; ++n) {
         const i32x8 B = {b0[n][0][0], b0[n][0][1], b0[n][0][2], b0[n][0][3],
@@ -393,11 +398,40 @@ __device__ __forceinline__ void step_mfma(uint32_t sa0, const i32x4 (&b0)[NTW][2
   }
 }
 
+// The weight operand's LDS reads are issued ahead of the MFMAs that take
+// them (scheduling groups, in order): left to itself the compiler reads each
+// row tile just before its MFMAs and waits for it there, so every row tile
+// paid the LDS latency (~200 cycles with two CTAs a CU) against 64-128 cycles
+// of MFMA work. The precise heads (16 reads, 16 NTW bf16 MFMAs a step) run
+// 8 reads ahead in one-tile CTAs and 4 in two-tile CTAs, whose registers are
+// full; the two-tile FP8 step (8 reads, 8 MFMAs) runs one row tile ahead. The
+// one-tile FP8 step keeps the compiler's order (reading ahead there did not
+// shorten the launch).
 template <bool PRECISE, int NTW, int SUB>
 __device__ __forceinline__ void stage_mfma(const Stage<PRECISE, NTW, SUB>& st, const uint8_t* slot,
                                            f32x16 (&acc)[NTW][4]) {
 #pragma unroll
   for (int u = 0; u < SUB; ++u) step_mfma<PRECISE, NTW>(st.sa[u], st.b[u], st.sb[u], slot + u * 8192, acc);
+  constexpr int kDs = 0x080, kDsRead = 0x100, kMfma = 0x008;  // sched_group_barrier masks
+  if constexpr (PRECISE) {
+    static_assert(SUB == 1, "one bf16 step a stage");
+    constexpr int ahead = NTW == 1 ? 8 : 4;
+    __builtin_amdgcn_sched_group_barrier(kDs, ahead + NTW, 0);  // + the scale shuffles
+#pragma unroll
+    for (int i = 0; i < 16 - ahead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, NTW, 0);
+      __builtin_amdgcn_sched_group_barrier(kDs, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, ahead * NTW, 0);
+  } else if constexpr (NTW == 2) {
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+  }
 }
 
 // One stage of the pipeline: wait until this wave's loads of stage s have
