@@ -505,6 +505,11 @@ __device__ __forceinline__ uint32_t gemv_tile(const KArgs& a, int h, int ks, con
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       wv[c][q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wb + c * 16384 + q * 1024));
+  // Every weight load is issued before the first MFMA. Left to itself the
+  // scheduler sinks each load next to its MFMAs (fewer live registers), which
+  // keeps two or three of a wave's loads in flight instead of all of them.
+  // (With a publisher the widening below already needs them all first.)
+  if constexpr (!FUSED) __builtin_amdgcn_sched_barrier(0);
   // with a publisher, the weights are widened while the norm statistics are
   // still on their way (off the critical path)
   bf16x8 aw[FUSED ? CPC : 1][FUSED ? 8 : 1];
