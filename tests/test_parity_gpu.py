@@ -80,6 +80,8 @@ PREFILL_SMALL = [
     (2560, 256, 4, {"oob_frac": 0.05}),                   # the same with 256-token CTAs
     (40, 16384, 1, {}),                                   # hidden past 8192: the norm pass's 1024-thread form
     (65, 12288, 2, {"skip_frac": 0.1}),                   # the same with 768 threads a row
+    (1000, 1024, 4, {}),                                  # more than one round of 128-token CTAs, ragged
+    (1700, 2048, 2, {"skip_frac": 0.1}),                  # the same at nkv 2
 ]
 
 
