@@ -117,7 +117,14 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
   const uint32_t xs_off = (tid & 1) ? 0x7ffffff0u : static_cast<uint32_t>(xs_offset(0, tid >> 1, nks));
   const uint32_t tile_q = static_cast<uint32_t>(nks) * kTileBytes, tile_s = static_cast<uint32_t>(nks) * 64;
 
-  int row = blockIdx.x;
+  // Rows 8i .. 8i + 7 of a token tile fill the packed activation's 128-byte
+  // lines together (16 bytes each), so they go to the 8 blocks of one XCD
+  // (equal index mod 8) in the same pass, and each line is assembled in one
+  // L2 rather than written back in pieces by all eight. The grid is a multiple
+  // of 64 and the mapping a bijection onto [0, grid) whatever the placement.
+  const int G = static_cast<int>(gridDim.x);
+  const int bx = static_cast<int>(blockIdx.x) & 7, bj = static_cast<int>(blockIdx.x) >> 3;
+  int row = 8 * (bx * (G >> 6) + (bj >> 3)) + (bj & 7);
   u32x4 av[2], bv[2];
   const auto load_row = [&](int r, u32x4* x, u32x4* y) {
     const auto ra = row_rsrc(ar, r), rb = row_rsrc(res, r);
@@ -1127,7 +1134,7 @@ hipError_t launch_prepass_t(const Args& a, const PrefillPlan& p, int mpad, int c
       per_cu = 1;
     per_cu_cache[threads >> 6].store(per_cu, std::memory_order_relaxed);
   }
-  const int grid = std::min(mpad, per_cu * cus);
+  const int grid = std::max(64, std::min(mpad, per_cu * cus) / 64 * 64);  // mpad is a multiple of 256
   hipLaunchKernelGGL(prefill_prepass<WIDE>, dim3(grid), dim3(threads), 0, a.stream, a.ar, a.res, a.h_out, a.g_in,
                      a.ws + p.off_xq, a.ws + p.off_xs, a.S, mpad, a.K, a.eps);
   return hipGetLastError();
