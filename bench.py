@@ -521,6 +521,7 @@ def run_drafter(args):
     gbs = nbytes / (kern_ms / 1e3) / 1e9
     tfs = flops / (kern_ms / 1e3) / 1e12
     prof = _profile_record("kernel_times.json", DRAFTER, "drafter")
+    traffic_rec = _profile_record("traffic.json", DRAFTER, "drafter")
     rec = {
         "workload": "drafter_attention_r16_seq2k_12k_split2", "metric": "drafter rows/s", "unit": "rows/s",
         "value": round(rows * args.steps / elapsed, 1), "ms_per_step": round(elapsed / args.steps * 1e3, 5),
@@ -530,7 +531,8 @@ def run_drafter(args):
                    "pool_sets": n_sets, "cache_flush_mb": 512,
                    "timing": "hip graph replay; hip events around the K steps, queued behind the untimed cache flush"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "drafter_split",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_rec.get("bytes_per_launch") if traffic_rec else None, "kernel": "drafter_split",
                      "kernel_ms": round(kern_ms, 5), "kernel_ms_from": "hip events, eager pass",
                      "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
                      "mfma_bf16_tflops": round(tfs, 1), "mfma_bf16_frac": round(tfs / BF16_PEAK_TFLOPS, 4)},
