@@ -134,6 +134,21 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
     y[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff + 16, 0, 0);
   };
   if constexpr (!WIDE) load_row(row, av, bv);
+  // A row's codes and scale are stored one row later, right after the next
+  // row's data has arrived. Loads and stores share the vector-memory counter
+  // and may complete out of order, so a wave with stores in flight can only
+  // wait for all of them: stored at the end of its row, they made every next
+  // row wait out their acknowledgements; stored early, they are done by then.
+  u32x4 pw = {0u, 0u, 0u, 0u};
+  uint32_t pcode = 0;
+  int prow = -1;  // uniform: no row pending
+  const auto store_codes = [&]() {
+    const size_t tt = static_cast<size_t>(prow >> 5);
+    const uint32_t tl = static_cast<uint32_t>(prow & 31);
+    __builtin_amdgcn_raw_buffer_store_b128(pw, panel(xq + tt * tile_q, tile_q), xq_off + 16u * tl, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(pcode), panel(xs + tt * tile_s, tile_s), xs_off + tl, 0,
+                                         0);
+  };
   for (int it = 0; row < mpad; ++it) {
     const int next = row + static_cast<int>(gridDim.x);
     u32x4 an[2], bn[2];
@@ -167,6 +182,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
     const auto hr = row_rsrc(h_out, row);
     __builtin_amdgcn_raw_buffer_store_b128(hv[0], hr, voff, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(hv[1], hr, voff + 16, 0, 0);
+    if (prow >= 0) store_codes();
     // row sum: DPP wave sums, then the waves' values in a fixed order; the two
     // halves of `red` alternate between rows, so one barrier per row suffices
     const double ss = wave_sum_f64((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]));
@@ -195,15 +211,15 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void prefill_prepass(
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = e4m3x4_scaled(xn[4 * j], xn[4 * j + 1], xn[4 * j + 2], xn[4 * j + 3], f) & keep;
-    const size_t tt = static_cast<size_t>(row >> 5);
-    const uint32_t tl = static_cast<uint32_t>(row & 31);
-    __builtin_amdgcn_raw_buffer_store_b128(w, panel(xq + tt * tile_q, tile_q), xq_off + 16u * tl, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), panel(xs + tt * tile_s, tile_s), xs_off + tl, 0, 0);
+    pw = w;
+    pcode = static_cast<uint32_t>(code);
+    prow = row;
     if constexpr (!WIDE) {
       av[0] = an[0], av[1] = an[1], bv[0] = bn[0], bv[1] = bn[1];
     }
     row = next;
   }
+  if (prow >= 0) store_codes();  // the last row's
 }
 
 // Packed weight: head h, k step ks, 32-row tile m -> 2 KB block at
